@@ -1,0 +1,7 @@
+"""Seeded synthetic workloads for the K2 MoE layer (shapes and input recipe only)."""
+from .configs import (ALL, FMT_F32, FMT_FP8, K2_DECODE, K2_DENSE, K2_PREFILL, K2_SKEWED,
+                      TINY, MoEShape, small_fp8)
+from .gen import MoEInputs, block_quantize_weight, generate
+
+__all__ = ["ALL", "FMT_F32", "FMT_FP8", "K2_DECODE", "K2_DENSE", "K2_PREFILL", "K2_SKEWED",
+           "TINY", "MoEShape", "small_fp8", "MoEInputs", "block_quantize_weight", "generate"]
