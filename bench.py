@@ -1,0 +1,219 @@
+"""Benchmark of the Kimi K2 MoE feed-forward layer on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload decode|prefill|skewed|dense]
+
+One step = one moe_forward over one batch: RMSNorm + activation
+quantisation, router, top-k, permutation, grouped gate/up GEMM + SwiGLU +
+requantisation, grouped down GEMM, combine + residual.  Inputs are seeded
+synthetic tensors already resident in HBM; weights are random-init FP8 with
+128x128 block scales at the released K2 shape.
+
+Prints one JSON line: tokens/s for the named workload (default: the 64-token
+decode step), the dominant kernel's roofline fraction measured with HIP
+events inside the timed region, the same for the 8192-token prefill, and the
+CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes as C
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s at K2 shape (64-tok decode, 8K prefill); % of roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA
+# bytes of one expert's gate+up codes and their 128x128 block scales
+GATEUP_BYTES_PER_EXPERT = 2 * 2048 * 7168 + 2 * 16 * 56 * 4
+DOWN_BYTES_PER_EXPERT = 7168 * 2048 + 56 * 16 * 4
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode",
+                    choices=["decode", "prefill", "skewed", "dense"])
+    ap.add_argument("--no-secondary", action="store_true", help="skip the prefill line")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=3)
+    return ap.parse_args()
+
+
+def shapes():
+    import synth
+    return {"decode": synth.K2_DECODE, "prefill": synth.K2_PREFILL,
+            "skewed": synth.K2_SKEWED, "dense": synth.K2_DENSE}
+
+
+def timed(layer, x, steps, warmup):
+    """Run warmup + steps forwards; per-stage HIP-event times of the timed steps."""
+    import torch
+    from sparse_moe_transformer_sigmoid_amd import _lib as L
+
+    lib = L.load()
+    out = torch.empty((x.shape[0], layer.shape.d_model), dtype=x.dtype, device=x.device)
+    for _ in range(warmup):
+        layer.forward(x, out)
+    torch.cuda.synchronize()
+    ms = (C.c_double * 8)()
+    n = (C.c_int64 * 8)()
+    L.check("moe_profile_read", lib.moe_profile_read(ms, n, 1))
+    L.check("moe_profile_enable", lib.moe_profile_enable(1))
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        layer.forward(x, out)
+    stop.record()
+    torch.cuda.synchronize()
+    L.check("moe_profile_enable", lib.moe_profile_enable(0))
+    L.check("moe_profile_read", lib.moe_profile_read(ms, n, 1))
+    stage = {name: (ms[i] / n[i] if n[i] else 0.0) for i, name in enumerate(L.STAGES)}
+    return start.elapsed_time(stop) / steps, stage
+
+
+def routing_stats(layer, x):
+    import numpy as np
+    import torch
+    r = layer.router(x)
+    pm = layer.permute(r.ids)
+    torch.cuda.synchronize()
+    counts = np.diff(pm.offsets.cpu().numpy())
+    return int(np.sum(counts > 0)), counts
+
+
+def run_workload(layer, inp, steps, warmup):
+    shape = inp.shape
+    T = inp.x.shape[0]
+    ms, stage = timed(layer, inp.x, steps, warmup)
+    touched, counts = routing_stats(layer, inp.x)
+    touched_all = touched + shape.n_shared
+    d, I, k = shape.d_model, shape.d_ff, shape.top_k
+    P = T * k
+    rows = P + (T if shape.n_shared else 0)
+    # gate/up kernel: expert weights read once, activations read once, a_q written once
+    gu_bytes = (touched_all * (2 * I * d + 2 * (I // 128) * (d // 128) * 4)
+                + T * d + T * (d // 128) * 4 + rows * I + rows * (I // 128) * 4)
+    gu_flops = 2.0 * rows * (2 * I) * d
+    dn_flops = 2.0 * rows * I * d
+    gu_s = stage["gateup"] * 1e-3
+    return dict(T=T, ms=ms, stage=stage, touched=touched_all, counts=counts,
+                gu_bytes=gu_bytes, gu_flops=gu_flops, total_flops=gu_flops + dn_flops,
+                gu_gbs=gu_bytes / gu_s / 1e9 if gu_s > 0 else 0.0,
+                gu_tflops=gu_flops / gu_s / 1e12 if gu_s > 0 else 0.0)
+
+
+def cpu_baseline(inp, n_tokens):
+    """The oracle on the host cores: routing of the batch, experts of n tokens."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle.adapt import to_f32
+    from oracle.moe_ref import moe_layer, params_from_shape
+
+    p = params_from_shape(inp.shape)
+    T = inp.x.shape[0]
+    sel = np.arange(min(n_tokens, T))
+    x = to_f32(inp.x)
+    norm_w = to_f32(inp.norm_w)
+    wr = None if inp.w_router is None else to_f32(inp.w_router)
+    bias = None if inp.bias is None else to_f32(inp.bias)
+    # host copies of every expert the sample needs, made before the clock starts
+    from oracle.moe_ref import rmsnorm, route
+    h = rmsnorm(x[sel], norm_w, p.rms_eps, round_bf16=p.fp8)
+    need = set(range(p.n_experts, p.n_experts + p.n_shared))
+    if p.dense:
+        need.add(0)
+    else:
+        need.update(np.unique(route(h, wr, bias, p.top_k, p.routed_scaling,
+                                    p.norm_topk_prob)["ids"]).tolist())
+    cache = {}
+    for e in need:
+        cache[e] = {n: (None if getattr(inp, n) is None else getattr(inp, n)[e].cpu().numpy())
+                    for n in ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down")}
+    t0 = time.perf_counter()
+    moe_layer(p, x, norm_w, wr, bias, lambda e: cache[e], tokens=sel)
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": len(sel) / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {len(sel)} of {T} tokens of the {inp.shape.name} batch: routing of "
+                      f"the batch and the experts of the sampled tokens, {dt:.1f} s on "
+                      f"{os.cpu_count()} host cores (BLAS threads {threads})"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus above 1 is not "
+                                   "supported (the layer is not sharded across GPUs)"}))
+        sys.exit(2)
+    import torch
+
+    import synth
+    from sparse_moe_transformer_sigmoid_amd.layer import K2MoE
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU"}))
+        sys.exit(1)
+    shp = shapes()[args.workload]
+    t0 = time.time()
+    if args.workload == "dense":
+        base = synth.generate(shp, seed=0, device="cuda")
+        inp = base
+    else:
+        base = synth.generate(synth.K2_DECODE, seed=0, device="cuda")
+        inp = synth.with_workload(base, shp, seed=0)
+    layer = K2MoE(base)
+    print(f"# inputs generated and packed in {time.time() - t0:.1f} s", file=sys.stderr,
+          flush=True)
+
+    res = run_workload(layer, inp, args.steps, args.warmup)
+    T = res["T"]
+    value = T / (res["ms"] * 1e-3)
+    gu_ms = res["stage"]["gateup"]
+    line = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["ms"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8e4m3", "data": "synthetic",
+        "config": {"workload": shp.name, "tokens": T, "d_model": shp.d_model,
+                   "routed_experts": shp.n_experts, "shared_experts": shp.n_shared,
+                   "top_k": shp.top_k, "d_ff": shp.d_ff,
+                   "touched_experts": res["touched"]},
+        "roofline": {"bound": "hbm", "kernel": "grouped gate/up GEMM + SwiGLU + requant",
+                     "achieved": res["gu_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": res["gu_gbs"] / HBM_PEAK_GBS, "traffic": None,
+                     "kernel_ms": gu_ms, "algorithmic_bytes": res["gu_bytes"]},
+        "stage_ms": res["stage"],
+    }
+    if args.workload in ("prefill", "skewed", "dense"):
+        line["roofline"].update({"bound": "mfma", "achieved": res["gu_tflops"],
+                                 "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                 "frac": res["gu_tflops"] / FP8_PEAK_TFLOPS,
+                                 "algorithmic_flops": res["gu_flops"]})
+    if args.workload == "decode" and not args.no_secondary:
+        pre = synth.with_workload(base, synth.K2_PREFILL, seed=0)
+        rp = run_workload(layer, pre, max(3, args.steps // 2), 2)
+        line["prefill"] = {
+            "tokens": rp["T"], "value": rp["T"] / (rp["ms"] * 1e-3), "unit": "tokens/s",
+            "ms_per_step": rp["ms"],
+            "fp8_tflops_layer": rp["total_flops"] / (rp["ms"] * 1e-3) / 1e12,
+            "frac_fp8_peak_layer": rp["total_flops"] / (rp["ms"] * 1e-3) / 1e12 / FP8_PEAK_TFLOPS,
+            "gateup_tflops": rp["gu_tflops"], "gateup_frac_fp8_peak":
+                rp["gu_tflops"] / FP8_PEAK_TFLOPS,
+            "gateup_gbs": rp["gu_gbs"], "stage_ms": rp["stage"]}
+        del pre
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(inp, args.cpu_tokens)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

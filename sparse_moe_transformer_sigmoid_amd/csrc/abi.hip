@@ -1,0 +1,647 @@
+// C ABI of the K2 MoE layer: argument validation, workspace layout and the
+// launch sequence of each entry point.  See include/k2moe.h for the contract.
+#include <algorithm>
+#include <cstdio>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "k2_launch.h"
+#include "k2moe.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+moe_status fail(moe_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+
+#define K2_REQUIRE(cond, st, msg) \
+  do {                            \
+    if (!(cond)) return fail(st, msg); \
+  } while (0)
+
+#define K2_HIP(expr)                                                          \
+  do {                                                                        \
+    hipError_t e_ = (expr);                                                   \
+    if (e_ != hipSuccess)                                                     \
+      return fail(MOE_ERR_HIP, std::string(#expr) + ": " + hipGetErrorString(e_)); \
+  } while (0)
+
+// ---- per-stage event profiling (off unless enabled)
+struct Profiler {
+  std::mutex mu;
+  bool on = false;
+  struct Rec { int stage; hipEvent_t a, b; };
+  std::vector<Rec> pending;
+  std::vector<hipEvent_t> pool;
+  double ms[MOE_STAGE_COUNT] = {};
+  int64_t n[MOE_STAGE_COUNT] = {};
+
+  hipEvent_t get() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+  // drain recorded pairs into the totals; caller holds mu
+  hipError_t drain() {
+    hipError_t first = hipSuccess;
+    for (const Rec& r : pending) {
+      float t = 0.f;
+      hipError_t err = hipEventSynchronize(r.b);
+      if (err == hipSuccess) err = hipEventElapsedTime(&t, r.a, r.b);
+      if (err == hipSuccess) {
+        ms[r.stage] += t;
+        n[r.stage] += 1;
+      } else if (first == hipSuccess) {
+        first = err;
+      }
+      pool.push_back(r.a);
+      pool.push_back(r.b);
+    }
+    pending.clear();
+    return first;
+  }
+};
+Profiler& prof() {
+  static Profiler p;
+  return p;
+}
+
+// Records an event pair around one stage when profiling is on.
+class Stage {
+ public:
+  Stage(int stage, hipStream_t s) : stage_(stage), s_(s) {
+    Profiler& p = prof();
+    std::lock_guard<std::mutex> g(p.mu);
+    if (!p.on) return;
+    a_ = p.get();
+    b_ = p.get();
+    if (a_ && b_ && hipEventRecord(a_, s_) == hipSuccess) active_ = true;
+  }
+  ~Stage() {
+    if (!active_) return;
+    Profiler& p = prof();
+    std::lock_guard<std::mutex> g(p.mu);
+    if (hipEventRecord(b_, s_) == hipSuccess) p.pending.push_back({stage_, a_, b_});
+  }
+
+ private:
+  int stage_;
+  hipStream_t s_;
+  hipEvent_t a_ = nullptr, b_ = nullptr;
+  bool active_ = false;
+};
+
+constexpr size_t ALIGN = 256;
+size_t align_up(size_t x) { return (x + ALIGN - 1) & ~(ALIGN - 1); }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Dims {
+  int d, E, S, k, I, G;
+  bool fp8, dense;
+  float scaling, eps;
+  int renorm;
+  int64_t T, P;
+};
+
+moe_status check_cfg(const moe_config* c, Dims* o) {
+  K2_REQUIRE(c != nullptr, MOE_ERR_INVALID_ARG, "config is NULL");
+  K2_REQUIRE(c->fmt == MOE_FMT_F32 || c->fmt == MOE_FMT_BF16_FP8B128, MOE_ERR_UNSUPPORTED,
+             "unknown fmt");
+  K2_REQUIRE(c->n_group == 1 && c->topk_group == 1, MOE_ERR_UNSUPPORTED,
+             "only one expert group (n_group = topk_group = 1) is implemented");
+  K2_REQUIRE(c->d_model > 0 && c->d_ff > 0 && c->n_experts > 0 && c->top_k > 0,
+             MOE_ERR_INVALID_ARG, "dimensions must be positive");
+  K2_REQUIRE(c->top_k <= c->n_experts, MOE_ERR_INVALID_ARG, "top_k > n_experts");
+  K2_REQUIRE(c->n_shared == 0 || c->n_shared == 1, MOE_ERR_UNSUPPORTED, "n_shared must be 0 or 1");
+  K2_REQUIRE(c->top_k <= 32 && c->n_experts <= 1024, MOE_ERR_UNSUPPORTED,
+             "top_k <= 32 and n_experts <= 1024 are supported");
+  K2_REQUIRE(c->d_model <= 16384, MOE_ERR_UNSUPPORTED, "d_model <= 16384 is supported");
+  K2_REQUIRE(c->dense == 0 || c->dense == 1, MOE_ERR_INVALID_ARG, "dense must be 0 or 1");
+  if (c->dense)
+    K2_REQUIRE(c->n_experts == 1 && c->top_k == 1 && c->n_shared == 0, MOE_ERR_INVALID_ARG,
+               "dense mode needs n_experts = top_k = 1 and n_shared = 0");
+  const bool fp8 = c->fmt == MOE_FMT_BF16_FP8B128;
+  if (fp8) {
+    K2_REQUIRE(c->d_model % 256 == 0 && c->d_ff % 128 == 0, MOE_ERR_UNSUPPORTED,
+               "FP8 format needs d_model % 256 == 0 and d_ff % 128 == 0");
+    K2_REQUIRE(c->dense || c->n_experts % 16 == 0, MOE_ERR_UNSUPPORTED,
+               "FP8 format needs n_experts % 16 == 0");
+  } else {
+    K2_REQUIRE(c->d_model % 8 == 0, MOE_ERR_UNSUPPORTED, "F32 format needs d_model % 8 == 0");
+  }
+  K2_REQUIRE(c->rms_eps >= 0.f, MOE_ERR_INVALID_ARG, "rms_eps < 0");
+  o->d = c->d_model;
+  o->E = c->n_experts;
+  o->S = c->n_shared;
+  o->k = c->top_k;
+  o->I = c->d_ff;
+  o->G = o->E + o->S;
+  o->fp8 = fp8;
+  o->dense = c->dense != 0;
+  o->scaling = c->routed_scaling;
+  o->eps = c->rms_eps;
+  o->renorm = c->norm_topk_prob ? 1 : 0;
+  o->T = 0;
+  o->P = 0;
+  return MOE_OK;
+}
+
+moe_status check_tokens(int64_t T, Dims* D) {
+  K2_REQUIRE(T >= 0, MOE_ERR_INVALID_ARG, "T < 0");
+  const int64_t P = T * D->k;
+  const int64_t rows = P + T;
+  K2_REQUIRE(T <= (1 << 24) && rows * std::max(D->d, D->I) < (int64_t)1 << 32,
+             MOE_ERR_UNSUPPORTED, "too many tokens for 32-bit row offsets");
+  D->T = T;
+  D->P = P;
+  return MOE_OK;
+}
+
+#define K2_PTR(p, name)                                                                 \
+  do {                                                                                  \
+    K2_REQUIRE((p) != nullptr, MOE_ERR_INVALID_ARG, std::string(name) + " is NULL");      \
+    K2_REQUIRE(aligned16(p), MOE_ERR_INVALID_ARG, std::string(name) + " is not 16-byte aligned"); \
+  } while (0)
+#define K2_OPT_PTR(p, name)                                                             \
+  do {                                                                                  \
+    K2_REQUIRE((p) == nullptr || aligned16(p), MOE_ERR_INVALID_ARG,                     \
+               std::string(name) + " is not 16-byte aligned");                          \
+  } while (0)
+
+// router GEMM split over K so small batches still fill the chip
+int router_ksplit(const Dims& D) {
+  if (!D.fp8 || D.dense) return 1;
+  const int64_t tiles = ((D.T + 63) / 64) * ((D.E + 63) / 64);
+  const int steps = D.d / 32;
+  int best = 1;
+  for (int ks = 1; ks <= 64; ++ks) {
+    if (steps % ks) continue;
+    best = ks;
+    if (tiles * ks >= 512) break;
+  }
+  return best;
+}
+
+int gemm_tt(const Dims& D) {
+  const double avg = D.dense ? (double)D.T : (double)D.P / D.E;
+  if (avg <= 12) return 1;
+  if (avg <= 24) return 2;
+  if (avg <= 48) return 4;
+  return 8;
+}
+
+struct Layout {
+  size_t hbuf = 0, xq = 0, xs = 0, zpart = 0, ids = 0, w = 0, gap = 0, ccount = 0, cbase = 0,
+         offsets = 0, row_pair = 0, pair_row = 0, mt_start = 0, aq = 0, as = 0, rows = 0,
+         shared = 0, total = 0;
+  int ksplit = 1, nchunk = 1;
+};
+
+// offsets of the workspace sub-buffers each entry point uses
+Layout layout(const Dims& D, int entry) {
+  Layout L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align_up(bytes);
+    return o;
+  };
+  const size_t T = (size_t)D.T, P = (size_t)D.P, d = (size_t)D.d, I = (size_t)D.I;
+  const size_t E = (size_t)D.E;
+  L.ksplit = router_ksplit(D);
+  const int chunk = k2::perm_chunk_tokens(D.E);
+  L.nchunk = (int)((D.T + chunk - 1) / chunk);
+  const bool fwd = entry == MOE_WS_FORWARD;
+  if (fwd) {
+    L.xq = take(T * d * (D.fp8 ? 1 : 4));
+    if (D.fp8) L.xs = take(T * (d / 128) * 4);
+    L.ids = take(P * 4);
+    L.w = take(P * 4);
+    L.gap = take(T * 4);
+    L.offsets = take((E + 1) * 4);
+    L.row_pair = take(P * 4);
+    L.pair_row = take(P * 4);
+    L.rows = take(P * d * 4);
+    if (D.S) L.shared = take(T * d * 4);
+  }
+  if (fwd || entry == MOE_WS_ROUTER) {
+    if (D.fp8) L.hbuf = take(T * d * 2);
+    if (!D.dense) L.zpart = take((size_t)L.ksplit * T * E * 4);
+  }
+  if (fwd || entry == MOE_WS_PERMUTE) {
+    L.ccount = take((size_t)L.nchunk * E * 4);
+    L.cbase = take((size_t)L.nchunk * E * 4);
+  }
+  if (fwd || entry == MOE_WS_SWIGLU) {
+    L.mt_start = take(((size_t)D.G + 1) * 4);
+    const size_t nrows = P + (D.S ? T : 0);
+    if (D.fp8) {
+      L.aq = take(nrows * I);
+      L.as = take(nrows * (I / 128) * 4);
+    } else {
+      L.aq = take(nrows * I * 4);
+    }
+  }
+  L.total = D.T == 0 ? 0 : off;  // no tokens, nothing enqueued, no workspace
+  return L;
+}
+
+struct Packed {
+  size_t expert_bytes, gu_scale_off, dn_scale_off, gu_scale_floats, dn_scale_floats, total;
+};
+
+Packed packed_layout(const Dims& D) {
+  Packed p{};
+  const size_t NE = (size_t)D.G, d = (size_t)D.d, I = (size_t)D.I;
+  if (D.fp8) {
+    p.expert_bytes = 3 * I * d;
+    p.gu_scale_floats = (I / 128) * (d / 128) * 2;
+    p.dn_scale_floats = (d / 128) * (I / 128);
+    p.gu_scale_off = align_up(NE * p.expert_bytes);
+    p.dn_scale_off = p.gu_scale_off + align_up(NE * p.gu_scale_floats * 4);
+    p.total = p.dn_scale_off + align_up(NE * p.dn_scale_floats * 4);
+  } else {
+    p.expert_bytes = 3 * I * d * 4;
+    p.total = NE * p.expert_bytes;
+  }
+  return p;
+}
+
+template <class Tp>
+Tp* at(void* base, size_t off) {
+  return reinterpret_cast<Tp*>(static_cast<uint8_t*>(base) + off);
+}
+
+// ---- launch sequences shared by the unfused entry points and moe_forward
+
+moe_status run_router(const Dims& D, const Layout& L, void* ws, const void* x, const void* norm_w,
+                      const void* w_router, const float* bias, int32_t* ids, float* w, float* gap,
+                      void* xq, float* xs, hipStream_t s) {
+  const int T = (int)D.T;
+  void* hbuf = D.fp8 ? at<void>(ws, L.hbuf) : nullptr;
+  {
+    Stage st(MOE_STAGE_NORM_QUANT, s);
+    K2_HIP(k2::launch_norm_quant(D.fp8, T, D.d, D.eps, x, norm_w, hbuf, xq, xs, s));
+  }
+  if (D.dense) {
+    Stage st(MOE_STAGE_TOPK, s);
+    K2_HIP(k2::launch_dense_route(T, D.scaling, ids, w, gap, s));
+    return MOE_OK;
+  }
+  float* zpart = at<float>(ws, L.zpart);
+  {
+  Stage st(MOE_STAGE_ROUTER_GEMM, s);
+  if (D.fp8)
+    K2_HIP(k2::launch_router_gemm_bf16(T, D.d, D.E, L.ksplit, static_cast<const uint16_t*>(hbuf),
+                                       static_cast<const uint16_t*>(w_router), zpart, s));
+  else
+    K2_HIP(k2::launch_router_gemm_f32(T, D.d, D.E, static_cast<const float*>(xq),
+                                      static_cast<const float*>(w_router), zpart, s));
+  }
+  Stage st(MOE_STAGE_TOPK, s);
+  K2_HIP(k2::launch_topk(T, D.E, D.k, D.fp8 ? L.ksplit : 1, zpart, bias, D.scaling, D.renorm,
+                         ids, w, gap, s));
+  return MOE_OK;
+}
+
+moe_status run_permute(const Dims& D, const Layout& L, void* ws, const int32_t* ids,
+                       int32_t* offsets, int32_t* row_pair, int32_t* pair_row, hipStream_t s) {
+  Stage st(MOE_STAGE_PERMUTE, s);
+  K2_HIP(k2::launch_permute((int)D.T, D.E, D.k, ids, at<int32_t>(ws, L.ccount),
+                            at<int32_t>(ws, L.cbase), offsets, row_pair, pair_row, s));
+  return MOE_OK;
+}
+
+moe_status run_experts(const Dims& D, const Layout& L, void* ws, const void* xq, const float* xs,
+                       const int32_t* offsets, const int32_t* row_pair, const void* packed_w,
+                       float* rows, float* shared_out, const float* topk_w, int weighted,
+                       hipStream_t s) {
+  const int T = (int)D.T, P = (int)D.P;
+  const Packed pk = packed_layout(D);
+  if (!D.fp8) {
+    Stage st(MOE_STAGE_GATEUP, s);
+    K2_HIP(k2::launch_experts_f32(T, D.d, D.I, D.E, D.k, D.S, static_cast<const float*>(xq),
+                                  offsets, row_pair, static_cast<const float*>(packed_w),
+                                  pk.expert_bytes / 4, at<float>(ws, L.aq), rows, shared_out,
+                                  topk_w, weighted, s));
+    return MOE_OK;
+  }
+  const int tt = gemm_tt(D);
+  const int bm = 16 * tt;
+  int32_t* mt_start = at<int32_t>(ws, L.mt_start);
+  {
+    Stage st(MOE_STAGE_TILES, s);
+    K2_HIP(k2::launch_build_tiles(D.E, D.S, T, D.k, bm, offsets, mt_start, s));
+  }
+  // upper bound of the m-tiles actually present (device-side count)
+  const int64_t nz = std::min<int64_t>(D.E, D.P);
+  const int64_t mt_bound = (D.P + (int64_t)(bm - 1) * nz) / bm + 1 + (D.S ? (T + bm - 1) / bm : 0);
+  auto grid_of = [&](int nc) {
+    const int64_t g = (mt_bound * nc + 7) / 8 * 8;
+    return (int)std::min<int64_t>(g, (int64_t)1 << 30);
+  };
+  uint8_t* aq = at<uint8_t>(ws, L.aq);
+  float* as = at<float>(ws, L.as);
+  const uint8_t* pw = static_cast<const uint8_t*>(packed_w);
+
+  k2::GemmArgs a{};
+  a.offsets = offsets;
+  a.row_pair = row_pair;
+  a.mt_start = mt_start;
+  a.E = D.E;
+  a.G = D.G;
+  a.T = T;
+  a.k = D.k;
+  a.P = P;
+  a.aq = aq;
+  a.as = as;
+  a.I = D.I;
+  a.rows = rows;
+  a.shared_out = shared_out;
+  a.topk_w = topk_w;
+  a.weighted = weighted;
+  a.d = D.d;
+
+  // gate/up + SwiGLU + requantisation: K = d, 128 hidden (256 weight rows) per chunk
+  a.wpk = pw;
+  a.expert_stride = pk.expert_bytes;
+  a.wscale = reinterpret_cast<const float*>(pw + pk.gu_scale_off);
+  a.wscale_stride = pk.gu_scale_floats;
+  a.act = static_cast<const uint8_t*>(xq);
+  a.act_s = xs;
+  a.act_ld = D.d;
+  a.nkb = D.d / 128;
+  a.NC = D.I / 128;
+  {
+    Stage st(MOE_STAGE_GATEUP, s);
+    K2_HIP(k2::launch_gemm_fp8(true, tt, a, grid_of(a.NC), s));
+  }
+
+  // down projection: K = I, 256 output rows per chunk
+  a.wpk = pw + 2 * (size_t)D.I * D.d;
+  a.wscale = reinterpret_cast<const float*>(pw + pk.dn_scale_off);
+  a.wscale_stride = pk.dn_scale_floats;
+  a.act = aq;
+  a.act_s = as;
+  a.act_ld = D.I;
+  a.nkb = D.I / 128;
+  a.NC = D.d / 256;
+  {
+    Stage st(MOE_STAGE_DOWN, s);
+    K2_HIP(k2::launch_gemm_fp8(false, tt, a, grid_of(a.NC), s));
+  }
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_str(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+const char* moe_last_error(void) { return g_err.c_str(); }
+
+moe_status moe_profile_enable(int32_t on) {
+  Profiler& p = prof();
+  std::lock_guard<std::mutex> g(p.mu);
+  p.on = on != 0;
+  return MOE_OK;
+}
+
+moe_status moe_profile_read(double* ms, int64_t* launches, int32_t reset) {
+  Profiler& p = prof();
+  std::lock_guard<std::mutex> g(p.mu);
+  const hipError_t err = p.drain();
+  for (int i = 0; i < MOE_STAGE_COUNT; ++i) {
+    if (ms) ms[i] = p.ms[i];
+    if (launches) launches[i] = p.n[i];
+  }
+  if (reset) {
+    for (int i = 0; i < MOE_STAGE_COUNT; ++i) {
+      p.ms[i] = 0.0;
+      p.n[i] = 0;
+    }
+  }
+  if (err != hipSuccess)
+    return fail(MOE_ERR_HIP, std::string("profile events: ") + hipGetErrorString(err));
+  return MOE_OK;
+}
+
+size_t moe_packed_weights_bytes(const moe_config* cfg) {
+  Dims D;
+  if (check_cfg(cfg, &D) != MOE_OK) return 0;
+  return packed_layout(D).total;
+}
+
+moe_status moe_workspace_bytes(const moe_config* cfg, int64_t T, int32_t entry, size_t* bytes) {
+  Dims D;
+  moe_status st = check_cfg(cfg, &D);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(T, &D)) != MOE_OK) return st;
+  K2_REQUIRE(entry >= MOE_WS_ROUTER && entry <= MOE_WS_FORWARD, MOE_ERR_INVALID_ARG,
+             "unknown workspace entry");
+  K2_REQUIRE(bytes != nullptr, MOE_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = layout(D, entry).total;
+  return MOE_OK;
+}
+
+moe_status moe_pack_weights(const moe_config* cfg, const moe_expert_w* experts,
+                            int32_t n_experts_total, void* packed, void* stream) {
+  Dims D;
+  moe_status st = check_cfg(cfg, &D);
+  if (st != MOE_OK) return st;
+  K2_REQUIRE(experts != nullptr, MOE_ERR_INVALID_ARG, "experts is NULL");
+  K2_REQUIRE(n_experts_total == D.G, MOE_ERR_INVALID_ARG,
+             "n_experts_total must be n_experts + n_shared");
+  K2_PTR(packed, "packed");
+  for (int e = 0; e < D.G; ++e) {
+    const moe_expert_w& x = experts[e];
+    const std::string nm = "expert " + std::to_string(e) + " ";
+    K2_PTR(x.w_gate, nm + "w_gate");
+    K2_PTR(x.w_up, nm + "w_up");
+    K2_PTR(x.w_down, nm + "w_down");
+    if (D.fp8) {
+      K2_PTR(x.s_gate, nm + "s_gate");
+      K2_PTR(x.s_up, nm + "s_up");
+      K2_PTR(x.s_down, nm + "s_down");
+    }
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Packed pk = packed_layout(D);
+  uint8_t* base = static_cast<uint8_t*>(packed);
+  for (int e = 0; e < D.G; ++e) {
+    const moe_expert_w& x = experts[e];
+    if (D.fp8) {
+      K2_HIP(k2::launch_pack_fp8(
+          D.d, D.I, static_cast<const uint8_t*>(x.w_gate), static_cast<const uint8_t*>(x.w_up),
+          static_cast<const uint8_t*>(x.w_down), x.s_gate, x.s_up, x.s_down,
+          base + e * pk.expert_bytes,
+          reinterpret_cast<float*>(base + pk.gu_scale_off) + e * pk.gu_scale_floats,
+          reinterpret_cast<float*>(base + pk.dn_scale_off) + e * pk.dn_scale_floats, s));
+    } else {
+      const size_t mat = (size_t)D.I * D.d * 4;
+      uint8_t* dst = base + e * pk.expert_bytes;
+      K2_HIP(hipMemcpyAsync(dst, x.w_gate, mat, hipMemcpyDeviceToDevice, s));
+      K2_HIP(hipMemcpyAsync(dst + mat, x.w_up, mat, hipMemcpyDeviceToDevice, s));
+      K2_HIP(hipMemcpyAsync(dst + 2 * mat, x.w_down, mat, hipMemcpyDeviceToDevice, s));
+    }
+  }
+  return MOE_OK;
+}
+
+moe_status moe_router(const moe_config* cfg, int64_t T, const void* x, const void* norm_w,
+                      const void* w_router, const float* bias, int32_t* topk_ids, float* topk_w,
+                      float* gap, void* xq, float* xs, void* ws, size_t ws_bytes, void* stream) {
+  Dims D;
+  moe_status st = check_cfg(cfg, &D);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(T, &D)) != MOE_OK) return st;
+  K2_PTR(x, "x");
+  K2_PTR(norm_w, "norm_w");
+  if (!D.dense) {
+    K2_PTR(w_router, "w_router");
+    K2_PTR(bias, "bias");
+  }
+  K2_PTR(topk_ids, "topk_ids");
+  K2_PTR(topk_w, "topk_w");
+  K2_OPT_PTR(gap, "gap");
+  K2_PTR(xq, "xq");
+  if (D.fp8) K2_PTR(xs, "xs");
+  else K2_REQUIRE(xs == nullptr, MOE_ERR_INVALID_ARG, "xs must be NULL in the F32 format");
+  const Layout L = layout(D, MOE_WS_ROUTER);
+  K2_REQUIRE(ws_bytes >= L.total, MOE_ERR_WORKSPACE, "workspace too small");
+  if (L.total) K2_PTR(ws, "ws");
+  if (T == 0) return MOE_OK;
+  return run_router(D, L, ws, x, norm_w, w_router, bias, topk_ids, topk_w, gap, xq, xs,
+                    static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_permute(const moe_config* cfg, int64_t T, const int32_t* topk_ids,
+                       int32_t* expert_offsets, int32_t* row_pair, int32_t* pair_row, void* ws,
+                       size_t ws_bytes, void* stream) {
+  Dims D;
+  moe_status st = check_cfg(cfg, &D);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(T, &D)) != MOE_OK) return st;
+  K2_PTR(topk_ids, "topk_ids");
+  K2_PTR(expert_offsets, "expert_offsets");
+  K2_PTR(row_pair, "row_pair");
+  K2_PTR(pair_row, "pair_row");
+  const Layout L = layout(D, MOE_WS_PERMUTE);
+  K2_REQUIRE(ws_bytes >= L.total, MOE_ERR_WORKSPACE, "workspace too small");
+  if (L.total) K2_PTR(ws, "ws");
+  if (T == 0) return MOE_OK;
+  return run_permute(D, L, ws, topk_ids, expert_offsets, row_pair, pair_row,
+                     static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_grouped_swiglu(const moe_config* cfg, int64_t T, const void* xq, const float* xs,
+                              const int32_t* expert_offsets, const int32_t* row_pair,
+                              const void* packed_w, float* rows, float* shared_out, void* ws,
+                              size_t ws_bytes, void* stream) {
+  Dims D;
+  moe_status st = check_cfg(cfg, &D);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(T, &D)) != MOE_OK) return st;
+  K2_PTR(xq, "xq");
+  if (D.fp8) K2_PTR(xs, "xs");
+  K2_PTR(expert_offsets, "expert_offsets");
+  K2_PTR(row_pair, "row_pair");
+  K2_PTR(packed_w, "packed_w");
+  K2_PTR(rows, "rows");
+  if (D.S) K2_PTR(shared_out, "shared_out");
+  else K2_REQUIRE(shared_out == nullptr, MOE_ERR_INVALID_ARG,
+                  "shared_out must be NULL without a shared expert");
+  const Layout L = layout(D, MOE_WS_SWIGLU);
+  K2_REQUIRE(ws_bytes >= L.total, MOE_ERR_WORKSPACE, "workspace too small");
+  if (L.total) K2_PTR(ws, "ws");
+  if (T == 0) return MOE_OK;
+  return run_experts(D, L, ws, xq, xs, expert_offsets, row_pair, packed_w, rows, shared_out,
+                     nullptr, 0, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_combine(const moe_config* cfg, int64_t T, const float* rows,
+                       const int32_t* pair_row, const float* topk_w, const float* shared_out,
+                       const void* residual, void* out, int32_t out_f32, void* stream) {
+  Dims D;
+  moe_status st = check_cfg(cfg, &D);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(T, &D)) != MOE_OK) return st;
+  K2_PTR(rows, "rows");
+  K2_PTR(pair_row, "pair_row");
+  K2_PTR(topk_w, "topk_w");
+  if (D.S) K2_PTR(shared_out, "shared_out");
+  else K2_REQUIRE(shared_out == nullptr, MOE_ERR_INVALID_ARG,
+                  "shared_out must be NULL without a shared expert");
+  K2_OPT_PTR(residual, "residual");
+  K2_PTR(out, "out");
+  K2_REQUIRE(out_f32 == 0 || out_f32 == 1, MOE_ERR_INVALID_ARG, "out_f32 must be 0 or 1");
+  if (T == 0) return MOE_OK;
+  Stage stg(MOE_STAGE_COMBINE, static_cast<hipStream_t>(stream));
+  K2_HIP(k2::launch_combine(D.fp8, !D.fp8 || out_f32, (int)T, D.d, D.k, rows, pair_row, topk_w,
+                            1, shared_out, residual, out, static_cast<hipStream_t>(stream)));
+  return MOE_OK;
+}
+
+moe_status moe_forward(const moe_config* cfg, int64_t T, const void* x, const void* norm_w,
+                       const void* w_router, const float* bias, const void* packed_w, void* out,
+                       void* ws, size_t ws_bytes, void* stream) {
+  Dims D;
+  moe_status st = check_cfg(cfg, &D);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(T, &D)) != MOE_OK) return st;
+  K2_PTR(x, "x");
+  K2_PTR(norm_w, "norm_w");
+  if (!D.dense) {
+    K2_PTR(w_router, "w_router");
+    K2_PTR(bias, "bias");
+  }
+  K2_PTR(packed_w, "packed_w");
+  K2_PTR(out, "out");
+  const Layout L = layout(D, MOE_WS_FORWARD);
+  K2_REQUIRE(ws_bytes >= L.total, MOE_ERR_WORKSPACE, "workspace too small");
+  if (L.total) K2_PTR(ws, "ws");
+  if (T == 0) return MOE_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void* xq = at<void>(ws, L.xq);
+  float* xs = D.fp8 ? at<float>(ws, L.xs) : nullptr;
+  int32_t* ids = at<int32_t>(ws, L.ids);
+  float* w = at<float>(ws, L.w);
+  float* gap = at<float>(ws, L.gap);
+  int32_t* offsets = at<int32_t>(ws, L.offsets);
+  int32_t* row_pair = at<int32_t>(ws, L.row_pair);
+  int32_t* pair_row = at<int32_t>(ws, L.pair_row);
+  float* rows = at<float>(ws, L.rows);
+  float* shared = D.S ? at<float>(ws, L.shared) : nullptr;
+  if ((st = run_router(D, L, ws, x, norm_w, w_router, bias, ids, w, gap, xq, xs, s)) != MOE_OK)
+    return st;
+  if ((st = run_permute(D, L, ws, ids, offsets, row_pair, pair_row, s)) != MOE_OK) return st;
+  if ((st = run_experts(D, L, ws, xq, xs, offsets, row_pair, packed_w, rows, shared, w, 1, s)) !=
+      MOE_OK)
+    return st;
+  Stage stg(MOE_STAGE_COMBINE, s);
+  K2_HIP(k2::launch_combine(D.fp8, !D.fp8, (int)T, D.d, D.k, rows, pair_row, w, 0, shared, x, out,
+                            s));
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,326 @@
+// RMSNorm + 1x128 FP8 activation quantisation, the bf16 router GEMM and the
+// sigmoid / correction-bias top-k selection of the K2 MoE layer.
+//
+// RMSNorm ("Kimi-K2-Base", Normalization and stability: RMSNorm, pre-norm,
+// eps 1e-6): ms = mean(x^2) rounded to fp32 (formed in fp64, so the rounding
+// does not depend on the reduction order), r = 1/sqrt(ms + eps) with IEEE
+// fp32 ops, h = bf16((x * r) * gamma).
+// Quantisation ("Kimi K2 · Architecture", config.json quantization_config,
+// activation_scheme dynamic; "Kimi-K2-Base", Training precision, 1x128 tiles
+// with fp32 scales): per token and 128 columns, s = amax/448,
+// q = e4m3(clamp(h/s, +-448)) with IEEE division.
+// Router ("Kimi-K2-Base", Mixture of experts): z = h . W_r^T (bf16 inputs,
+// fp32 accumulate), s = sigmoid(z), the correction bias is added for the
+// choice only, top-k with one group, weights = s / sum(s) * scaling.
+#include "k2_common.h"
+#include "k2_launch.h"
+
+namespace k2 {
+
+namespace {
+
+constexpr int NQ_THREADS = 256;
+constexpr int NQ_MAXIT = 8;  // d <= 8 * 256 * 8 = 16384
+
+template <bool FP8>
+__global__ __launch_bounds__(NQ_THREADS) void norm_quant_kernel(int d, float eps,
+                                                                const void* __restrict__ x,
+                                                                const void* __restrict__ gamma,
+                                                                uint16_t* __restrict__ hbuf,
+                                                                void* __restrict__ xq,
+                                                                float* __restrict__ xs) {
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nch = d >> 3;  // chunks of 8 elements
+  float v[NQ_MAXIT][8];
+  double ss = 0.0;
+#pragma unroll
+  for (int it = 0; it < NQ_MAXIT; ++it) {
+    const int c = tid + NQ_THREADS * it;
+    if (c < nch) {
+      if constexpr (FP8) {
+        const uint4 p = reinterpret_cast<const uint4*>(
+            static_cast<const uint16_t*>(x) + (size_t)t * d)[c];
+        const uint32_t w4[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v[it][2 * j] = bf16_to_f32(w4[j] & 0xFFFFu);
+          v[it][2 * j + 1] = bf16_to_f32(w4[j] >> 16);
+        }
+      } else {
+        const float4* xp = reinterpret_cast<const float4*>(
+            static_cast<const float*>(x) + (size_t)t * d + (size_t)c * 8);
+        const float4 a = xp[0], b = xp[1];
+        v[it][0] = a.x; v[it][1] = a.y; v[it][2] = a.z; v[it][3] = a.w;
+        v[it][4] = b.x; v[it][5] = b.y; v[it][6] = b.z; v[it][7] = b.w;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ss += (double)v[it][j] * (double)v[it][j];
+    }
+  }
+  __shared__ double red[NQ_THREADS / WAVE];
+  ss = wave_sum(ss);
+  if (lane == 0) red[wave] = ss;
+  __syncthreads();
+  double tot = 0.0;
+#pragma unroll
+  for (int w = 0; w < NQ_THREADS / WAVE; ++w) tot += red[w];
+  const float ms = (float)(tot / (double)d);
+  const float r = 1.0f / sqrtf(ms + eps);
+
+#pragma unroll
+  for (int it = 0; it < NQ_MAXIT; ++it) {
+    const int c = tid + NQ_THREADS * it;
+    if (c < nch) {
+      float h[8];
+      if constexpr (FP8) {
+        const uint4 gp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(gamma))[c];
+        const uint32_t g4[4] = {gp.x, gp.y, gp.z, gp.w};
+        uint32_t hb[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float g0 = bf16_to_f32(g4[j] & 0xFFFFu), g1 = bf16_to_f32(g4[j] >> 16);
+          const uint32_t b0 = f32_to_bf16_rne((v[it][2 * j] * r) * g0);
+          const uint32_t b1 = f32_to_bf16_rne((v[it][2 * j + 1] * r) * g1);
+          h[2 * j] = bf16_to_f32(b0);
+          h[2 * j + 1] = bf16_to_f32(b1);
+          hb[j] = b0 | (b1 << 16);
+        }
+        reinterpret_cast<uint4*>(hbuf + (size_t)t * d)[c] = make_uint4(hb[0], hb[1], hb[2], hb[3]);
+        // 16 consecutive lanes hold one 128-column block
+        float amax = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(h[j]));
+#pragma unroll
+        for (int m = 1; m < 16; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
+        const float sc = fp8_scale(amax);
+        const uint32_t q0 = cvt4_e4m3(clamp_fp8(h[0] / sc), clamp_fp8(h[1] / sc),
+                                      clamp_fp8(h[2] / sc), clamp_fp8(h[3] / sc));
+        const uint32_t q1 = cvt4_e4m3(clamp_fp8(h[4] / sc), clamp_fp8(h[5] / sc),
+                                      clamp_fp8(h[6] / sc), clamp_fp8(h[7] / sc));
+        reinterpret_cast<uint2*>(static_cast<uint8_t*>(xq) + (size_t)t * d)[c] =
+            make_uint2(q0, q1);
+        if ((c & 15) == 0) xs[(size_t)t * (d / QBLK) + (c >> 4)] = sc;
+      } else {
+        const float* gp = static_cast<const float*>(gamma) + (size_t)c * 8;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) h[j] = (v[it][j] * r) * gp[j];
+        float4* op = reinterpret_cast<float4*>(static_cast<float*>(xq) + (size_t)t * d +
+                                               (size_t)c * 8);
+        op[0] = make_float4(h[0], h[1], h[2], h[3]);
+        op[1] = make_float4(h[4], h[5], h[6], h[7]);
+      }
+    }
+  }
+}
+
+// z partial sums: zpart[ks][t][e] over columns [ks*kchunk, (ks+1)*kchunk).
+// Workgroup: 64 tokens x 64 experts; wave w owns tokens 16w..16w+15 and four
+// 16x16 MFMA tiles over the 64 experts (A = router rows, B = tokens).
+__global__ __launch_bounds__(256) void router_gemm_bf16_kernel(int T, int d, int E, int kchunk,
+                                                              const uint16_t* __restrict__ h,
+                                                              const uint16_t* __restrict__ wr,
+                                                              float* __restrict__ zpart) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t0 = blockIdx.x * 64 + wave * 16;
+  const int e0 = blockIdx.y * 64;
+  const int ks = blockIdx.z;
+  const int kbeg = ks * kchunk;
+  const int tok = min(t0 + (lane & 15), T - 1);
+  const int kl = (lane >> 4) * 8;
+  const uint16_t* hp = h + (size_t)tok * d + kbeg + kl;
+  const uint16_t* wp[4];
+  bool fon[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    fon[f] = e0 + 16 * f < E;
+    const int e = min(e0 + 16 * f + (lane & 15), E - 1);
+    wp[f] = wr + (size_t)e * d + kbeg + kl;
+  }
+  v4f acc[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) acc[f] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+  for (int kk = 0; kk < kchunk; kk += 32) {
+    const v8bf b = *reinterpret_cast<const v8bf*>(hp + kk);
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      if (fon[f]) {
+        const v8bf a = *reinterpret_cast<const v8bf*>(wp[f] + kk);
+        acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[f], 0, 0, 0);
+      }
+    }
+  }
+  // lane holds rows (experts) 4*(lane/16)+r of each tile, column (token) lane%16
+  const int tt = t0 + (lane & 15);
+  if (tt < T) {
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      if (fon[f]) {
+        const int e = e0 + 16 * f + 4 * (lane >> 4);
+        float4* zp = reinterpret_cast<float4*>(zpart + ((size_t)ks * T + tt) * E + e);
+        *zp = make_float4(acc[f][0], acc[f][1], acc[f][2], acc[f][3]);
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void router_gemm_f32_kernel(int T, int d, int E,
+                                                             const float* __restrict__ h,
+                                                             const float* __restrict__ wr,
+                                                             float* __restrict__ z) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= T * E) return;
+  const int t = i / E, e = i - t * E;
+  const float* hp = h + (size_t)t * d;
+  const float* wp = wr + (size_t)e * d;
+  float acc = 0.f;
+  for (int j = 0; j < d; ++j) acc = fmaf(hp[j], wp[j], acc);
+  z[i] = acc;
+}
+
+// Order-preserving map of an fp32 value to uint32 (larger float -> larger key).
+__device__ __forceinline__ uint32_t ordered_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float unordered_bits(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+
+constexpr int TK_WAVES = 4;
+
+// One wavefront per token.  Key = (ordered biased score << 32) | ~expert, so
+// the wave maximum is the highest score and, on equal scores, the lower id.
+template <int MAXJ, int MAXK>
+__global__ __launch_bounds__(TK_WAVES * 64) void topk_kernel(int T, int E, int k, int ksplit,
+                                                            const float* __restrict__ zpart,
+                                                            const float* __restrict__ bias,
+                                                            float scaling, int renorm,
+                                                            int32_t* __restrict__ ids,
+                                                            float* __restrict__ wout,
+                                                            float* __restrict__ gap) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t_raw = blockIdx.x * TK_WAVES + wave;
+  const int t = min(t_raw, T - 1);
+  __shared__ float s_sh[TK_WAVES][MAXJ * 64];
+  uint64_t key[MAXJ];
+#pragma unroll
+  for (int j = 0; j < MAXJ; ++j) {
+    const int e = lane + 64 * j;
+    key[j] = 0;
+    if (e < E) {
+      float z = 0.f;
+      for (int ks = 0; ks < ksplit; ++ks) z += zpart[((size_t)ks * T + t) * E + e];
+      const float s = (float)(1.0 / (1.0 + exp(-(double)z)));
+      const float sb = s + bias[e];
+      s_sh[wave][e] = s;
+      key[j] = ((uint64_t)ordered_bits(sb) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
+    }
+  }
+  __syncthreads();
+  int sel[MAXK];
+  float sel_sb[MAXK + 1];
+  const int rounds = min(k + 1, E);
+#pragma unroll
+  for (int r = 0; r < MAXK + 1; ++r) {
+    if (r < rounds) {
+      uint64_t best = 0;
+#pragma unroll
+      for (int j = 0; j < MAXJ; ++j) best = key[j] > best ? key[j] : best;
+      best = wave_max(best);
+#pragma unroll
+      for (int j = 0; j < MAXJ; ++j)
+        if (key[j] == best) key[j] = 0;
+      if (r < MAXK) sel[r] = (int)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFu));
+      sel_sb[r] = unordered_bits((uint32_t)(best >> 32));
+    }
+  }
+  // ascending ids: lane r < k places its expert at its rank among the chosen
+  int my_e = 0;
+  double my_s = 0.0;
+#pragma unroll
+  for (int r = 0; r < MAXK; ++r)
+    if (r < k && lane == r) my_e = sel[r];
+  int rank = 0;
+#pragma unroll
+  for (int r = 0; r < MAXK; ++r)
+    if (r < k && sel[r] < my_e) ++rank;
+  float s_me = 0.f;
+  if (lane < k) {
+    s_me = s_sh[wave][my_e];
+    my_s = (double)s_me;
+  }
+  const float denom = (float)wave_sum(my_s);
+  if (t_raw < T) {
+    if (lane < k) {
+      const float wv = renorm ? (s_me / denom) * scaling : s_me * scaling;
+      ids[(size_t)t * k + rank] = my_e;
+      wout[(size_t)t * k + rank] = wv;
+    }
+    if (gap != nullptr && lane == 0) {
+      float g = __builtin_inff();
+#pragma unroll
+      for (int r = 0; r < MAXK; ++r)
+        if (r == k - 1 && k < E) g = sel_sb[r] - sel_sb[r + 1];
+      gap[t] = g;
+    }
+  }
+}
+
+__global__ void dense_route_kernel(int T, float scaling, int32_t* ids, float* w, float* gap) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= T) return;
+  ids[t] = 0;
+  w[t] = scaling;
+  if (gap) gap[t] = __builtin_inff();
+}
+
+}  // namespace
+
+hipError_t launch_norm_quant(bool fp8, int T, int d, float eps, const void* x, const void* gamma,
+                             void* hbuf, void* xq, float* xs, hipStream_t s) {
+  if (fp8)
+    norm_quant_kernel<true><<<T, NQ_THREADS, 0, s>>>(d, eps, x, gamma,
+                                                     static_cast<uint16_t*>(hbuf), xq, xs);
+  else
+    norm_quant_kernel<false><<<T, NQ_THREADS, 0, s>>>(d, eps, x, gamma, nullptr, xq, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_gemm_bf16(int T, int d, int E, int ksplit, const uint16_t* h,
+                                   const uint16_t* wr, float* zpart, hipStream_t s) {
+  dim3 grid((T + 63) / 64, (E + 63) / 64, ksplit);
+  router_gemm_bf16_kernel<<<grid, 256, 0, s>>>(T, d, E, d / ksplit, h, wr, zpart);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_gemm_f32(int T, int d, int E, const float* h, const float* wr,
+                                  float* zpart, hipStream_t s) {
+  const long n = (long)T * E;
+  router_gemm_f32_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(T, d, E, h, wr, zpart);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(int T, int E, int k, int ksplit, const float* zpart, const float* bias,
+                       float scaling, int renorm, int32_t* ids, float* w, float* gap,
+                       hipStream_t s) {
+  const unsigned grid = (unsigned)((T + TK_WAVES - 1) / TK_WAVES);
+#define K2_TOPK(J, K)                                                                      \
+  topk_kernel<J, K><<<grid, TK_WAVES * 64, 0, s>>>(T, E, k, ksplit, zpart, bias, scaling, \
+                                                   renorm, ids, w, gap)
+  if (E <= 64 && k <= 8) K2_TOPK(1, 8);
+  else if (E <= 384 && k <= 8) K2_TOPK(6, 8);
+  else if (E <= 1024 && k <= 32) K2_TOPK(16, 32);
+  else return hipErrorInvalidValue;
+#undef K2_TOPK
+  return hipGetLastError();
+}
+
+hipError_t launch_dense_route(int T, float scaling, int32_t* ids, float* w, float* gap,
+                              hipStream_t s) {
+  dense_route_kernel<<<(T + 255) / 256, 256, 0, s>>>(T, scaling, ids, w, gap);
+  return hipGetLastError();
+}
+
+}  // namespace k2

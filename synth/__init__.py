@@ -1,7 +1,8 @@
 """Seeded synthetic workloads for the K2 MoE layer (shapes and input recipe only)."""
 from .configs import (ALL, FMT_F32, FMT_FP8, K2_DECODE, K2_DENSE, K2_PREFILL, K2_SKEWED,
                       TINY, MoEShape, small_fp8)
-from .gen import MoEInputs, block_quantize_weight, generate
+from .gen import MoEInputs, block_quantize_weight, generate, with_workload
 
 __all__ = ["ALL", "FMT_F32", "FMT_FP8", "K2_DECODE", "K2_DENSE", "K2_PREFILL", "K2_SKEWED",
-           "TINY", "MoEShape", "small_fp8", "MoEInputs", "block_quantize_weight", "generate"]
+           "TINY", "MoEShape", "small_fp8", "MoEInputs", "block_quantize_weight", "generate",
+           "with_workload"]

@@ -144,3 +144,24 @@ def generate(shape: MoEShape, seed: int = 0, device="cpu", tokens: Optional[int]
                 wt[e].copy_(w)
             del w
     return MoEInputs(shape, x, norm_w, w_router, bias, w_gate, w_up, w_down, s_gate, s_up, s_down)
+
+
+def with_workload(base: MoEInputs, shape: MoEShape, seed: int = 0,
+                  tokens: Optional[int] = None) -> MoEInputs:
+    """Inputs of ``shape`` that reuse ``base``'s expert and router weights.
+
+    Expert and router weights depend only on the seed and the layer
+    dimensions, so workloads of one layer (decode, prefill, skewed routing)
+    share them; x is drawn for the new token count and the bias from the
+    new shape's recipe.
+    """
+    b = base.shape
+    assert (b.d_model, b.n_experts, b.n_shared, b.d_ff, b.fmt) == \
+        (shape.d_model, shape.n_experts, shape.n_shared, shape.d_ff, shape.fmt)
+    device = base.x.device
+    T = shape.tokens if tokens is None else tokens
+    act_dtype = base.x.dtype
+    x = _randn((T, shape.d_model), shape.x_std, device, seed, ROLE_X).to(act_dtype)
+    bias = None if shape.dense else bias_vector(shape, seed, device)
+    return MoEInputs(shape, x, base.norm_w, base.w_router, bias, base.w_gate, base.w_up,
+                     base.w_down, base.s_gate, base.s_up, base.s_down)

@@ -1,0 +1,161 @@
+"""Host-side checks of the C ABI: symbols, sizes and argument validation.
+
+Runs without a GPU.  Every call here either fails validation or has T = 0,
+so the library returns before making any HIP call.
+"""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+import synth
+from sparse_moe_transformer_sigmoid_amd import _lib as L
+from sparse_moe_transformer_sigmoid_amd.build import lib_path
+from sparse_moe_transformer_sigmoid_amd.layer import config_from_shape
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "k2moe.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(lib_path()),
+                                reason="libk2moe.so not built")
+
+FAKE = 0x10000          # aligned non-null stand-in; never dereferenced (validation fails first)
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = _declared_functions()
+    assert set(names) == set(L.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", lib_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (moe_\w+)", out))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    lib = L.load()
+    for n in names:
+        assert getattr(lib, n) is not None
+
+
+def _cfg(shape=synth.K2_DECODE, **kw):
+    c = config_from_shape(shape)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def test_status_strings():
+    lib = L.load()
+    assert lib.moe_status_str(0) == b"MOE_OK"
+    assert lib.moe_status_str(3) == b"MOE_ERR_WORKSPACE"
+
+
+def test_packed_bytes_match_page_expert_size():
+    lib = L.load()
+    cfg = _cfg()
+    n = lib.moe_packed_weights_bytes(C.byref(cfg))
+    per_expert = 3 * 2048 * 7168          # 44,040,192 FP8 weights per expert
+    assert per_expert == 44_040_192
+    scales = 385 * (16 * 56 * 2 + 56 * 16) * 4
+    assert 385 * per_expert + scales <= n < 385 * per_expert + scales + 3 * 256
+    bad = _cfg(n_group=2)
+    assert lib.moe_packed_weights_bytes(C.byref(bad)) == 0
+
+
+def test_workspace_sizes_monotone_in_tokens():
+    cfg = _cfg()
+    sizes = []
+    for T in (0, 1, 64, 8192):
+        n = C.c_size_t()
+        L.call("moe_workspace_bytes", C.byref(cfg), T, L.MOE_WS_FORWARD, C.byref(n))
+        sizes.append(n.value)
+    assert sizes == sorted(sizes) and sizes[-1] > 8192 * 8 * 7168 * 4
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("n_group", 2, L.MOE_ERR_UNSUPPORTED),
+    ("topk_group", 4, L.MOE_ERR_UNSUPPORTED),
+    ("fmt", 7, L.MOE_ERR_UNSUPPORTED),
+    ("top_k", 0, L.MOE_ERR_INVALID_ARG),
+    ("top_k", 385, L.MOE_ERR_INVALID_ARG),
+    ("n_shared", 2, L.MOE_ERR_UNSUPPORTED),
+    ("d_model", 7168 + 128, L.MOE_ERR_UNSUPPORTED),
+    ("d_ff", 2048 + 64, L.MOE_ERR_UNSUPPORTED),
+    ("n_experts", 392 + 4, L.MOE_ERR_UNSUPPORTED),
+    ("dense", 1, L.MOE_ERR_INVALID_ARG),
+])
+def test_config_validation(field, value, status):
+    cfg = _cfg(**{field: value})
+    n = C.c_size_t()
+    assert L.status_of("moe_workspace_bytes", C.byref(cfg), 8, 0, C.byref(n)) == status
+    assert L.load().moe_last_error()
+
+
+def _forward_args(cfg, T=4, ws_bytes=1 << 40, **over):
+    args = dict(x=FAKE, norm_w=FAKE, w_router=FAKE, bias=FAKE, packed=FAKE, out=FAKE, ws=FAKE)
+    args.update(over)
+    return (C.byref(cfg), T, args["x"], args["norm_w"], args["w_router"], args["bias"],
+            args["packed"], args["out"], args["ws"], ws_bytes, None)
+
+
+@pytest.mark.parametrize("name", ["x", "norm_w", "w_router", "bias", "packed", "out", "ws"])
+def test_forward_rejects_null_pointer(name):
+    cfg = _cfg()
+    assert L.status_of("moe_forward", *_forward_args(cfg, **{name: None})) == L.MOE_ERR_INVALID_ARG
+
+
+def test_forward_rejects_misaligned_pointer():
+    cfg = _cfg()
+    assert L.status_of("moe_forward", *_forward_args(cfg, x=FAKE + 2)) == L.MOE_ERR_INVALID_ARG
+
+
+def test_forward_small_workspace_and_negative_tokens():
+    cfg = _cfg()
+    n = C.c_size_t()
+    L.call("moe_workspace_bytes", C.byref(cfg), 64, L.MOE_WS_FORWARD, C.byref(n))
+    assert L.status_of("moe_forward", *_forward_args(cfg, T=64, ws_bytes=n.value - 1)) == \
+        L.MOE_ERR_WORKSPACE
+    assert L.status_of("moe_forward", *_forward_args(cfg, T=-1)) == L.MOE_ERR_INVALID_ARG
+
+
+def test_zero_tokens_is_a_no_op():
+    cfg = _cfg()
+    assert L.status_of("moe_forward", *_forward_args(cfg, T=0, ws_bytes=0)) == L.MOE_OK
+    assert L.status_of("moe_permute", C.byref(cfg), 0, FAKE, FAKE, FAKE, FAKE, FAKE, 0,
+                       None) == L.MOE_OK
+
+
+def test_dense_mode_allows_missing_router():
+    cfg = _cfg(synth.K2_DENSE)
+    assert L.status_of("moe_forward", *_forward_args(cfg, T=0, w_router=None, bias=None,
+                                                     ws_bytes=0)) == L.MOE_OK
+    cfg2 = _cfg()
+    assert L.status_of("moe_forward", *_forward_args(cfg2, T=0, w_router=None)) == \
+        L.MOE_ERR_INVALID_ARG
+
+
+def test_router_f32_requires_null_scales():
+    cfg = _cfg(synth.TINY)
+    st = L.status_of("moe_router", C.byref(cfg), 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                     FAKE, FAKE, FAKE, 1 << 30, None)
+    assert st == L.MOE_ERR_INVALID_ARG
+
+
+def test_swiglu_shared_out_must_match_config():
+    cfg = _cfg()
+    st = L.status_of("moe_grouped_swiglu", C.byref(cfg), 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                     None, FAKE, 1 << 40, None)
+    assert st == L.MOE_ERR_INVALID_ARG
+
+
+def test_pack_rejects_wrong_expert_count():
+    cfg = _cfg(synth.TINY)
+    arr = (L.moe_expert_w * 3)()
+    assert L.status_of("moe_pack_weights", C.byref(cfg), arr, 3, FAKE, None) == \
+        L.MOE_ERR_INVALID_ARG
