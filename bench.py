@@ -92,6 +92,7 @@ def routing_stats(layer, x):
 def run_workload(layer, inp, steps, warmup):
     shape = inp.shape
     T = inp.x.shape[0]
+    layer.use_router(inp)
     ms, stage = timed(layer, inp.x, steps, warmup)
     touched, counts = routing_stats(layer, inp.x)
     touched_all = touched + shape.n_shared

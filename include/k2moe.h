@@ -18,15 +18,19 @@
  * Training precision).
  *
  * Conventions for every entry point:
- *  - All tensor pointers are DEVICE pointers owned by the caller, row-major,
- *    16-byte aligned.  Nothing here allocates device memory except through
+ *  - All tensor pointers are DEVICE pointers owned by the caller, row-major.
+ *    Buffers the kernels access in vectors (x, norm_w, w_router, xq, rows,
+ *    shared_out, residual, out, packed weights, workspace, expert codes) must
+ *    be 16-byte aligned; scales, bias, ids, weights, gap and index arrays
+ *    4-byte aligned.  Nothing here allocates device memory except through
  *    the caller's workspace, and nothing is kept between calls.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
  *    enqueues work on it and returns without synchronising; device faults
  *    surface at the caller's next synchronisation.
  *  - Arguments are validated on the host before any HIP call; on error
  *    nothing is enqueued and moe_last_error() describes the problem.
- *  - T (tokens) = 0 is valid and enqueues nothing.
+ *  - T (tokens) = 0 is valid: tensor pointers are not examined and nothing
+ *    is enqueued.
  *  - Results are bitwise deterministic: no floating-point atomics.
  *
  * Formats (moe_config.fmt):
@@ -162,11 +166,16 @@ moe_status moe_permute(const moe_config* cfg, int64_t T, const int32_t* topk_ids
  *  xq, xs: from moe_router.  expert_offsets, row_pair: from moe_permute.
  *  packed_w: from moe_pack_weights.
  *  rows [T*k, d] fp32: unweighted expert output of each permuted row.
- *  shared_out [T, d] fp32: shared expert output; NULL iff n_shared == 0. */
+ *  shared_out [T, d] fp32: shared expert output; NULL iff n_shared == 0.
+ *  act_q, act_s (nullable, FP8 format only, both or neither): where the
+ *  requantised SwiGLU activations of the permuted rows go, instead of the
+ *  workspace: act_q [T*k + n_shared*T, d_ff] e4m3 codes, act_s [same rows,
+ *  d_ff/128] fp32 scales; the shared expert's rows follow the routed ones. */
 moe_status moe_grouped_swiglu(const moe_config* cfg, int64_t T, const void* xq,
                               const float* xs, const int32_t* expert_offsets,
                               const int32_t* row_pair, const void* packed_w, float* rows,
-                              float* shared_out, void* ws, size_t ws_bytes, void* stream);
+                              float* shared_out, void* act_q, float* act_s, void* ws,
+                              size_t ws_bytes, void* stream);
 
 /* Weighted combine plus residual ("Kimi K2 · Dense transformer block", Code:
  * residual add after the MLP).  For each token, in ascending expert order:

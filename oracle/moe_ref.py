@@ -199,12 +199,16 @@ def swiglu_expert(hrows: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndar
     a = silu_mul(g, u)
     if fp8:
         a_codes, a_scales = quantize_1x128(a)
-        a_in = dequantize_1x128(a_codes, a_scales)
+        o = down_projection(a_codes, a_scales, wd)
     else:
         a_codes = a_scales = None
-        a_in = a.astype(np.float64)
-    o = f32(a_in @ wd.T)
+        o = f32(a.astype(np.float64) @ wd.T)
     return o, a, a_codes, a_scales
+
+
+def down_projection(a_codes: np.ndarray, a_scales: np.ndarray, wd: np.ndarray) -> np.ndarray:
+    """o = dequant(a) . W_down^T from requantised SwiGLU activations (exact, to fp32)."""
+    return f32(dequantize_1x128(a_codes, a_scales) @ wd.T)
 
 
 # ----------------------------------------------------------------- layer ---
@@ -220,7 +224,8 @@ def _expert_f64(wts: dict, fp8: bool):
 def moe_layer(p: LayerParams, x: np.ndarray, norm_w: np.ndarray,
               w_router: Optional[np.ndarray], bias: Optional[np.ndarray],
               expert: Callable[[int], dict], tokens: Optional[np.ndarray] = None,
-              ids_override: Optional[np.ndarray] = None) -> dict:
+              ids_override: Optional[np.ndarray] = None,
+              act_override: Optional[dict] = None) -> dict:
     """Full sub-layer: out = x + MoE(RMSNorm(x)).
 
     x, norm_w, w_router: float32 arrays holding the (exact) values of the
@@ -230,6 +235,14 @@ def moe_layer(p: LayerParams, x: np.ndarray, norm_w: np.ndarray,
     expert outputs, y and out are computed for ``tokens`` (default: all).
     ids_override replaces the selected sets (weights still come from the
     oracle's own unbiased scores).
+
+    act_override (FP8 layer) gives requantised SwiGLU activations to feed the
+    down projections instead of the oracle's own: a dict with "codes"
+    [n, k, d_ff], "scales" [n, k, d_ff/128] for the routed pairs of the
+    selected tokens and "shared_codes" / "shared_scales" [n, ...] for the
+    shared expert.  Each e4m3 code is a decision taken on an fp32 value; this
+    evaluates the rest of the layer on another implementation's decisions.
+    The results then also hold o_pairs_ov, shared_ov, y_ov and out_ov.
     """
     T = x.shape[0]
     k, E = p.top_k, p.n_experts
@@ -259,33 +272,46 @@ def moe_layer(p: LayerParams, x: np.ndarray, norm_w: np.ndarray,
     used = res["used_ids"][sel]
     wsel = res["w"][sel]
     n = len(sel)
-    o_pairs = np.zeros((n, used.shape[1], p.d_model), dtype=np.float32)
-    a_pairs = np.zeros((n, used.shape[1], p.d_ff), dtype=np.float32)
+    kk = used.shape[1]
+    ov = act_override is not None
+    o_pairs = np.zeros((n, kk, p.d_model), dtype=np.float32)
+    a_pairs = np.zeros((n, kk, p.d_ff), dtype=np.float32)
+    o_pairs_ov = np.zeros_like(o_pairs) if ov else None
     for e in np.unique(used):
         ti, si = np.nonzero(used == e)
         wg, wu, wd = _expert_f64(expert(int(e)), p.fp8)
         o, a, _, _ = swiglu_expert(hin[ti], wg, wu, wd, p.fp8)
         o_pairs[ti, si] = o
         a_pairs[ti, si] = a
+        if ov:
+            o_pairs_ov[ti, si] = down_projection(act_override["codes"][ti, si],
+                                                 act_override["scales"][ti, si], wd)
         del wg, wu, wd
-    shared = np.zeros((n, p.d_model), dtype=np.float32)
-    shared_parts = []
+    shared_parts, shared_parts_ov = [], []
     for j in range(p.n_shared):
         wg, wu, wd = _expert_f64(expert(E + j), p.fp8)
         o, _, _, _ = swiglu_expert(hin, wg, wu, wd, p.fp8)
         shared_parts.append(o)
+        if ov:
+            shared_parts_ov.append(down_projection(act_override["shared_codes"],
+                                                   act_override["shared_scales"], wd))
         del wg, wu, wd
-    y64 = np.einsum("ts,tsd->td", wsel.astype(np.float64), o_pairs.astype(np.float64))
-    for o in shared_parts:
-        y64 = y64 + o.astype(np.float64)
-    if shared_parts:
-        shared = f32(np.sum([o.astype(np.float64) for o in shared_parts], axis=0))
-    y = f32(y64)
-    xo = f32(x[sel])
-    out = f32(xo + y)
-    if p.fp8:
-        out = bf16_round(out)
+
+    def combine(o_pairs_, parts):
+        y64 = np.einsum("ts,tsd->td", wsel.astype(np.float64), o_pairs_.astype(np.float64))
+        for o in parts:
+            y64 = y64 + o.astype(np.float64)
+        sh = (f32(np.sum([o.astype(np.float64) for o in parts], axis=0)) if parts
+              else np.zeros((n, p.d_model), dtype=np.float32))
+        y_ = f32(y64)
+        out_ = f32(f32(x[sel]) + y_)
+        return sh, y_, (bf16_round(out_) if p.fp8 else out_)
+
+    shared, y, out = combine(o_pairs, shared_parts)
     res.update(tokens=sel, o_pairs=o_pairs, a_pairs=a_pairs, shared=shared, y=y, out=out)
+    if ov:
+        shared_ov, y_ov, out_ov = combine(o_pairs_ov, shared_parts_ov)
+        res.update(o_pairs_ov=o_pairs_ov, shared_ov=shared_ov, y_ov=y_ov, out_ov=out_ov)
     return res
 
 

@@ -63,7 +63,8 @@ def load(path: str | None = None) -> C.CDLL:
         "moe_workspace_bytes": (i32, [cfgp, i64, i32, C.POINTER(sz)]),
         "moe_router": (i32, [cfgp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "moe_permute": (i32, [cfgp, i64, vp, vp, vp, vp, vp, sz, vp]),
-        "moe_grouped_swiglu": (i32, [cfgp, i64, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "moe_grouped_swiglu": (i32, [cfgp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                     vp]),
         "moe_combine": (i32, [cfgp, i64, vp, vp, vp, vp, vp, vp, i32, vp]),
         "moe_forward": (i32, [cfgp, i64, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "moe_profile_enable": (i32, [i32]),

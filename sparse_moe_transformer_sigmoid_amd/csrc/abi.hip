@@ -172,6 +172,18 @@ moe_status check_tokens(int64_t T, Dims* D) {
     K2_REQUIRE((p) != nullptr, MOE_ERR_INVALID_ARG, std::string(name) + " is NULL");      \
     K2_REQUIRE(aligned16(p), MOE_ERR_INVALID_ARG, std::string(name) + " is not 16-byte aligned"); \
   } while (0)
+// buffers read or written element by element need only 4-byte alignment
+#define K2_PTR4(p, name)                                                                \
+  do {                                                                                  \
+    K2_REQUIRE((p) != nullptr, MOE_ERR_INVALID_ARG, std::string(name) + " is NULL");      \
+    K2_REQUIRE((reinterpret_cast<uintptr_t>(p) & 3u) == 0, MOE_ERR_INVALID_ARG,          \
+               std::string(name) + " is not 4-byte aligned");                           \
+  } while (0)
+#define K2_OPT_PTR4(p, name)                                                            \
+  do {                                                                                  \
+    K2_REQUIRE((p) == nullptr || (reinterpret_cast<uintptr_t>(p) & 3u) == 0,            \
+               MOE_ERR_INVALID_ARG, std::string(name) + " is not 4-byte aligned");      \
+  } while (0)
 #define K2_OPT_PTR(p, name)                                                             \
   do {                                                                                  \
     K2_REQUIRE((p) == nullptr || aligned16(p), MOE_ERR_INVALID_ARG,                     \
@@ -325,7 +337,7 @@ moe_status run_permute(const Dims& D, const Layout& L, void* ws, const int32_t* 
 moe_status run_experts(const Dims& D, const Layout& L, void* ws, const void* xq, const float* xs,
                        const int32_t* offsets, const int32_t* row_pair, const void* packed_w,
                        float* rows, float* shared_out, const float* topk_w, int weighted,
-                       hipStream_t s) {
+                       void* act_q, float* act_s, hipStream_t s) {
   const int T = (int)D.T, P = (int)D.P;
   const Packed pk = packed_layout(D);
   if (!D.fp8) {
@@ -350,8 +362,8 @@ moe_status run_experts(const Dims& D, const Layout& L, void* ws, const void* xq,
     const int64_t g = (mt_bound * nc + 7) / 8 * 8;
     return (int)std::min<int64_t>(g, (int64_t)1 << 30);
   };
-  uint8_t* aq = at<uint8_t>(ws, L.aq);
-  float* as = at<float>(ws, L.as);
+  uint8_t* aq = act_q ? static_cast<uint8_t*>(act_q) : at<uint8_t>(ws, L.aq);
+  float* as = act_s ? act_s : at<float>(ws, L.as);
   const uint8_t* pw = static_cast<const uint8_t*>(packed_w);
 
   k2::GemmArgs a{};
@@ -480,9 +492,9 @@ moe_status moe_pack_weights(const moe_config* cfg, const moe_expert_w* experts,
     K2_PTR(x.w_up, nm + "w_up");
     K2_PTR(x.w_down, nm + "w_down");
     if (D.fp8) {
-      K2_PTR(x.s_gate, nm + "s_gate");
-      K2_PTR(x.s_up, nm + "s_up");
-      K2_PTR(x.s_down, nm + "s_down");
+      K2_PTR4(x.s_gate, nm + "s_gate");
+      K2_PTR4(x.s_up, nm + "s_up");
+      K2_PTR4(x.s_down, nm + "s_down");
     }
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -515,17 +527,18 @@ moe_status moe_router(const moe_config* cfg, int64_t T, const void* x, const voi
   moe_status st = check_cfg(cfg, &D);
   if (st != MOE_OK) return st;
   if ((st = check_tokens(T, &D)) != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
   K2_PTR(x, "x");
   K2_PTR(norm_w, "norm_w");
   if (!D.dense) {
     K2_PTR(w_router, "w_router");
-    K2_PTR(bias, "bias");
+    K2_PTR4(bias, "bias");
   }
-  K2_PTR(topk_ids, "topk_ids");
-  K2_PTR(topk_w, "topk_w");
-  K2_OPT_PTR(gap, "gap");
+  K2_PTR4(topk_ids, "topk_ids");
+  K2_PTR4(topk_w, "topk_w");
+  K2_OPT_PTR4(gap, "gap");
   K2_PTR(xq, "xq");
-  if (D.fp8) K2_PTR(xs, "xs");
+  if (D.fp8) K2_PTR4(xs, "xs");
   else K2_REQUIRE(xs == nullptr, MOE_ERR_INVALID_ARG, "xs must be NULL in the F32 format");
   const Layout L = layout(D, MOE_WS_ROUTER);
   K2_REQUIRE(ws_bytes >= L.total, MOE_ERR_WORKSPACE, "workspace too small");
@@ -542,10 +555,11 @@ moe_status moe_permute(const moe_config* cfg, int64_t T, const int32_t* topk_ids
   moe_status st = check_cfg(cfg, &D);
   if (st != MOE_OK) return st;
   if ((st = check_tokens(T, &D)) != MOE_OK) return st;
-  K2_PTR(topk_ids, "topk_ids");
-  K2_PTR(expert_offsets, "expert_offsets");
-  K2_PTR(row_pair, "row_pair");
-  K2_PTR(pair_row, "pair_row");
+  if (T == 0) return MOE_OK;
+  K2_PTR4(topk_ids, "topk_ids");
+  K2_PTR4(expert_offsets, "expert_offsets");
+  K2_PTR4(row_pair, "row_pair");
+  K2_PTR4(pair_row, "pair_row");
   const Layout L = layout(D, MOE_WS_PERMUTE);
   K2_REQUIRE(ws_bytes >= L.total, MOE_ERR_WORKSPACE, "workspace too small");
   if (L.total) K2_PTR(ws, "ws");
@@ -556,27 +570,34 @@ moe_status moe_permute(const moe_config* cfg, int64_t T, const int32_t* topk_ids
 
 moe_status moe_grouped_swiglu(const moe_config* cfg, int64_t T, const void* xq, const float* xs,
                               const int32_t* expert_offsets, const int32_t* row_pair,
-                              const void* packed_w, float* rows, float* shared_out, void* ws,
-                              size_t ws_bytes, void* stream) {
+                              const void* packed_w, float* rows, float* shared_out, void* act_q,
+                              float* act_s, void* ws, size_t ws_bytes, void* stream) {
   Dims D;
   moe_status st = check_cfg(cfg, &D);
   if (st != MOE_OK) return st;
   if ((st = check_tokens(T, &D)) != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
   K2_PTR(xq, "xq");
-  if (D.fp8) K2_PTR(xs, "xs");
-  K2_PTR(expert_offsets, "expert_offsets");
-  K2_PTR(row_pair, "row_pair");
+  if (D.fp8) K2_PTR4(xs, "xs");
+  K2_PTR4(expert_offsets, "expert_offsets");
+  K2_PTR4(row_pair, "row_pair");
   K2_PTR(packed_w, "packed_w");
   K2_PTR(rows, "rows");
   if (D.S) K2_PTR(shared_out, "shared_out");
   else K2_REQUIRE(shared_out == nullptr, MOE_ERR_INVALID_ARG,
                   "shared_out must be NULL without a shared expert");
+  K2_REQUIRE((act_q == nullptr) == (act_s == nullptr), MOE_ERR_INVALID_ARG,
+             "act_q and act_s go together");
+  K2_REQUIRE(act_q == nullptr || D.fp8, MOE_ERR_INVALID_ARG,
+             "act_q / act_s exist only in the FP8 format");
+  K2_OPT_PTR(act_q, "act_q");
+  K2_OPT_PTR4(act_s, "act_s");
   const Layout L = layout(D, MOE_WS_SWIGLU);
   K2_REQUIRE(ws_bytes >= L.total, MOE_ERR_WORKSPACE, "workspace too small");
   if (L.total) K2_PTR(ws, "ws");
   if (T == 0) return MOE_OK;
   return run_experts(D, L, ws, xq, xs, expert_offsets, row_pair, packed_w, rows, shared_out,
-                     nullptr, 0, static_cast<hipStream_t>(stream));
+                     nullptr, 0, act_q, act_s, static_cast<hipStream_t>(stream));
 }
 
 moe_status moe_combine(const moe_config* cfg, int64_t T, const float* rows,
@@ -586,9 +607,10 @@ moe_status moe_combine(const moe_config* cfg, int64_t T, const float* rows,
   moe_status st = check_cfg(cfg, &D);
   if (st != MOE_OK) return st;
   if ((st = check_tokens(T, &D)) != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
   K2_PTR(rows, "rows");
-  K2_PTR(pair_row, "pair_row");
-  K2_PTR(topk_w, "topk_w");
+  K2_PTR4(pair_row, "pair_row");
+  K2_PTR4(topk_w, "topk_w");
   if (D.S) K2_PTR(shared_out, "shared_out");
   else K2_REQUIRE(shared_out == nullptr, MOE_ERR_INVALID_ARG,
                   "shared_out must be NULL without a shared expert");
@@ -609,11 +631,12 @@ moe_status moe_forward(const moe_config* cfg, int64_t T, const void* x, const vo
   moe_status st = check_cfg(cfg, &D);
   if (st != MOE_OK) return st;
   if ((st = check_tokens(T, &D)) != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
   K2_PTR(x, "x");
   K2_PTR(norm_w, "norm_w");
   if (!D.dense) {
     K2_PTR(w_router, "w_router");
-    K2_PTR(bias, "bias");
+    K2_PTR4(bias, "bias");
   }
   K2_PTR(packed_w, "packed_w");
   K2_PTR(out, "out");
@@ -635,7 +658,8 @@ moe_status moe_forward(const moe_config* cfg, int64_t T, const void* x, const vo
   if ((st = run_router(D, L, ws, x, norm_w, w_router, bias, ids, w, gap, xq, xs, s)) != MOE_OK)
     return st;
   if ((st = run_permute(D, L, ws, ids, offsets, row_pair, pair_row, s)) != MOE_OK) return st;
-  if ((st = run_experts(D, L, ws, xq, xs, offsets, row_pair, packed_w, rows, shared, w, 1, s)) !=
+  if ((st = run_experts(D, L, ws, xq, xs, offsets, row_pair, packed_w, rows, shared, w, 1,
+                        nullptr, nullptr, s)) !=
       MOE_OK)
     return st;
   Stage stg(MOE_STAGE_COMBINE, s);

@@ -179,19 +179,23 @@ __global__ __launch_bounds__(256) void gemm_fp8_kernel(const GemmArgs g) {
   };
 
   // ---------------------------------------------------------------- K loop
-  const int nkb = g.nkb;  // even
+  const int nkb = g.nkb;
   load_w(wA, 0);
   load_b(0);
   load_s(saA, swA, 0);
   store_b(0);
   __syncthreads();
   for (int kb = 0; kb < nkb; kb += 2) {
-    load_w(wB, kb + 1);
-    load_b(kb + 1);
-    load_s(saB, swB, kb + 1);
+    const bool has_next = kb + 1 < nkb;  // block kb+1 exists
+    if (has_next) {
+      load_w(wB, kb + 1);
+      load_b(kb + 1);
+      load_s(saB, swB, kb + 1);
+    }
     compute(wA, 0, saA, swA);
-    store_b(1);
+    if (has_next) store_b(1);
     __syncthreads();
+    if (!has_next) break;
     const bool more = kb + 2 < nkb;
     if (more) {
       load_w(wA, kb + 2);

@@ -92,6 +92,14 @@ class K2MoE:
         torch.cuda.current_stream().synchronize()
         self._ws = {}
 
+    def use_router(self, inputs) -> "K2MoE":
+        """Take the norm weight, router weight and correction bias of ``inputs``
+        (workloads of one layer share the experts but may differ in the bias)."""
+        self.norm_w = inputs.norm_w
+        self.w_router = inputs.w_router
+        self.bias = inputs.bias
+        return self
+
     # ------------------------------------------------------------- buffers
     def workspace(self, T: int, entry: int) -> torch.Tensor:
         key = (T, entry)
@@ -134,16 +142,25 @@ class K2MoE:
                _p(pair_row), _p(ws), ws.numel(), _stream())
         return PermuteOut(offsets, row_pair, pair_row)
 
-    def grouped_swiglu(self, T: int, xq, xs, offsets, row_pair):
-        d = self.shape.d_model
+    def grouped_swiglu(self, T: int, xq, xs, offsets, row_pair, return_act: bool = False):
+        """Expert rows and shared output; with return_act (FP8 format) also the
+        requantised SwiGLU activations (codes [rows, d_ff], scales [rows, d_ff/128])."""
+        d, I = self.shape.d_model, self.shape.d_ff
         P = T * self.shape.top_k
         rows = torch.empty((P, d), dtype=torch.float32, device=self.device)
         shared = (torch.empty((T, d), dtype=torch.float32, device=self.device)
                   if self.shape.n_shared else None)
+        act_q = act_s = None
+        if return_act and self.fp8:
+            nrows = P + (T if self.shape.n_shared else 0)
+            act_q = torch.empty((nrows, I), dtype=torch.uint8, device=self.device)
+            act_s = torch.empty((nrows, I // 128), dtype=torch.float32, device=self.device)
         ws = self.workspace(T, L.MOE_WS_SWIGLU)
         L.call("moe_grouped_swiglu", C.byref(self.cfg), T, _p(xq), _p(xs), _p(offsets),
-               _p(row_pair), _p(self.packed), _p(rows), _p(shared), _p(ws), ws.numel(),
-               _stream())
+               _p(row_pair), _p(self.packed), _p(rows), _p(shared), _p(act_q), _p(act_s),
+               _p(ws), ws.numel(), _stream())
+        if return_act:
+            return rows, shared, act_q, act_s
         return rows, shared
 
     def combine(self, rows, pair_row, w, shared, residual=None, out_f32=False):

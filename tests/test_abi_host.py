@@ -127,6 +127,9 @@ def test_forward_small_workspace_and_negative_tokens():
 def test_zero_tokens_is_a_no_op():
     cfg = _cfg()
     assert L.status_of("moe_forward", *_forward_args(cfg, T=0, ws_bytes=0)) == L.MOE_OK
+    # empty tensors may have null data pointers
+    assert L.status_of("moe_forward", *_forward_args(cfg, T=0, ws_bytes=0, x=None, out=None,
+                                                     ws=None)) == L.MOE_OK
     assert L.status_of("moe_permute", C.byref(cfg), 0, FAKE, FAKE, FAKE, FAKE, FAKE, 0,
                        None) == L.MOE_OK
 
@@ -136,7 +139,7 @@ def test_dense_mode_allows_missing_router():
     assert L.status_of("moe_forward", *_forward_args(cfg, T=0, w_router=None, bias=None,
                                                      ws_bytes=0)) == L.MOE_OK
     cfg2 = _cfg()
-    assert L.status_of("moe_forward", *_forward_args(cfg2, T=0, w_router=None)) == \
+    assert L.status_of("moe_forward", *_forward_args(cfg2, T=4, w_router=None)) == \
         L.MOE_ERR_INVALID_ARG
 
 
@@ -150,7 +153,10 @@ def test_router_f32_requires_null_scales():
 def test_swiglu_shared_out_must_match_config():
     cfg = _cfg()
     st = L.status_of("moe_grouped_swiglu", C.byref(cfg), 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
-                     None, FAKE, 1 << 40, None)
+                     None, None, None, FAKE, 1 << 40, None)
+    assert st == L.MOE_ERR_INVALID_ARG
+    st = L.status_of("moe_grouped_swiglu", C.byref(cfg), 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                     FAKE, FAKE, None, FAKE, 1 << 40, None)     # act_q without act_s
     assert st == L.MOE_ERR_INVALID_ARG
 
 

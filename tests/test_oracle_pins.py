@@ -398,3 +398,28 @@ def test_doubling_down_scales_doubles_output_exactly():
     inp.s_down = inp.s_down * 2
     r1 = run_oracle(inp)
     assert np.array_equal(r1["y"], r0["y"] * 2)
+
+
+def test_act_override_with_own_codes_reproduces_layer():
+    shape = synth.small_fp8(tokens=20, n_experts=8, top_k=2)
+    inp = synth.generate(shape, seed=5)
+    r0 = run_oracle(inp)
+    n, k, I = 20, 2, shape.d_ff
+    codes, scales = R.quantize_1x128(r0["a_pairs"].reshape(-1, I))
+    hin = R.dequantize_1x128(r0["xq"], r0["xs"])
+    w = inp.expert_numpy(8)
+    g = R.f32(hin @ R.dequantize_weight(w["w_gate"], w["s_gate"]).T)
+    u = R.f32(hin @ R.dequantize_weight(w["w_up"], w["s_up"]).T)
+    sc, ss = R.quantize_1x128(R.silu_mul(g, u))
+    ov = dict(codes=codes.reshape(n, k, I), scales=scales.reshape(n, k, -1),
+              shared_codes=sc, shared_scales=ss)
+    r1 = run_oracle(inp, act_override=ov)
+    assert np.array_equal(r1["o_pairs_ov"], r0["o_pairs"])
+    assert np.array_equal(r1["shared_ov"], r0["shared"])
+    assert np.array_equal(r1["y_ov"], r0["y"]) and np.array_equal(r1["out_ov"], r0["out"])
+    # a different code in one pair changes only that pair's row
+    ov2 = dict(ov, codes=ov["codes"].copy())
+    ov2["codes"][3, 1, 0] ^= 1
+    r2 = run_oracle(inp, act_override=ov2)
+    diff = np.any(r2["o_pairs_ov"] != r0["o_pairs"], axis=2)
+    assert diff[3, 1] and diff.sum() == 1
