@@ -28,9 +28,21 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer tokens/s at K2 shape (64-tok decode, 8K prefill); % of roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA
-# bytes of one expert's gate+up codes and their 128x128 block scales
-GATEUP_BYTES_PER_EXPERT = 2 * 2048 * 7168 + 2 * 16 * 56 * 4
-DOWN_BYTES_PER_EXPERT = 7168 * 2048 + 56 * 16 * 4
+# HBM bytes per launch of the gate/up GEMM, from rocprofv3 --pmc FETCH_SIZE (x2.000,
+# the factor a 1 GiB copy probe gives) + WRITE_SIZE (x1.000), see
+# profiles/gemm_gateup_k2_decode.md; valid only for the gemm_fp8.hip source whose
+# sha256 starts with the recorded prefix (null otherwise).
+MEASURED_TRAFFIC = {"k2_decode": ("62a56a6558074288", 7.812e9)}
+GEMM_SRC = os.path.join(ROOT, "sparse_moe_transformer_sigmoid_amd", "csrc", "gemm_fp8.hip")
+
+
+def measured_traffic(workload: str):
+    import hashlib
+    rec = MEASURED_TRAFFIC.get(workload)
+    if rec is None:
+        return None
+    sha = hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()
+    return rec[1] if sha.startswith(rec[0]) else None
 
 
 def parse():
@@ -42,7 +54,9 @@ def parse():
                     choices=["decode", "prefill", "skewed", "dense"])
     ap.add_argument("--no-secondary", action="store_true", help="skip the prefill line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=3)
+    ap.add_argument("--cpu-tokens", type=int, default=16)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="also run a plain fp32 copy of BYTES (counter calibration)")
     return ap.parse_args()
 
 
@@ -190,7 +204,8 @@ def main():
                    "touched_experts": res["touched"]},
         "roofline": {"bound": "hbm", "kernel": "grouped gate/up GEMM + SwiGLU + requant",
                      "achieved": res["gu_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": res["gu_gbs"] / HBM_PEAK_GBS, "traffic": None,
+                     "frac": res["gu_gbs"] / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(shp.name),
                      "kernel_ms": gu_ms, "algorithmic_bytes": res["gu_bytes"]},
         "stage_ms": res["stage"],
     }
@@ -211,6 +226,15 @@ def main():
                 rp["gu_tflops"] / FP8_PEAK_TFLOPS,
             "gateup_gbs": rp["gu_gbs"], "stage_ms": rp["stage"]}
         del pre
+    if args.copy_probe:
+        n = args.copy_probe // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)       # reads and writes copy_probe bytes
+        torch.cuda.synchronize()
+        line["copy_probe_bytes"] = n * 4
+        del src, dst
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp, args.cpu_tokens)
     print(json.dumps(line), flush=True)
