@@ -71,6 +71,7 @@ typedef enum { MOE_FMT_F32 = 0, MOE_FMT_BF16_FP8B128 = 1 } moe_fmt;
  *  - dense = 1 runs the first block's dense SwiGLU as one expert with
  *    weight routed_scaling and no router: n_experts = top_k = 1, n_shared = 0.
  * FP8 format limits: d_model % 256 == 0, d_model <= 16384, d_ff % 128 == 0,
+ * d_ff <= 65536,
  * n_experts % 16 == 0 unless dense.  F32 format: d_model % 8 == 0,
  * d_model <= 16384.  Both: top_k <= 32, n_experts <= 1024. */
 typedef struct {

@@ -35,6 +35,8 @@ def compile_flags() -> list:
     return ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC",
             # keep packed-fp32 instructions out of the generated code
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # MFMA results in VGPRs: the fp32 block-scale FMAs read them directly
+            "-mllvm", "-amdgpu-mfma-vgpr-form=1",
             "-I", INCLUDE, "-I", CSRC, "-Wno-unused-command-line-argument"]
 
 

@@ -126,6 +126,7 @@ moe_status check_cfg(const moe_config* c, Dims* o) {
   K2_REQUIRE(c->top_k <= 32 && c->n_experts <= 1024, MOE_ERR_UNSUPPORTED,
              "top_k <= 32 and n_experts <= 1024 are supported");
   K2_REQUIRE(c->d_model <= 16384, MOE_ERR_UNSUPPORTED, "d_model <= 16384 is supported");
+  K2_REQUIRE(c->d_ff <= 65536, MOE_ERR_UNSUPPORTED, "d_ff <= 65536 is supported");
   K2_REQUIRE(c->dense == 0 || c->dense == 1, MOE_ERR_INVALID_ARG, "dense must be 0 or 1");
   if (c->dense)
     K2_REQUIRE(c->n_experts == 1 && c->top_k == 1 && c->n_shared == 0, MOE_ERR_INVALID_ARG,
@@ -204,12 +205,12 @@ int router_ksplit(const Dims& D) {
   return best;
 }
 
+// token tiles (16 rows each) per GEMM m-tile, from the mean rows per group
 int gemm_tt(const Dims& D) {
   const double avg = D.dense ? (double)D.T : (double)D.P / D.E;
   if (avg <= 12) return 1;
   if (avg <= 24) return 2;
-  if (avg <= 48) return 4;
-  return 8;
+  return 4;
 }
 
 struct Layout {

@@ -34,6 +34,9 @@ namespace k2 {
 
 namespace {
 
+// largest K / 128 of either GEMM (d_model <= 16384, d_ff <= 65536)
+constexpr int MAX_NKB = 512;
+
 __device__ __forceinline__ v8i join8(v4i a, v4i b) {
   return v8i{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 }
@@ -44,11 +47,24 @@ __device__ __forceinline__ v4f mfma_fp8(v8i a, v8i b) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 127, 0, 127);
 }
 
-template <bool GATEUP, int TT>
+// TT: 16-row token tiles per m-tile; NBUF: weight register ring depth (prefetch
+// distance NBUF-1 K blocks); NT: stream weights with non-temporal loads, for
+// launches where each weight chunk is read by a single m-tile.
+template <bool GATEUP, int TT, int NBUF, bool NT>
 __global__ __launch_bounds__(256) void gemm_fp8_kernel(const GemmArgs g) {
+  static_assert(NBUF >= 2 && NBUF <= 4, "NBUF must be 2, 3 or 4");
   constexpr int BM = 16 * TT;
   constexpr int CPT = (TT * 128 + 255) / 256;   // 16-byte staging chunks per thread
-  __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][TT * 2048];
+  // LDS rows past the tile (TT < 2) are write-only padding: every thread
+  // stages its chunk unconditionally, keeping the K loop free of branches
+  constexpr int LDS_B = (TT * 2048 > 256 * 16 * ((TT * 128 + 255) / 256)) ? TT * 2048
+                                                                          : 256 * 16 * ((TT * 128 + 255) / 256);
+  __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][LDS_B];
+  __shared__ float lds_sa[2][256];
+  // this chunk's weight scales for every K block, loaded once: scalar loads in
+  // the loop would share lgkmcnt with the LDS reads and stall each step on
+  // a memory round trip
+  __shared__ float lds_sw[2 * MAX_NKB];
   __shared__ float lds_red[GATEUP ? 4 * TT * 16 : 1];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -95,28 +111,28 @@ __global__ __launch_bounds__(256) void gemm_fp8_kernel(const GemmArgs g) {
     }
   };
 
-  // staging of the activation tile into LDS, fragment order:
-  // [tt][half p][lane][16 B], lane = token%16 + 16 * (32-byte group)
+  // staging of the activation tile into LDS in fragment order
+  // [tt][half p][lane][16 B]: LDS chunk q = tid + 256 i holds, for
+  // tt = q / 128, p = (q / 64) % 2, lane = q % 64, the 16 bytes of row
+  // 16 tt + lane % 16 at column 32 (lane / 16) + 16 p.  Consecutive lanes
+  // write consecutive 16-byte LDS chunks (no bank conflicts).
   uint32_t boff[CPT];
-  int bdst[CPT];
-  bool bon[CPT];
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
-    const int c = tid + 256 * i;
-    bon[i] = c < TT * 128;
-    const int m = c >> 3, piece = c & 7;
-    boff[i] = bon[i] ? (uint32_t)act_row(m) * (uint32_t)g.act_ld + piece * 16 : 0u;
-    bdst[i] = (m >> 4) * 2048 + (piece & 1) * 1024 + ((m & 15) + 16 * (piece >> 1)) * 16;
+    const int q = tid + 256 * i;
+    const int m = (q >> 7) * 16 + (q & 15);   // past the tile for q >= TT*128: clamped row
+    const int col = 32 * ((q & 63) >> 4) + 16 * ((q >> 6) & 1);
+    boff[i] = (uint32_t)act_row(m) * (uint32_t)g.act_ld + col;
   }
-  uint32_t saoff[TT];
-#pragma unroll
-  for (int tt = 0; tt < TT; ++tt) saoff[tt] = (uint32_t)act_row(tt * 16 + (lane & 15)) * g.nkb;
+  // thread tid stages the activation scale of tile row tid (clamped past the tile)
+  const uint32_t saoff = (uint32_t)act_row(tid) * g.nkb;
 
   const uint8_t* wp = g.wpk + (size_t)grp * g.expert_stride +
                       (size_t)(nc * 4 + wave) * (size_t)g.nkb * 8192 + lane * 16;
-  const float* swp = GATEUP
-      ? g.wscale + (size_t)grp * g.wscale_stride + (size_t)nc * g.nkb * 2
-      : g.wscale + (size_t)grp * g.wscale_stride + (size_t)(nc * 2 + (wave >> 1)) * g.nkb;
+  const float* swp_base = g.wscale + (size_t)grp * g.wscale_stride + (size_t)nc * g.nkb * 2;
+
+  // gate/up: [kb][gate, up] of chunk nc; down: [row block 2nc + h][kb], h = 0, 1
+  for (int i = tid; i < 2 * g.nkb; i += 256) lds_sw[i] = swp_base[i];
 
   v4f acc[4][TT];
 #pragma unroll
@@ -124,88 +140,120 @@ __global__ __launch_bounds__(256) void gemm_fp8_kernel(const GemmArgs g) {
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) acc[rt][tt] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  v8i wA[4], wB[4];
-  v4i breg[CPT];
-  float saA[TT], saB[TT];
-  float swA[2], swB[2];
+  // weight fragments: a ring of NBUF register buffers, loaded NBUF-1 K blocks ahead;
+  // activations: two register sets, loaded two K blocks ahead, stored to LDS one
+  // block ahead (LDS double buffer)
+  v8i wbuf[NBUF][4];
+  v4i breg[2][CPT];
+  float sareg[2] = {0.f, 0.f};
 
   auto load_w = [&](v8i (&w)[4], int kb) {
     const uint8_t* p = wp + (size_t)kb * 8192;
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
-      const v4i lo4 = *reinterpret_cast<const v4i*>(p + rt * 2048);
-      const v4i hi4 = *reinterpret_cast<const v4i*>(p + rt * 2048 + 1024);
-      w[rt] = join8(lo4, hi4);
-    }
-  };
-  auto load_b = [&](int kb) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i)
-      if (bon[i]) breg[i] = *reinterpret_cast<const v4i*>(g.act + boff[i] + kb * 128);
-  };
-  auto store_b = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i)
-      if (bon[i]) *reinterpret_cast<v4i*>(&lds_b[buf][bdst[i]]) = breg[i];
-  };
-  auto load_s = [&](float (&sa)[TT], float (&sw)[2], int kb) {
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt) sa[tt] = g.act_s[saoff[tt] + kb];
-    if constexpr (GATEUP) {
-      sw[0] = swp[2 * kb];
-      sw[1] = swp[2 * kb + 1];
-    } else {
-      sw[0] = swp[kb];
-      sw[1] = sw[0];
-    }
-  };
-  auto compute = [&](const v8i (&w)[4], int buf, const float (&sa)[TT], const float (&sw)[2]) {
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt) {
-      if (tt < ntt) {
-        const uint8_t* bp = &lds_b[buf][tt * 2048 + lane * 16];
-        const v8i bf = join8(*reinterpret_cast<const v4i*>(bp),
-                             *reinterpret_cast<const v4i*>(bp + 1024));
-        const float s0 = sa[tt] * sw[0];
-        const float s1 = sa[tt] * sw[1];
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-          const v4f f = mfma_fp8(w[rt], bf);
-          const float sc = rt < 2 ? s0 : s1;
-          acc[rt][tt] += f * sc;
-        }
+      const v4i* p4 = reinterpret_cast<const v4i*>(p + rt * 2048);
+      if constexpr (NT) {
+        w[rt] = join8(__builtin_nontemporal_load(p4), __builtin_nontemporal_load(p4 + 64));
+      } else {
+        w[rt] = join8(p4[0], p4[64]);
       }
+    }
+  };
+  auto load_b = [&](int set, int kb) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i)
+      breg[set][i] = *reinterpret_cast<const v4i*>(g.act + boff[i] + kb * 128);
+    sareg[set] = g.act_s[saoff + kb];
+  };
+  auto store_b = [&](int set, int buf) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i)
+      *reinterpret_cast<v4i*>(&lds_b[buf][(tid + 256 * i) * 16]) = breg[set][i];
+    lds_sa[buf][tid] = sareg[set];
+  };
+  auto weight_scales = [&](int kb, float& s_gate_or_down, float& s_up) {
+    if constexpr (GATEUP) {
+      s_gate_or_down = lds_sw[2 * kb];
+      s_up = lds_sw[2 * kb + 1];
+    } else {
+      s_gate_or_down = lds_sw[(wave >> 1) * g.nkb + kb];
+      s_up = s_gate_or_down;
+    }
+  };
+  // Every tile of the m-tile is computed (rows past mcount are discarded at
+  // the end): no branches in the hot loop, so the MFMA of one tile overlaps
+  // the fp32 scaling of the previous tile's result.  Token tiles go in groups
+  // of GRP; a scheduling fence between groups keeps the compiler from hoisting
+  // every B fragment at once (register pressure at large TT).
+  constexpr int GRP = TT < 4 ? TT : 4;
+  auto compute = [&](const v8i (&w)[4], int buf, int kb) {
+    float swg, swu;
+    weight_scales(kb, swg, swu);
+#pragma unroll
+    for (int t0 = 0; t0 < TT; t0 += GRP) {
+      v8i bf[GRP];
+      float s0[GRP], s1[GRP];
+#pragma unroll
+      for (int u = 0; u < GRP; ++u) {
+        const uint8_t* bp = &lds_b[buf][(t0 + u) * 2048 + lane * 16];
+        bf[u] = join8(*reinterpret_cast<const v4i*>(bp), *reinterpret_cast<const v4i*>(bp + 1024));
+        const float sa_t = lds_sa[buf][(t0 + u) * 16 + (lane & 15)];
+        s0[u] = sa_t * swg;
+        s1[u] = sa_t * swu;
+      }
+      v4f prev = mfma_fp8(w[0], bf[0]);
+#pragma unroll
+      for (int i = 1; i < 4 * GRP; ++i) {
+        const int u = i >> 2, rt = i & 3;
+        const v4f cur = mfma_fp8(w[rt], bf[u]);
+        const int pu = (i - 1) >> 2, pr = (i - 1) & 3;
+        acc[pr][t0 + pu] += prev * (pr < 2 ? s0[pu] : s1[pu]);
+        prev = cur;
+      }
+      acc[3][t0 + GRP - 1] += prev * s1[GRP - 1];
+      if (t0 + GRP < TT) __builtin_amdgcn_sched_barrier(0);
     }
   };
 
   // ---------------------------------------------------------------- K loop
+  // Block kb: weights in wbuf[kb % NBUF] with scales sw[kb % NBUF]; activations
+  // in LDS buffer kb & 1, staged from register set (kb & 1).  Vector loads
+  // retire in issue order, so each step issues the activations of block kb+2
+  // before the weights of block kb+NBUF-1, and ends by waiting only for the
+  // activations of block kb+1 (issued one step earlier).
   const int nkb = g.nkb;
-  load_w(wA, 0);
-  load_b(0);
-  load_s(saA, swA, 0);
-  store_b(0);
+  load_b(0, 0);
+  if (nkb > 1) load_b(1, 1);
+#pragma unroll
+  for (int i = 0; i < NBUF - 1; ++i)
+    if (i < nkb) load_w(wbuf[i], i);
+  store_b(0, 0);
   __syncthreads();
-  for (int kb = 0; kb < nkb; kb += 2) {
-    const bool has_next = kb + 1 < nkb;  // block kb+1 exists
-    if (has_next) {
-      load_w(wB, kb + 1);
-      load_b(kb + 1);
-      load_s(saB, swB, kb + 1);
-    }
-    compute(wA, 0, saA, swA);
-    if (has_next) store_b(1);
+  // One step: prefetch (activations of kb+2, weights of kb+NBUF-1; indices
+  // clamped to the last block, so the tail re-reads a block instead of
+  // branching), compute block kb, stage block kb+1 into LDS, barrier.  STEP is
+  // a multiple of NBUF and of 2, so every buffer index is a compile-time
+  // constant; full STEPs run without guards, the tail with them.
+  constexpr int STEP = (NBUF & 1) ? 2 * NBUF : NBUF;
+  auto step = [&](const int j, const int kb) {
+    const int cur = j & 1;
+    load_b(cur, min(kb + 2, nkb - 1));
+    load_w(wbuf[(j + NBUF - 1) % NBUF], min(kb + NBUF - 1, nkb - 1));
+    // keep the prefetches issued here: the scheduler would otherwise sink
+    // them next to their use to save registers, undoing the ring
+    __builtin_amdgcn_sched_barrier(0);
+    compute(wbuf[j % NBUF], cur, kb);
+    store_b(cur ^ 1, cur ^ 1);
     __syncthreads();
-    if (!has_next) break;
-    const bool more = kb + 2 < nkb;
-    if (more) {
-      load_w(wA, kb + 2);
-      load_b(kb + 2);
-      load_s(saA, swA, kb + 2);
-    }
-    compute(wB, 1, saB, swB);
-    if (more) store_b(0);
-    __syncthreads();
+  };
+  int kb0 = 0;
+  for (; kb0 + STEP <= nkb; kb0 += STEP) {
+#pragma unroll
+    for (int j = 0; j < STEP; ++j) step(j, kb0 + j);
   }
+#pragma unroll
+  for (int j = 0; j < STEP; ++j)
+    if (kb0 + j < nkb) step(j, kb0 + j);
 
   // ---------------------------------------------------------------- epilogue
   if constexpr (GATEUP) {
@@ -278,13 +326,16 @@ __global__ __launch_bounds__(256) void gemm_fp8_kernel(const GemmArgs g) {
   }
 }
 
+// Per m-tile width: TT = 1 (decode-sized groups) streams weights once, so
+// non-temporal loads keep them from displacing the activations in L2; wider
+// tiles share each weight chunk between m-tiles of one XCD through L2.
+// NBUF = 3 at TT = 4 (two K blocks of weights in flight) fits in 2 waves/SIMD.
 template <bool GATEUP>
 hipError_t launch_tt(int tt, const GemmArgs& a, int grid, hipStream_t s) {
   switch (tt) {
-    case 1: gemm_fp8_kernel<GATEUP, 1><<<grid, 256, 0, s>>>(a); break;
-    case 2: gemm_fp8_kernel<GATEUP, 2><<<grid, 256, 0, s>>>(a); break;
-    case 4: gemm_fp8_kernel<GATEUP, 4><<<grid, 256, 0, s>>>(a); break;
-    case 8: gemm_fp8_kernel<GATEUP, 8><<<grid, 256, 0, s>>>(a); break;
+    case 1: gemm_fp8_kernel<GATEUP, 1, 2, true><<<grid, 256, 0, s>>>(a); break;
+    case 2: gemm_fp8_kernel<GATEUP, 2, 2, false><<<grid, 256, 0, s>>>(a); break;
+    case 4: gemm_fp8_kernel<GATEUP, 4, 3, false><<<grid, 256, 0, s>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
