@@ -194,13 +194,14 @@ moe_status check_tokens(int64_t T, Dims* D) {
 // router GEMM split over K so small batches still fill the chip
 int router_ksplit(const Dims& D) {
   if (!D.fp8 || D.dense) return 1;
-  const int64_t tiles = ((D.T + 63) / 64) * ((D.E + 63) / 64);
-  const int steps = D.d / 32;
+  // workgroup tile: 64 tokens x 192 experts; K split in multiples of 128 columns
+  const int64_t tiles = ((D.T + 63) / 64) * ((D.E + 191) / 192);
+  const int steps = D.d / 128;
   int best = 1;
   for (int ks = 1; ks <= 64; ++ks) {
     if (steps % ks) continue;
     best = ks;
-    if (tiles * ks >= 512) break;
+    if (tiles * ks >= 256) break;
   }
   return best;
 }
@@ -210,7 +211,8 @@ int gemm_tt(const Dims& D) {
   const double avg = D.dense ? (double)D.T : (double)D.P / D.E;
   if (avg <= 12) return 1;
   if (avg <= 24) return 2;
-  return 4;
+  if (avg <= 48) return 4;
+  return 8;
 }
 
 struct Layout {

@@ -30,6 +30,7 @@
 #include "k2_common.h"
 #include "k2_launch.h"
 
+
 namespace k2 {
 
 namespace {
@@ -47,215 +48,75 @@ __device__ __forceinline__ v4f mfma_fp8(v8i a, v8i b) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 127, 0, 127);
 }
 
-// TT: 16-row token tiles per m-tile; NBUF: weight register ring depth (prefetch
-// distance NBUF-1 K blocks); NT: stream weights with non-temporal loads, for
-// launches where each weight chunk is read by a single m-tile.
-template <bool GATEUP, int TT, int NBUF, bool NT>
-__global__ __launch_bounds__(256) void gemm_fp8_kernel(const GemmArgs g) {
-  static_assert(NBUF >= 2 && NBUF <= 4, "NBUF must be 2, 3 or 4");
-  constexpr int BM = 16 * TT;
-  constexpr int CPT = (TT * 128 + 255) / 256;   // 16-byte staging chunks per thread
-  // LDS rows past the tile (TT < 2) are write-only padding: every thread
-  // stages its chunk unconditionally, keeping the K loop free of branches
-  constexpr int LDS_B = (TT * 2048 > 256 * 16 * ((TT * 128 + 255) / 256)) ? TT * 2048
-                                                                          : 256 * 16 * ((TT * 128 + 255) / 256);
-  __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][LDS_B];
-  __shared__ float lds_sa[2][256];
-  // this chunk's weight scales for every K block, loaded once: scalar loads in
-  // the loop would share lgkmcnt with the LDS reads and stall each step on
-  // a memory round trip
-  __shared__ float lds_sw[2 * MAX_NKB];
-  __shared__ float lds_red[GATEUP ? 4 * TT * 16 : 1];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+struct WorkItem {
+  bool valid;
+  bool shared_grp;
+  int grp, nc, row0, mcount, ntt;
+};
 
-  // ---------------------------------------------------------------- work item
+// Work item L (after the XCD remap) -> (group, weight chunk, m-tile).  The
+// grid is a host-side upper bound; workgroups past the device-side m-tile
+// count get valid = false.
+__device__ __forceinline__ WorkItem decode_work(const GemmArgs& g, int BM) {
+  WorkItem w{};
   const int Wtot = g.mt_start[g.G] * g.NC;
   const int Wp = (Wtot + 7) & ~7;
   const int b = blockIdx.x;
-  if (b >= Wp) return;
+  w.valid = false;
+  if (b >= Wp) return w;
   const int L = (b & 7) * (Wp >> 3) + (b >> 3);
-  if (L >= Wtot) return;
+  if (L >= Wtot) return w;
   const int q = L / g.NC;
   int lo = 0, hi = g.G;                    // mt_start[lo] <= q < mt_start[hi]
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
     if (g.mt_start[mid] <= q) lo = mid; else hi = mid;
   }
-  const int grp = lo;
-  const bool shared_grp = grp >= g.E;
+  w.grp = lo;
+  w.shared_grp = lo >= g.E;
   int row0_g, m_g;
-  if (shared_grp) {
+  if (w.shared_grp) {
     row0_g = g.P;
     m_g = g.T;
   } else {
-    row0_g = min(max(g.offsets[grp], 0), g.P);
-    m_g = min(max(g.offsets[grp + 1] - row0_g, 0), g.P - row0_g);
+    row0_g = min(max(g.offsets[lo], 0), g.P);
+    m_g = min(max(g.offsets[lo + 1] - row0_g, 0), g.P - row0_g);
   }
+  // the group's rows are split into ceil(m / BM) m-tiles of near-equal size
+  // (at most BM rows each), so the last tile of a group is not mostly padding
   const int mtiles = (m_g + BM - 1) / BM;
-  const int rr = L - g.mt_start[grp] * g.NC;
-  const int nc = rr / mtiles, mt = rr - nc * mtiles;
-  const int row0 = row0_g + mt * BM;
-  const int mcount = min(BM, m_g - mt * BM);
-  const int ntt = (mcount + 15) >> 4;
+  const int rr = L - g.mt_start[lo] * g.NC;
+  w.nc = rr / mtiles;
+  const int mt = rr - w.nc * mtiles;
+  const int r_lo = (int)(((int64_t)mt * m_g) / mtiles);
+  const int r_hi = (int)(((int64_t)(mt + 1) * m_g) / mtiles);
+  w.row0 = row0_g + r_lo;
+  w.mcount = r_hi - r_lo;
+  w.ntt = (w.mcount + 15) >> 4;
+  w.valid = true;
+  return w;
+}
 
-  // activation row of the m-th row of this tile (padding rows repeat the last)
-  auto act_row = [&](int m) -> int {
-    const int mm = min(m, mcount - 1);
-    if constexpr (GATEUP) {
-      if (shared_grp) return row0 + mm - g.P;
-      const int tok = g.row_pair[row0 + mm] / g.k;
-      return min(max(tok, 0), g.T - 1);
-    } else {
-      return row0 + mm;
-    }
-  };
-
-  // staging of the activation tile into LDS in fragment order
-  // [tt][half p][lane][16 B]: LDS chunk q = tid + 256 i holds, for
-  // tt = q / 128, p = (q / 64) % 2, lane = q % 64, the 16 bytes of row
-  // 16 tt + lane % 16 at column 32 (lane / 16) + 16 p.  Consecutive lanes
-  // write consecutive 16-byte LDS chunks (no bank conflicts).
-  uint32_t boff[CPT];
-#pragma unroll
-  for (int i = 0; i < CPT; ++i) {
-    const int q = tid + 256 * i;
-    const int m = (q >> 7) * 16 + (q & 15);   // past the tile for q >= TT*128: clamped row
-    const int col = 32 * ((q & 63) >> 4) + 16 * ((q >> 6) & 1);
-    boff[i] = (uint32_t)act_row(m) * (uint32_t)g.act_ld + col;
+// activation row of the m-th row of a tile (padding rows repeat the last)
+template <bool GATEUP>
+__device__ __forceinline__ int act_row_of(const GemmArgs& g, const WorkItem& w, int m) {
+  const int mm = min(m, w.mcount - 1);
+  if constexpr (GATEUP) {
+    if (w.shared_grp) return w.row0 + mm - g.P;
+    const int tok = g.row_pair[w.row0 + mm] / g.k;
+    return min(max(tok, 0), g.T - 1);
+  } else {
+    return w.row0 + mm;
   }
-  // thread tid stages the activation scale of tile row tid (clamped past the tile)
-  const uint32_t saoff = (uint32_t)act_row(tid) * g.nkb;
+}
 
-  const uint8_t* wp = g.wpk + (size_t)grp * g.expert_stride +
-                      (size_t)(nc * 4 + wave) * (size_t)g.nkb * 8192 + lane * 16;
-  const float* swp_base = g.wscale + (size_t)grp * g.wscale_stride + (size_t)nc * g.nkb * 2;
-
-  // gate/up: [kb][gate, up] of chunk nc; down: [row block 2nc + h][kb], h = 0, 1
-  for (int i = tid; i < 2 * g.nkb; i += 256) lds_sw[i] = swp_base[i];
-
-  v4f acc[4][TT];
-#pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt) acc[rt][tt] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  // weight fragments: a ring of NBUF register buffers, loaded NBUF-1 K blocks ahead;
-  // activations: two register sets, loaded two K blocks ahead, stored to LDS one
-  // block ahead (LDS double buffer)
-  v8i wbuf[NBUF][4];
-  v4i breg[2][CPT];
-  float sareg[2] = {0.f, 0.f};
-
-  auto load_w = [&](v8i (&w)[4], int kb) {
-    const uint8_t* p = wp + (size_t)kb * 8192;
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      const v4i* p4 = reinterpret_cast<const v4i*>(p + rt * 2048);
-      if constexpr (NT) {
-        w[rt] = join8(__builtin_nontemporal_load(p4), __builtin_nontemporal_load(p4 + 64));
-      } else {
-        w[rt] = join8(p4[0], p4[64]);
-      }
-    }
-  };
-  auto load_b = [&](int set, int kb) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i)
-      breg[set][i] = *reinterpret_cast<const v4i*>(g.act + boff[i] + kb * 128);
-    sareg[set] = g.act_s[saoff + kb];
-  };
-  auto store_b = [&](int set, int buf) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i)
-      *reinterpret_cast<v4i*>(&lds_b[buf][(tid + 256 * i) * 16]) = breg[set][i];
-    lds_sa[buf][tid] = sareg[set];
-  };
-  auto weight_scales = [&](int kb, float& s_gate_or_down, float& s_up) {
-    if constexpr (GATEUP) {
-      s_gate_or_down = lds_sw[2 * kb];
-      s_up = lds_sw[2 * kb + 1];
-    } else {
-      s_gate_or_down = lds_sw[(wave >> 1) * g.nkb + kb];
-      s_up = s_gate_or_down;
-    }
-  };
-  // Every tile of the m-tile is computed (rows past mcount are discarded at
-  // the end): no branches in the hot loop, so the MFMA of one tile overlaps
-  // the fp32 scaling of the previous tile's result.  Token tiles go in groups
-  // of GRP; a scheduling fence between groups keeps the compiler from hoisting
-  // every B fragment at once (register pressure at large TT).
-  constexpr int GRP = TT < 4 ? TT : 4;
-  auto compute = [&](const v8i (&w)[4], int buf, int kb) {
-    float swg, swu;
-    weight_scales(kb, swg, swu);
-#pragma unroll
-    for (int t0 = 0; t0 < TT; t0 += GRP) {
-      v8i bf[GRP];
-      float s0[GRP], s1[GRP];
-#pragma unroll
-      for (int u = 0; u < GRP; ++u) {
-        const uint8_t* bp = &lds_b[buf][(t0 + u) * 2048 + lane * 16];
-        bf[u] = join8(*reinterpret_cast<const v4i*>(bp), *reinterpret_cast<const v4i*>(bp + 1024));
-        const float sa_t = lds_sa[buf][(t0 + u) * 16 + (lane & 15)];
-        s0[u] = sa_t * swg;
-        s1[u] = sa_t * swu;
-      }
-      v4f prev = mfma_fp8(w[0], bf[0]);
-#pragma unroll
-      for (int i = 1; i < 4 * GRP; ++i) {
-        const int u = i >> 2, rt = i & 3;
-        const v4f cur = mfma_fp8(w[rt], bf[u]);
-        const int pu = (i - 1) >> 2, pr = (i - 1) & 3;
-        acc[pr][t0 + pu] += prev * (pr < 2 ? s0[pu] : s1[pu]);
-        prev = cur;
-      }
-      acc[3][t0 + GRP - 1] += prev * s1[GRP - 1];
-      if (t0 + GRP < TT) __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-
-  // ---------------------------------------------------------------- K loop
-  // Block kb: weights in wbuf[kb % NBUF] with scales sw[kb % NBUF]; activations
-  // in LDS buffer kb & 1, staged from register set (kb & 1).  Vector loads
-  // retire in issue order, so each step issues the activations of block kb+2
-  // before the weights of block kb+NBUF-1, and ends by waiting only for the
-  // activations of block kb+1 (issued one step earlier).
-  const int nkb = g.nkb;
-  load_b(0, 0);
-  if (nkb > 1) load_b(1, 1);
-#pragma unroll
-  for (int i = 0; i < NBUF - 1; ++i)
-    if (i < nkb) load_w(wbuf[i], i);
-  store_b(0, 0);
-  __syncthreads();
-  // One step: prefetch (activations of kb+2, weights of kb+NBUF-1; indices
-  // clamped to the last block, so the tail re-reads a block instead of
-  // branching), compute block kb, stage block kb+1 into LDS, barrier.  STEP is
-  // a multiple of NBUF and of 2, so every buffer index is a compile-time
-  // constant; full STEPs run without guards, the tail with them.
-  constexpr int STEP = (NBUF & 1) ? 2 * NBUF : NBUF;
-  auto step = [&](const int j, const int kb) {
-    const int cur = j & 1;
-    load_b(cur, min(kb + 2, nkb - 1));
-    load_w(wbuf[(j + NBUF - 1) % NBUF], min(kb + NBUF - 1, nkb - 1));
-    // keep the prefetches issued here: the scheduler would otherwise sink
-    // them next to their use to save registers, undoing the ring
-    __builtin_amdgcn_sched_barrier(0);
-    compute(wbuf[j % NBUF], cur, kb);
-    store_b(cur ^ 1, cur ^ 1);
-    __syncthreads();
-  };
-  int kb0 = 0;
-  for (; kb0 + STEP <= nkb; kb0 += STEP) {
-#pragma unroll
-    for (int j = 0; j < STEP; ++j) step(j, kb0 + j);
-  }
-#pragma unroll
-  for (int j = 0; j < STEP; ++j)
-    if (kb0 + j < nkb) step(j, kb0 + j);
-
-  // ---------------------------------------------------------------- epilogue
+// Accumulators -> outputs.  acc[rt][tt] lane l holds weight rows
+// 64 wave + 16 rt + 4 (l / 16) + r of token row 16 tt + l % 16.
+template <bool GATEUP, int TT>
+__device__ __forceinline__ void epilogue(const GemmArgs& g, v4f (&acc)[4][TT], float* lds_red,
+                                         const WorkItem& wi, int wave, int lane) {
+  const int nc = wi.nc, row0 = wi.row0, mcount = wi.mcount, ntt = wi.ntt;
+  const bool shared_grp = wi.shared_grp;
   if constexpr (GATEUP) {
     // a = silu(g) * u for hidden 32w + 16h + 4(l/16) + r, h in {0,1}
 #pragma unroll
@@ -326,16 +187,201 @@ __global__ __launch_bounds__(256) void gemm_fp8_kernel(const GemmArgs g) {
   }
 }
 
+// TT: 16-row token tiles per m-tile; NBUF: weight register ring depth (prefetch
+// distance NBUF-1 K blocks); NT: stream weights with non-temporal loads, for
+// launches where each weight chunk is read by a single m-tile.
+// BSETS: activation register sets (2: loaded two K blocks ahead; 1: one block
+// ahead, saving registers); MINW: waves per SIMD the register budget must allow.
+template <bool GATEUP, int TT, int NBUF, bool NT, int BSETS = 2, int MINW = 1>
+__global__ __launch_bounds__(256, MINW) void gemm_fp8_kernel(const GemmArgs g) {
+  static_assert(NBUF >= 2 && NBUF <= 4, "NBUF must be 2, 3 or 4");
+  static_assert(BSETS == 1 || BSETS == 2, "BSETS must be 1 or 2");
+  constexpr int BM = 16 * TT;
+  constexpr int CPT = (TT * 128 + 255) / 256;   // 16-byte staging chunks per thread
+  // LDS rows past the tile (TT < 2) are write-only padding: every thread
+  // stages its chunk unconditionally, keeping the K loop free of branches
+  constexpr int LDS_B = (TT * 2048 > 256 * 16 * ((TT * 128 + 255) / 256)) ? TT * 2048
+                                                                          : 256 * 16 * ((TT * 128 + 255) / 256);
+  __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][LDS_B];
+  __shared__ float lds_sa[2][256];
+  // this chunk's weight scales for every K block, loaded once: scalar loads in
+  // the loop would share lgkmcnt with the LDS reads and stall each step on
+  // a memory round trip
+  __shared__ float lds_sw[2 * MAX_NKB];
+  __shared__ float lds_red[GATEUP ? 4 * TT * 16 : 1];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  const WorkItem wi = decode_work(g, BM);
+  if (!wi.valid) return;
+  const int grp = wi.grp, nc = wi.nc, row0 = wi.row0, mcount = wi.mcount, ntt = wi.ntt;
+  const bool shared_grp = wi.shared_grp;
+
+  auto act_row = [&](int m) { return act_row_of<GATEUP>(g, wi, m); };
+
+  // staging of the activation tile into LDS in fragment order
+  // [tt][half p][lane][16 B]: LDS chunk q = tid + 256 i holds, for
+  // tt = q / 128, p = (q / 64) % 2, lane = q % 64, the 16 bytes of row
+  // 16 tt + lane % 16 at column 32 (lane / 16) + 16 p.  Consecutive lanes
+  // write consecutive 16-byte LDS chunks (no bank conflicts).
+  uint32_t boff[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int q = tid + 256 * i;
+    const int m = (q >> 7) * 16 + (q & 15);   // past the tile for q >= TT*128: clamped row
+    const int col = 32 * ((q & 63) >> 4) + 16 * ((q >> 6) & 1);
+    boff[i] = (uint32_t)act_row(m) * (uint32_t)g.act_ld + col;
+  }
+  // thread tid stages the activation scale of tile row tid (clamped past the tile)
+  const uint32_t saoff = (uint32_t)act_row(tid) * g.nkb;
+
+  const uint8_t* wp = g.wpk + (size_t)grp * g.expert_stride +
+                      (size_t)(nc * 4 + wave) * (size_t)g.nkb * 8192 + lane * 16;
+  const float* swp_base = g.wscale + (size_t)grp * g.wscale_stride + (size_t)nc * g.nkb * 2;
+
+  // gate/up: [kb][gate, up] of chunk nc; down: [row block 2nc + h][kb], h = 0, 1
+  for (int i = tid; i < 2 * g.nkb; i += 256) lds_sw[i] = swp_base[i];
+
+  v4f acc[4][TT];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) acc[rt][tt] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // weight fragments: a ring of NBUF register buffers, loaded NBUF-1 K blocks ahead;
+  // activations: two register sets, loaded two K blocks ahead, stored to LDS one
+  // block ahead (LDS double buffer)
+  v8i wbuf[NBUF][4];
+  v4i breg[BSETS][CPT];
+  float sareg[2] = {0.f, 0.f};
+
+  auto load_w = [&](v8i (&w)[4], int kb) {
+    const uint8_t* p = wp + (size_t)kb * 8192;
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      const v4i* p4 = reinterpret_cast<const v4i*>(p + rt * 2048);
+      if constexpr (NT) {
+        w[rt] = join8(__builtin_nontemporal_load(p4), __builtin_nontemporal_load(p4 + 64));
+      } else {
+        w[rt] = join8(p4[0], p4[64]);
+      }
+    }
+  };
+  auto load_b = [&](int set, int kb) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i)
+      breg[set][i] = *reinterpret_cast<const v4i*>(g.act + boff[i] + kb * 128);
+    sareg[set] = g.act_s[saoff + kb];
+  };
+  auto store_b = [&](int set, int buf) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i)
+      *reinterpret_cast<v4i*>(&lds_b[buf][(tid + 256 * i) * 16]) = breg[set][i];
+    lds_sa[buf][tid] = sareg[set];
+  };
+  auto weight_scales = [&](int kb, float& s_gate_or_down, float& s_up) {
+    if constexpr (GATEUP) {
+      s_gate_or_down = lds_sw[2 * kb];
+      s_up = lds_sw[2 * kb + 1];
+    } else {
+      s_gate_or_down = lds_sw[(wave >> 1) * g.nkb + kb];
+      s_up = s_gate_or_down;
+    }
+  };
+  // Every tile of the m-tile is computed (rows past mcount are discarded at
+  // the end): no branches in the hot loop, so the MFMA of one tile overlaps
+  // the fp32 scaling of the previous tile's result.  Token tiles go in groups
+  // of GRP; a scheduling fence between groups keeps the compiler from hoisting
+  // every B fragment at once (register pressure at large TT; one tile per
+  // group when the register budget is sized for 2 waves/SIMD).
+  constexpr int GRP = TT < 4 ? TT : (MINW > 1 ? 1 : 4);
+  auto compute = [&](const v8i (&w)[4], int buf, int kb) {
+    float swg, swu;
+    weight_scales(kb, swg, swu);
+#pragma unroll
+    for (int t0 = 0; t0 < TT; t0 += GRP) {
+      v8i bf[GRP];
+      float s0[GRP], s1[GRP];
+#pragma unroll
+      for (int u = 0; u < GRP; ++u) {
+        const uint8_t* bp = &lds_b[buf][(t0 + u) * 2048 + lane * 16];
+        bf[u] = join8(*reinterpret_cast<const v4i*>(bp), *reinterpret_cast<const v4i*>(bp + 1024));
+        const float sa_t = lds_sa[buf][(t0 + u) * 16 + (lane & 15)];
+        s0[u] = sa_t * swg;
+        s1[u] = sa_t * swu;
+      }
+      v4f prev = mfma_fp8(w[0], bf[0]);
+#pragma unroll
+      for (int i = 1; i < 4 * GRP; ++i) {
+        const int u = i >> 2, rt = i & 3;
+        const v4f cur = mfma_fp8(w[rt], bf[u]);
+        const int pu = (i - 1) >> 2, pr = (i - 1) & 3;
+        acc[pr][t0 + pu] += prev * (pr < 2 ? s0[pu] : s1[pu]);
+        prev = cur;
+      }
+      acc[3][t0 + GRP - 1] += prev * s1[GRP - 1];
+      if (t0 + GRP < TT) __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // ---------------------------------------------------------------- K loop
+  // Block kb: weights in wbuf[kb % NBUF] with scales sw[kb % NBUF]; activations
+  // in LDS buffer kb & 1, staged from register set (kb & 1).  Vector loads
+  // retire in issue order, so each step issues the activations of block kb+2
+  // before the weights of block kb+NBUF-1, and ends by waiting only for the
+  // activations of block kb+1 (issued one step earlier).
+  const int nkb = g.nkb;
+  load_b(0, 0);
+  if (BSETS == 2 && nkb > 1) load_b(BSETS - 1, 1);
+#pragma unroll
+  for (int i = 0; i < NBUF - 1; ++i)
+    if (i < nkb) load_w(wbuf[i], i);
+  store_b(0, 0);
+  __syncthreads();
+  // One step: prefetch (activations of kb+2, weights of kb+NBUF-1; indices
+  // clamped to the last block, so the tail re-reads a block instead of
+  // branching), compute block kb, stage block kb+1 into LDS, barrier.  STEP is
+  // a multiple of NBUF and of 2, so every buffer index is a compile-time
+  // constant; full STEPs run without guards, the tail with them.
+  constexpr int STEP = (NBUF & 1) ? 2 * NBUF : NBUF;
+  auto step = [&](const int j, const int kb) {
+    const int cur = j & 1;
+    if constexpr (BSETS == 2) load_b(cur, min(kb + 2, nkb - 1));
+    else load_b(0, min(kb + 1, nkb - 1));
+    load_w(wbuf[(j + NBUF - 1) % NBUF], min(kb + NBUF - 1, nkb - 1));
+    // keep the prefetches issued here: the scheduler would otherwise sink
+    // them next to their use to save registers, undoing the ring
+    __builtin_amdgcn_sched_barrier(0);
+    compute(wbuf[j % NBUF], cur, kb);
+    store_b(BSETS == 2 ? cur ^ 1 : 0, cur ^ 1);
+    __syncthreads();
+  };
+  int kb0 = 0;
+  for (; kb0 + STEP <= nkb; kb0 += STEP) {
+#pragma unroll
+    for (int j = 0; j < STEP; ++j) step(j, kb0 + j);
+  }
+#pragma unroll
+  for (int j = 0; j < STEP; ++j)
+    if (kb0 + j < nkb) step(j, kb0 + j);
+
+  epilogue<GATEUP, TT>(g, acc, lds_red, wi, wave, lane);
+}
+
 // Per m-tile width: TT = 1 (decode-sized groups) streams weights once, so
 // non-temporal loads keep them from displacing the activations in L2; wider
 // tiles share each weight chunk between m-tiles of one XCD through L2.
 // NBUF = 3 at TT = 4 (two K blocks of weights in flight) fits in 2 waves/SIMD.
+// TT = 8 halves the weight bytes per MFMA; with one activation register set
+// and one token tile per scheduling group it also fits 2 waves/SIMD (two
+// workgroups per CU), which hides each other's load and barrier waits.
 template <bool GATEUP>
 hipError_t launch_tt(int tt, const GemmArgs& a, int grid, hipStream_t s) {
   switch (tt) {
     case 1: gemm_fp8_kernel<GATEUP, 1, 2, true><<<grid, 256, 0, s>>>(a); break;
     case 2: gemm_fp8_kernel<GATEUP, 2, 2, false><<<grid, 256, 0, s>>>(a); break;
     case 4: gemm_fp8_kernel<GATEUP, 4, 3, false><<<grid, 256, 0, s>>>(a); break;
+    case 8: gemm_fp8_kernel<GATEUP, 8, 2, false, 1, 2><<<grid, 256, 0, s>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -14,7 +14,7 @@ hipError_t launch_router_gemm_bf16(int T, int d, int E, int ksplit, const uint16
                                    const uint16_t* wr, float* zpart, hipStream_t s);
 hipError_t launch_router_gemm_f32(int T, int d, int E, const float* h, const float* wr,
                                   float* zpart, hipStream_t s);
-hipError_t launch_topk(int T, int E, int k, int ksplit, const float* zpart, const float* bias,
+hipError_t launch_topk(int T, int E, int k, int ksplit, float* zpart, const float* bias,
                        float scaling, int renorm, int32_t* ids, float* w, float* gap,
                        hipStream_t s);
 hipError_t launch_dense_route(int T, float scaling, int32_t* ids, float* w, float* gap,

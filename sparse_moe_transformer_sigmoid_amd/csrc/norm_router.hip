@@ -115,52 +115,96 @@ __global__ __launch_bounds__(NQ_THREADS) void norm_quant_kernel(int d, float eps
 }
 
 // z partial sums: zpart[ks][t][e] over columns [ks*kchunk, (ks+1)*kchunk).
-// Workgroup: 64 tokens x 64 experts; wave w owns tokens 16w..16w+15 and four
-// 16x16 MFMA tiles over the 64 experts (A = router rows, B = tokens).
+// Workgroup: 64 tokens x RG_E experts.  The tokens' h columns are staged
+// through LDS 128 columns at a time (double-buffered, in MFMA fragment order)
+// and shared by the 4 waves; wave w streams the router rows of experts
+// e0 + 48w .. e0 + 48w + 47 straight from global memory (the 5.5 MB router
+// matrix stays in L2) and keeps 3 x 4 tiles of 16 experts x 16 tokens.
+// MFMA v_mfma_f32_16x16x32_bf16: A = 16 router rows, B = 16 tokens, lane l
+// holds k = 8 (l / 16) .. + 7 of row / token l % 16.
+constexpr int RG_E = 192;
+constexpr int RG_KC = 128;
+
 __global__ __launch_bounds__(256) void router_gemm_bf16_kernel(int T, int d, int E, int kchunk,
                                                               const uint16_t* __restrict__ h,
                                                               const uint16_t* __restrict__ wr,
                                                               float* __restrict__ zpart) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t0 = blockIdx.x * 64 + wave * 16;
-  const int e0 = blockIdx.y * 64;
+  // [buffer][token tile tt][k32 step s][lane][16 B]
+  __shared__ __attribute__((aligned(16))) uint8_t hs[2][4 * 4 * 1024];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t0 = blockIdx.x * 64;
+  const int e0 = blockIdx.y * RG_E + 48 * wave;
   const int ks = blockIdx.z;
   const int kbeg = ks * kchunk;
-  const int tok = min(t0 + (lane & 15), T - 1);
-  const int kl = (lane >> 4) * 8;
-  const uint16_t* hp = h + (size_t)tok * d + kbeg + kl;
-  const uint16_t* wp[4];
-  bool fon[4];
+  const int nch = kchunk / RG_KC;
+
+  // staging: thread tid moves LDS chunk q = tid + 256 i (i = token tile):
+  // token 16 i + lane % 16, columns 32 s + 8 (lane / 16) .. + 7 with s = tid / 64
+  const int s_st = tid >> 6;
+  const uint16_t* hsrc[4];
 #pragma unroll
-  for (int f = 0; f < 4; ++f) {
+  for (int i = 0; i < 4; ++i) {
+    const int tok = min(t0 + 16 * i + (lane & 15), T - 1);
+    hsrc[i] = h + (size_t)tok * d + kbeg + 32 * s_st + 8 * (lane >> 4);
+  }
+  const uint16_t* wsrc[3];
+  bool fon[3];
+#pragma unroll
+  for (int f = 0; f < 3; ++f) {
     fon[f] = e0 + 16 * f < E;
     const int e = min(e0 + 16 * f + (lane & 15), E - 1);
-    wp[f] = wr + (size_t)e * d + kbeg + kl;
+    wsrc[f] = wr + (size_t)e * d + kbeg + 8 * (lane >> 4);
   }
-  v4f acc[4];
+  v4f acc[3][4];
 #pragma unroll
-  for (int f = 0; f < 4; ++f) acc[f] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-  for (int kk = 0; kk < kchunk; kk += 32) {
-    const v8bf b = *reinterpret_cast<const v8bf*>(hp + kk);
+  for (int f = 0; f < 3; ++f)
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      if (fon[f]) {
-        const v8bf a = *reinterpret_cast<const v8bf*>(wp[f] + kk);
-        acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[f], 0, 0, 0);
+    for (int i = 0; i < 4; ++i) acc[f][i] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  v4i stage[4];
+  auto load_h = [&](int c) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) stage[i] = *reinterpret_cast<const v4i*>(hsrc[i] + c * RG_KC);
+  };
+  auto store_h = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<v4i*>(&hs[buf][(tid + 256 * i) * 16]) = stage[i];
+  };
+  load_h(0);
+  store_h(0);
+  __syncthreads();
+  for (int c = 0; c < nch; ++c) {
+    const int buf = c & 1;
+    if (c + 1 < nch) load_h(c + 1);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      v8bf a[3];
+#pragma unroll
+      for (int f = 0; f < 3; ++f)
+        a[f] = *reinterpret_cast<const v8bf*>(wsrc[f] + c * RG_KC + 32 * s);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const v8bf b = *reinterpret_cast<const v8bf*>(&hs[buf][((i * 4 + s) * 64 + lane) * 16]);
+#pragma unroll
+        for (int f = 0; f < 3; ++f)
+          acc[f][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[f], b, acc[f][i], 0, 0, 0);
       }
     }
+    if (c + 1 < nch) store_h(buf ^ 1);
+    __syncthreads();
   }
-  // lane holds rows (experts) 4*(lane/16)+r of each tile, column (token) lane%16
-  const int tt = t0 + (lane & 15);
-  if (tt < T) {
+  // lane holds rows (experts) 4 (lane / 16) + r of each tile, column (token) lane % 16
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      if (fon[f]) {
-        const int e = e0 + 16 * f + 4 * (lane >> 4);
-        float4* zp = reinterpret_cast<float4*>(zpart + ((size_t)ks * T + tt) * E + e);
-        *zp = make_float4(acc[f][0], acc[f][1], acc[f][2], acc[f][3]);
-      }
+  for (int i = 0; i < 4; ++i) {
+    const int tt = t0 + 16 * i + (lane & 15);
+    if (tt >= T) continue;
+#pragma unroll
+    for (int f = 0; f < 3; ++f) {
+      if (!fon[f]) continue;
+      const int e = e0 + 16 * f + 4 * (lane >> 4);
+      float4* zp = reinterpret_cast<float4*>(zpart + ((size_t)ks * T + tt) * E + e);
+      *zp = make_float4(acc[f][i][0], acc[f][i][1], acc[f][i][2], acc[f][i][3]);
     }
   }
 }
@@ -268,6 +312,16 @@ __global__ __launch_bounds__(TK_WAVES * 64) void topk_kernel(int T, int E, int k
   }
 }
 
+// Split-K router partials -> logits, in place in slice 0: one thread per
+// (token, expert), partials added in ascending split order.
+__global__ __launch_bounds__(256) void zsum_kernel(long n, int ksplit, float* __restrict__ zpart) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float z = 0.f;
+  for (int ks = 0; ks < ksplit; ++ks) z += zpart[(size_t)ks * n + i];
+  zpart[i] = z;
+}
+
 __global__ void dense_route_kernel(int T, float scaling, int32_t* ids, float* w, float* gap) {
   const int t = blockIdx.x * 256 + threadIdx.x;
   if (t >= T) return;
@@ -290,7 +344,7 @@ hipError_t launch_norm_quant(bool fp8, int T, int d, float eps, const void* x, c
 
 hipError_t launch_router_gemm_bf16(int T, int d, int E, int ksplit, const uint16_t* h,
                                    const uint16_t* wr, float* zpart, hipStream_t s) {
-  dim3 grid((T + 63) / 64, (E + 63) / 64, ksplit);
+  dim3 grid((T + 63) / 64, (E + RG_E - 1) / RG_E, ksplit);
   router_gemm_bf16_kernel<<<grid, 256, 0, s>>>(T, d, E, d / ksplit, h, wr, zpart);
   return hipGetLastError();
 }
@@ -302,10 +356,17 @@ hipError_t launch_router_gemm_f32(int T, int d, int E, const float* h, const flo
   return hipGetLastError();
 }
 
-hipError_t launch_topk(int T, int E, int k, int ksplit, const float* zpart, const float* bias,
+hipError_t launch_topk(int T, int E, int k, int ksplit, float* zpart, const float* bias,
                        float scaling, int renorm, int32_t* ids, float* w, float* gap,
                        hipStream_t s) {
   const unsigned grid = (unsigned)((T + TK_WAVES - 1) / TK_WAVES);
+  // with split-K partials, reduce them over all CUs first: one wave per token
+  // summing ksplit partials of each expert is a long dependent load chain
+  if (ksplit > 1) {
+    const long n = (long)T * E;
+    zsum_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(n, ksplit, zpart);
+    ksplit = 1;
+  }
 #define K2_TOPK(J, K)                                                                      \
   topk_kernel<J, K><<<grid, TK_WAVES * 64, 0, s>>>(T, E, k, ksplit, zpart, bias, scaling, \
                                                    renorm, ids, w, gap)
