@@ -19,8 +19,11 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBDIR = os.path.join(PKG, "lib")
 LIBNAME = "libk2moe.so"
-SOURCES = ["abi.hip", "norm_router.hip", "permute.hip", "gemm_fp8.hip", "gemm_f32.hip",
-           "combine_pack.hip"]
+SOURCES = ["abi.hip", "norm_router.hip", "permute.hip", "gemm_fp8.hip", "gemm_fp8_wide.hip",
+           "gemm_f32.hip", "combine_pack.hip"]
+# per-source extra flags: the wide gate/up GEMM is scheduled to minimise registers,
+# which lets it keep two token tiles in flight at 2 waves/SIMD without spilling
+EXTRA_FLAGS = {"gemm_fp8_wide.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-minreg"]}
 ARCH = "gfx950"
 
 
@@ -52,7 +55,8 @@ def build(verbose: bool = False) -> str:
 
     def one(src):
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
-        cmd = [cc, *compile_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *compile_flags(), *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src),
+               "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

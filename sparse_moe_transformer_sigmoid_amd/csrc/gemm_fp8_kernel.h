@@ -1,0 +1,378 @@
+// Grouped block-scaled FP8 GEMMs of the K2 experts on gfx950 MFMA.
+//
+// Experts are SwiGLU MLPs without biases ("Kimi-K2-Base", Feed-forward:
+// down_proj(act_fn(gate_proj(x)) * up_proj(x)), act_fn = SiLU); weights are
+// e4m3 with one fp32 scale per 128x128 block and activations e4m3 with one
+// fp32 scale per token and 128 columns ("Kimi K2 · Architecture",
+// config.json quantization_config).  Per 128-wide K block the MFMA sums
+// exact e4m3 products into a fresh fp32 tile, which is then added to the
+// running accumulator times (activation scale * weight scale).
+//
+// Work item = (group, 256-row weight chunk, m-tile of 16*TT rows).  A
+// workgroup has 4 waves; wave w streams 64 weight rows (four 16x128 MFMA
+// fragments per K block, 8 KiB, contiguous in the packed layout) straight
+// into registers, double-buffered one K block ahead.  The m-tile's activation
+// rows are gathered into LDS in fragment order (double-buffered).  MFMA:
+// v_mfma_scale_f32_16x16x128_f8f6f4 with unit scales, A = 16 weight rows,
+// B = 16 tokens, so lane l of the 16x16 result holds weight rows
+// 4*(l/16)..+3 of token l%16.
+//
+// Gate/up (GATEUP): the 256 rows of chunk j are hidden features
+// 128j..128j+127 of gate and of up; wave w holds gate and up rows
+// 32w..32w+31 of them, so silu(g)*u is formed in registers and the 1x128
+// requantisation needs one cross-wave max.  Down: chunk j is output
+// features 256j..256j+255; the epilogue optionally multiplies by the
+// routing weight and writes fp32 rows.
+//
+// Workgroup ids are remapped so each XCD takes a contiguous run of work
+// items: the m-tiles of one weight chunk, and the chunks of one expert, then
+// share that XCD's L2.
+#pragma once
+#include "k2_common.h"
+#include "k2_launch.h"
+
+
+namespace k2 {
+
+namespace {
+
+// largest K / 128 of either GEMM (d_model <= 16384, d_ff <= 65536)
+constexpr int MAX_NKB = 512;
+
+__device__ __forceinline__ v8i join8(v4i a, v4i b) {
+  return v8i{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+}
+
+__device__ __forceinline__ v4f mfma_fp8(v8i a, v8i b) {
+  const v4f zero = {0.f, 0.f, 0.f, 0.f};
+  // atype = btype = 0 (e4m3), E8M0 scales 127 = 2^0
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 127, 0, 127);
+}
+
+struct WorkItem {
+  bool valid;
+  bool shared_grp;
+  int grp, nc, row0, mcount, ntt;
+};
+
+// Work item L (after the XCD remap) -> (group, weight chunk, m-tile).  The
+// grid is a host-side upper bound; workgroups past the device-side m-tile
+// count get valid = false.
+__device__ __forceinline__ WorkItem decode_work(const GemmArgs& g, int BM) {
+  WorkItem w{};
+  const int Wtot = g.mt_start[g.G] * g.NC;
+  const int Wp = (Wtot + 7) & ~7;
+  const int b = blockIdx.x;
+  w.valid = false;
+  if (b >= Wp) return w;
+  const int L = (b & 7) * (Wp >> 3) + (b >> 3);
+  if (L >= Wtot) return w;
+  const int q = L / g.NC;
+  int lo = 0, hi = g.G;                    // mt_start[lo] <= q < mt_start[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (g.mt_start[mid] <= q) lo = mid; else hi = mid;
+  }
+  w.grp = lo;
+  w.shared_grp = lo >= g.E;
+  int row0_g, m_g;
+  if (w.shared_grp) {
+    row0_g = g.P;
+    m_g = g.T;
+  } else {
+    row0_g = min(max(g.offsets[lo], 0), g.P);
+    m_g = min(max(g.offsets[lo + 1] - row0_g, 0), g.P - row0_g);
+  }
+  // the group's rows are split into ceil(m / BM) m-tiles of near-equal size
+  // (at most BM rows each), so the last tile of a group is not mostly padding
+  const int mtiles = (m_g + BM - 1) / BM;
+  const int rr = L - g.mt_start[lo] * g.NC;
+  w.nc = rr / mtiles;
+  const int mt = rr - w.nc * mtiles;
+  const int r_lo = (int)(((int64_t)mt * m_g) / mtiles);
+  const int r_hi = (int)(((int64_t)(mt + 1) * m_g) / mtiles);
+  w.row0 = row0_g + r_lo;
+  w.mcount = r_hi - r_lo;
+  w.ntt = (w.mcount + 15) >> 4;
+  w.valid = true;
+  return w;
+}
+
+// activation row of the m-th row of a tile (padding rows repeat the last)
+template <bool GATEUP>
+__device__ __forceinline__ int act_row_of(const GemmArgs& g, const WorkItem& w, int m) {
+  const int mm = min(m, w.mcount - 1);
+  if constexpr (GATEUP) {
+    if (w.shared_grp) return w.row0 + mm - g.P;
+    const int tok = g.row_pair[w.row0 + mm] / g.k;
+    return min(max(tok, 0), g.T - 1);
+  } else {
+    return w.row0 + mm;
+  }
+}
+
+// Accumulators -> outputs.  acc[rt][tt] lane l holds weight rows
+// 64 wave + 16 rt + 4 (l / 16) + r of token row 16 tt + l % 16.
+template <bool GATEUP, int TT>
+__device__ __forceinline__ void epilogue(const GemmArgs& g, v4f (&acc)[4][TT], float* lds_red,
+                                         const WorkItem& wi, int wave, int lane) {
+  const int nc = wi.nc, row0 = wi.row0, mcount = wi.mcount, ntt = wi.ntt;
+  const bool shared_grp = wi.shared_grp;
+  if constexpr (GATEUP) {
+    // a = silu(g) * u for hidden 32w + 16h + 4(l/16) + r, h in {0,1}
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      float mx = 0.f;
+      if (tt < ntt) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float gv = acc[h][tt][r], uv = acc[h + 2][tt][r];
+            const float a = gv / (1.0f + expf(-gv)) * uv;
+            acc[h][tt][r] = a;
+            mx = fmaxf(mx, fabsf(a));
+          }
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      if (lane < 16) lds_red[(wave * TT + tt) * 16 + lane] = mx;
+    }
+    __syncthreads();
+    const int nblk = g.I / QBLK;
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      if (tt < ntt) {
+        const int j = lane & 15;
+        float amax = lds_red[(0 * TT + tt) * 16 + j];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) amax = fmaxf(amax, lds_red[(w * TT + tt) * 16 + j]);
+        const float sc = fp8_scale(amax);
+        const int m = tt * 16 + j;
+        if (m < mcount) {
+          const size_t row = (size_t)(row0 + m);
+          uint8_t* dst = g.aq + row * g.I + nc * QBLK + 32 * wave + 4 * (lane >> 4);
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const v4f a = acc[h][tt];
+            const uint32_t q4 = cvt4_e4m3(clamp_fp8(a[0] / sc), clamp_fp8(a[1] / sc),
+                                          clamp_fp8(a[2] / sc), clamp_fp8(a[3] / sc));
+            *reinterpret_cast<uint32_t*>(dst + 16 * h) = q4;
+          }
+          if (wave == 0 && lane < 16) g.as[row * nblk + nc] = sc;
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      if (tt < ntt) {
+        const int m = tt * 16 + (lane & 15);
+        if (m < mcount) {
+          const int row = row0 + m;
+          float wt = 1.f;
+          const bool mul = g.weighted && !shared_grp;
+          if (mul) wt = g.topk_w[min(max(g.row_pair[row], 0), g.P - 1)];
+          float* dst = shared_grp ? g.shared_out + (size_t)(row - g.P) * g.d
+                                  : g.rows + (size_t)row * g.d;
+          dst += nc * 256 + 64 * wave + 4 * (lane >> 4);
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt) {
+            v4f o = acc[rt][tt];
+            if (mul) o = o * wt;
+            *reinterpret_cast<float4*>(dst + 16 * rt) = make_float4(o[0], o[1], o[2], o[3]);
+          }
+        }
+      }
+    }
+  }
+}
+
+// TT: 16-row token tiles per m-tile; NBUF: weight register ring depth (prefetch
+// distance NBUF-1 K blocks); NT: stream weights with non-temporal loads, for
+// launches where each weight chunk is read by a single m-tile.
+// BSETS: activation register sets (2: loaded two K blocks ahead; 1: one block
+// ahead, saving registers); MINW: waves per SIMD the register budget must allow.
+// GRPX: token tiles per scheduling group (0: the default for TT and MINW).
+template <bool GATEUP, int TT, int NBUF, bool NT, int BSETS = 2, int MINW = 1, int GRPX = 0>
+__global__ __launch_bounds__(256, MINW) void gemm_fp8_kernel(const GemmArgs g) {
+  static_assert(NBUF >= 2 && NBUF <= 4, "NBUF must be 2, 3 or 4");
+  static_assert(BSETS == 1 || BSETS == 2, "BSETS must be 1 or 2");
+  constexpr int BM = 16 * TT;
+  constexpr int CPT = (TT * 128 + 255) / 256;   // 16-byte staging chunks per thread
+  // LDS rows past the tile (TT < 2) are write-only padding: every thread
+  // stages its chunk unconditionally, keeping the K loop free of branches
+  constexpr int LDS_B = (TT * 2048 > 256 * 16 * ((TT * 128 + 255) / 256)) ? TT * 2048
+                                                                          : 256 * 16 * ((TT * 128 + 255) / 256);
+  __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][LDS_B];
+  __shared__ float lds_sa[2][256];
+  // this chunk's weight scales for every K block, loaded once: scalar loads in
+  // the loop would share lgkmcnt with the LDS reads and stall each step on
+  // a memory round trip
+  __shared__ float lds_sw[2 * MAX_NKB];
+  __shared__ float lds_red[GATEUP ? 4 * TT * 16 : 1];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  const WorkItem wi = decode_work(g, BM);
+  if (!wi.valid) return;
+  const int grp = wi.grp, nc = wi.nc, row0 = wi.row0, mcount = wi.mcount, ntt = wi.ntt;
+  const bool shared_grp = wi.shared_grp;
+
+  auto act_row = [&](int m) { return act_row_of<GATEUP>(g, wi, m); };
+
+  // staging of the activation tile into LDS in fragment order
+  // [tt][half p][lane][16 B]: LDS chunk q = tid + 256 i holds, for
+  // tt = q / 128, p = (q / 64) % 2, lane = q % 64, the 16 bytes of row
+  // 16 tt + lane % 16 at column 32 (lane / 16) + 16 p.  Consecutive lanes
+  // write consecutive 16-byte LDS chunks (no bank conflicts).
+  uint32_t boff[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int q = tid + 256 * i;
+    const int m = (q >> 7) * 16 + (q & 15);   // past the tile for q >= TT*128: clamped row
+    const int col = 32 * ((q & 63) >> 4) + 16 * ((q >> 6) & 1);
+    boff[i] = (uint32_t)act_row(m) * (uint32_t)g.act_ld + col;
+  }
+  // thread tid stages the activation scale of tile row tid (clamped past the tile)
+  const uint32_t saoff = (uint32_t)act_row(tid) * g.nkb;
+
+  const uint8_t* wp = g.wpk + (size_t)grp * g.expert_stride +
+                      (size_t)(nc * 4 + wave) * (size_t)g.nkb * 8192 + lane * 16;
+  const float* swp_base = g.wscale + (size_t)grp * g.wscale_stride + (size_t)nc * g.nkb * 2;
+
+  // gate/up: [kb][gate, up] of chunk nc; down: [row block 2nc + h][kb], h = 0, 1
+  for (int i = tid; i < 2 * g.nkb; i += 256) lds_sw[i] = swp_base[i];
+
+  v4f acc[4][TT];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) acc[rt][tt] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // weight fragments: a ring of NBUF register buffers, loaded NBUF-1 K blocks ahead;
+  // activations: two register sets, loaded two K blocks ahead, stored to LDS one
+  // block ahead (LDS double buffer)
+  v8i wbuf[NBUF][4];
+  v4i breg[BSETS][CPT];
+  float sareg[2] = {0.f, 0.f};
+
+  auto load_w = [&](v8i (&w)[4], int kb) {
+    const uint8_t* p = wp + (size_t)kb * 8192;
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      const v4i* p4 = reinterpret_cast<const v4i*>(p + rt * 2048);
+      if constexpr (NT) {
+        w[rt] = join8(__builtin_nontemporal_load(p4), __builtin_nontemporal_load(p4 + 64));
+      } else {
+        w[rt] = join8(p4[0], p4[64]);
+      }
+    }
+  };
+  auto load_b = [&](int set, int kb) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i)
+      breg[set][i] = *reinterpret_cast<const v4i*>(g.act + boff[i] + kb * 128);
+    sareg[set] = g.act_s[saoff + kb];
+  };
+  auto store_b = [&](int set, int buf) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i)
+      *reinterpret_cast<v4i*>(&lds_b[buf][(tid + 256 * i) * 16]) = breg[set][i];
+    lds_sa[buf][tid] = sareg[set];
+  };
+  auto weight_scales = [&](int kb, float& s_gate_or_down, float& s_up) {
+    if constexpr (GATEUP) {
+      s_gate_or_down = lds_sw[2 * kb];
+      s_up = lds_sw[2 * kb + 1];
+    } else {
+      s_gate_or_down = lds_sw[(wave >> 1) * g.nkb + kb];
+      s_up = s_gate_or_down;
+    }
+  };
+  // Every tile of the m-tile is computed (rows past mcount are discarded at
+  // the end): no branches in the hot loop, so the MFMA of one tile overlaps
+  // the fp32 scaling of the previous tile's result.  Token tiles go in groups
+  // of GRP; a scheduling fence between groups keeps the compiler from hoisting
+  // every B fragment at once (register pressure at large TT; one tile per
+  // group when the register budget is sized for 2 waves/SIMD).
+  constexpr int GRP = GRPX ? GRPX : (TT < 4 ? TT : (MINW > 1 ? 1 : 4));
+  auto compute = [&](const v8i (&w)[4], int buf, int kb) {
+    float swg, swu;
+    weight_scales(kb, swg, swu);
+#pragma unroll
+    for (int t0 = 0; t0 < TT; t0 += GRP) {
+      v8i bf[GRP];
+      float s0[GRP], s1[GRP];
+#pragma unroll
+      for (int u = 0; u < GRP; ++u) {
+        const uint8_t* bp = &lds_b[buf][(t0 + u) * 2048 + lane * 16];
+        bf[u] = join8(*reinterpret_cast<const v4i*>(bp), *reinterpret_cast<const v4i*>(bp + 1024));
+        const float sa_t = lds_sa[buf][(t0 + u) * 16 + (lane & 15)];
+        s0[u] = sa_t * swg;
+        s1[u] = sa_t * swu;
+      }
+      v4f prev = mfma_fp8(w[0], bf[0]);
+#pragma unroll
+      for (int i = 1; i < 4 * GRP; ++i) {
+        const int u = i >> 2, rt = i & 3;
+        const v4f cur = mfma_fp8(w[rt], bf[u]);
+        const int pu = (i - 1) >> 2, pr = (i - 1) & 3;
+        acc[pr][t0 + pu] += prev * (pr < 2 ? s0[pu] : s1[pu]);
+        prev = cur;
+      }
+      acc[3][t0 + GRP - 1] += prev * s1[GRP - 1];
+      if (t0 + GRP < TT) __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // ---------------------------------------------------------------- K loop
+  // Block kb: weights in wbuf[kb % NBUF] with scales sw[kb % NBUF]; activations
+  // in LDS buffer kb & 1, staged from register set (kb & 1).  Vector loads
+  // retire in issue order, so each step issues the activations of block kb+2
+  // before the weights of block kb+NBUF-1, and ends by waiting only for the
+  // activations of block kb+1 (issued one step earlier).
+  const int nkb = g.nkb;
+  load_b(0, 0);
+  if (BSETS == 2 && nkb > 1) load_b(BSETS - 1, 1);
+#pragma unroll
+  for (int i = 0; i < NBUF - 1; ++i)
+    if (i < nkb) load_w(wbuf[i], i);
+  store_b(0, 0);
+  __syncthreads();
+  // One step: prefetch (activations of kb+2, weights of kb+NBUF-1; indices
+  // clamped to the last block, so the tail re-reads a block instead of
+  // branching), compute block kb, stage block kb+1 into LDS, barrier.  STEP is
+  // a multiple of NBUF and of 2, so every buffer index is a compile-time
+  // constant; full STEPs run without guards, the tail with them.
+  constexpr int STEP = (NBUF & 1) ? 2 * NBUF : NBUF;
+  auto step = [&](const int j, const int kb) {
+    const int cur = j & 1;
+    if constexpr (BSETS == 2) load_b(cur, min(kb + 2, nkb - 1));
+    else load_b(0, min(kb + 1, nkb - 1));
+    load_w(wbuf[(j + NBUF - 1) % NBUF], min(kb + NBUF - 1, nkb - 1));
+    // keep the prefetches issued here: the scheduler would otherwise sink
+    // them next to their use to save registers, undoing the ring
+    __builtin_amdgcn_sched_barrier(0);
+    compute(wbuf[j % NBUF], cur, kb);
+    store_b(BSETS == 2 ? cur ^ 1 : 0, cur ^ 1);
+    __syncthreads();
+  };
+  int kb0 = 0;
+  for (; kb0 + STEP <= nkb; kb0 += STEP) {
+#pragma unroll
+    for (int j = 0; j < STEP; ++j) step(j, kb0 + j);
+  }
+#pragma unroll
+  for (int j = 0; j < STEP; ++j)
+    if (kb0 + j < nkb) step(j, kb0 + j);
+
+  epilogue<GATEUP, TT>(g, acc, lds_red, wi, wave, lane);
+}
+
+}  // namespace
+
+// gate/up launch of 128-row m-tiles (compiled in its own translation unit)
+hipError_t launch_gateup_tt8(const GemmArgs& a, int grid, hipStream_t s);
+
+}  // namespace k2
