@@ -30,10 +30,11 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA
 # HBM bytes per launch of the gate/up GEMM, from rocprofv3 --pmc FETCH_SIZE (x2.000,
 # the factor a 1 GiB copy probe gives) + WRITE_SIZE (x1.000), see
-# profiles/gemm_gateup_k2_decode.md; valid only for the gemm_fp8.hip source whose
+# profiles/gemm_gateup_k2_decode.md; valid only for the GEMM sources whose combined
 # sha256 starts with the recorded prefix (null otherwise).
-MEASURED_TRAFFIC = {"k2_decode": ("62a56a6558074288", 7.812e9)}
-GEMM_SRC = os.path.join(ROOT, "sparse_moe_transformer_sigmoid_amd", "csrc", "gemm_fp8.hip")
+MEASURED_TRAFFIC = {"k2_decode": ("5b152551a76d0812", 7.928e9)}
+GEMM_SRCS = [os.path.join(ROOT, "sparse_moe_transformer_sigmoid_amd", "csrc", f)
+             for f in ("gemm_fp8_kernel.h", "gemm_fp8.hip")]
 
 
 def measured_traffic(workload: str):
@@ -41,8 +42,10 @@ def measured_traffic(workload: str):
     rec = MEASURED_TRAFFIC.get(workload)
     if rec is None:
         return None
-    sha = hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()
-    return rec[1] if sha.startswith(rec[0]) else None
+    h = hashlib.sha256()
+    for f in GEMM_SRCS:
+        h.update(open(f, "rb").read())
+    return rec[1] if h.hexdigest().startswith(rec[0]) else None
 
 
 def parse():
