@@ -19,11 +19,16 @@ __global__ __launch_bounds__(256) void combine_kernel(int T, int d, int k,
                                                      int mul_w, const float* __restrict__ shared,
                                                      const void* __restrict__ residual,
                                                      void* __restrict__ out) {
+  // one token per blockIdx.x, 1024 columns per blockIdx.y: small batches
+  // still spread over the chip, and the k row reads of a thread are issued
+  // together (the sum itself stays in slot order)
   const int t = blockIdx.x;
   const int P = T * k;
   const int d4 = d >> 2;
-  for (int n4 = threadIdx.x; n4 < d4; n4 += 256) {
+  const int n4 = blockIdx.y * 256 + threadIdx.x;
+  if (n4 < d4) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
     for (int slot = 0; slot < k; ++slot) {
       const int p = t * k + slot;
       const int r = min(max(pair_row[p], 0), P - 1);
@@ -121,8 +126,8 @@ hipError_t launch_combine(bool x_bf16, bool out_f32, int T, int d, int k, const 
                           const float* shared_out, const void* residual, void* out,
                           hipStream_t s) {
 #define K2_COMB(XB, OF)                                                                   \
-  combine_kernel<XB, OF><<<T, 256, 0, s>>>(T, d, k, rows, pair_row, topk_w, mul_w, shared_out, \
-                                           residual, out)
+  combine_kernel<XB, OF><<<dim3(T, (d / 4 + 255) / 256), 256, 0, s>>>(                     \
+      T, d, k, rows, pair_row, topk_w, mul_w, shared_out, residual, out)
   if (x_bf16) {
     if (out_f32) K2_COMB(true, true); else K2_COMB(true, false);
   } else {

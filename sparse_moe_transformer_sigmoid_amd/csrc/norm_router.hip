@@ -171,29 +171,45 @@ __global__ __launch_bounds__(256) void router_gemm_bf16_kernel(int T, int d, int
     for (int i = 0; i < 4; ++i)
       *reinterpret_cast<v4i*>(&hs[buf][(tid + 256 * i) * 16]) = stage[i];
   };
-  load_h(0);
-  store_h(0);
-  __syncthreads();
-  for (int c = 0; c < nch; ++c) {
+  // router-row fragments of one 128-column chunk, loaded one chunk ahead
+  v8bf wa[2][3][4];
+  auto load_w = [&](v8bf (&a)[3][4], int c) {
+#pragma unroll
+    for (int f = 0; f < 3; ++f)
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        a[f][s] = *reinterpret_cast<const v8bf*>(wsrc[f] + c * RG_KC + 32 * s);
+  };
+  auto chunk = [&](const v8bf (&a)[3][4], v8bf (&an)[3][4], int c) {
     const int buf = c & 1;
-    if (c + 1 < nch) load_h(c + 1);
+    const bool more = c + 1 < nch;
+    if (more) {
+      load_h(c + 1);
+      load_w(an, c + 1);
+    }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      v8bf a[3];
-#pragma unroll
-      for (int f = 0; f < 3; ++f)
-        a[f] = *reinterpret_cast<const v8bf*>(wsrc[f] + c * RG_KC + 32 * s);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const v8bf b = *reinterpret_cast<const v8bf*>(&hs[buf][((i * 4 + s) * 64 + lane) * 16]);
 #pragma unroll
         for (int f = 0; f < 3; ++f)
-          acc[f][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[f], b, acc[f][i], 0, 0, 0);
+          acc[f][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[f][s], b, acc[f][i], 0, 0, 0);
       }
     }
-    if (c + 1 < nch) store_h(buf ^ 1);
+    if (more) store_h(buf ^ 1);
     __syncthreads();
+  };
+  load_h(0);
+  load_w(wa[0], 0);
+  store_h(0);
+  __syncthreads();
+  int c = 0;
+  for (; c + 2 <= nch; c += 2) {
+    chunk(wa[0], wa[1], c);
+    chunk(wa[1], wa[0], c + 1);
   }
+  if (c < nch) chunk(wa[0], wa[1], c);
   // lane holds rows (experts) 4 (lane / 16) + r of each tile, column (token) lane % 16
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -318,6 +334,8 @@ __global__ __launch_bounds__(256) void zsum_kernel(long n, int ksplit, float* __
   const long i = (long)blockIdx.x * 256 + threadIdx.x;
   if (i >= n) return;
   float z = 0.f;
+  // loads issued 16 at a time; the additions stay in ascending split order
+#pragma unroll 16
   for (int ks = 0; ks < ksplit; ++ks) z += zpart[(size_t)ks * n + i];
   zpart[i] = z;
 }

@@ -18,7 +18,7 @@ namespace k2 {
 
 namespace {
 
-constexpr int MASK_WORDS = 12288;  // 48 KiB of per-expert token bitmasks
+constexpr int MASK_WORDS = 2048;  // per-expert token bitmasks: 2 words x up to 1024 experts
 
 // Exclusive scan of get(0..n-1) by a 1024-thread block; out[n] = total.
 template <int IPT, class F>
@@ -72,6 +72,7 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(int E, int nchunk,
   __shared__ int32_t tot[1024];
   for (int e = threadIdx.x; e < E; e += 1024) {
     int32_t run = 0;
+#pragma unroll 8
     for (int c = 0; c < nchunk; ++c) {
       chunk_base[(size_t)c * E + e] = run;
       run += chunk_counts[(size_t)c * E + e];
@@ -135,9 +136,12 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(int E, int n_shared, 
 
 }  // namespace
 
+// 64 tokens per chunk: a large batch spreads the count and scatter passes over
+// many workgroups (8192 tokens -> 128), and a token's rank needs at most two
+// mask words
 int perm_chunk_tokens(int E) {
   int words = MASK_WORDS / E;
-  if (words > 32) words = 32;
+  if (words > 2) words = 2;
   return 32 * words;
 }
 
