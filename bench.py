@@ -9,9 +9,10 @@ synthetic tensors already resident in HBM; weights are random-init FP8 with
 128x128 block scales at the released K2 shape.
 
 Prints one JSON line: tokens/s for the named workload (default: the 64-token
-decode step), the dominant kernel's roofline fraction measured with HIP
-events inside the timed region, the same for the 8192-token prefill, and the
-CPU oracle timed on a bounded sample of the same workload.
+decode step, its timed steps replayed from a HIP graph of moe_forward; --eager
+times plain launches), the dominant kernel's roofline fraction measured with
+HIP events inside an eager timed region, the same for the 8192-token prefill,
+and the CPU oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -57,6 +58,8 @@ def parse():
                     choices=["decode", "prefill", "skewed", "dense"])
     ap.add_argument("--no-secondary", action="store_true", help="skip the prefill line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="time decode with eager launches instead of a HIP graph")
     ap.add_argument("--cpu-tokens", type=int, default=16)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="also run a plain fp32 copy of BYTES (counter calibration)")
@@ -96,6 +99,24 @@ def timed(layer, x, steps, warmup):
     return start.elapsed_time(stop) / steps, stage
 
 
+def timed_graph(layer, x, steps, warmup):
+    """ms per forward when moe_forward is replayed from a HIP graph."""
+    import torch
+    out = torch.empty((x.shape[0], layer.shape.d_model), dtype=x.dtype, device=x.device)
+    g = layer.capture_forward(x, out)
+    for _ in range(warmup):
+        g.replay()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        g.replay()
+    stop.record()
+    torch.cuda.synchronize()
+    del g
+    return start.elapsed_time(stop) / steps
+
+
 def routing_stats(layer, x):
     import numpy as np
     import torch
@@ -106,11 +127,14 @@ def routing_stats(layer, x):
     return int(np.sum(counts > 0)), counts
 
 
-def run_workload(layer, inp, steps, warmup):
+def run_workload(layer, inp, steps, warmup, graph=False):
     shape = inp.shape
     T = inp.x.shape[0]
     layer.use_router(inp)
     ms, stage = timed(layer, inp.x, steps, warmup)
+    eager_ms = ms
+    if graph:
+        ms = timed_graph(layer, inp.x, steps, warmup)
     touched, counts = routing_stats(layer, inp.x)
     touched_all = touched + shape.n_shared
     d, I, k = shape.d_model, shape.d_ff, shape.top_k
@@ -122,7 +146,7 @@ def run_workload(layer, inp, steps, warmup):
     gu_flops = 2.0 * rows * (2 * I) * d
     dn_flops = 2.0 * rows * I * d
     gu_s = stage["gateup"] * 1e-3
-    return dict(T=T, ms=ms, stage=stage, touched=touched_all, counts=counts,
+    return dict(T=T, ms=ms, eager_ms=eager_ms, stage=stage, touched=touched_all, counts=counts,
                 gu_bytes=gu_bytes, gu_flops=gu_flops, total_flops=gu_flops + dn_flops,
                 gu_gbs=gu_bytes / gu_s / 1e9 if gu_s > 0 else 0.0,
                 gu_tflops=gu_flops / gu_s / 1e12 if gu_s > 0 else 0.0)
@@ -192,13 +216,17 @@ def main():
     print(f"# inputs generated and packed in {time.time() - t0:.1f} s", file=sys.stderr,
           flush=True)
 
-    res = run_workload(layer, inp, args.steps, args.warmup)
+    # decode is launch-sensitive: the timed steps replay moe_forward from a HIP
+    # graph (the same kernels and buffers); the eager time is reported beside it
+    graph = args.workload == "decode" and not args.eager
+    res = run_workload(layer, inp, args.steps, args.warmup, graph=graph)
     T = res["T"]
     value = T / (res["ms"] * 1e-3)
     gu_ms = res["stage"]["gateup"]
     line = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["ms"],
+        "eager_ms_per_step": res["eager_ms"], "launch": "hip_graph" if graph else "eager",
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp8e4m3", "data": "synthetic",
         "config": {"workload": shp.name, "tokens": T, "d_model": shp.d_model,

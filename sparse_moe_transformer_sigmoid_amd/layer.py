@@ -179,3 +179,21 @@ class K2MoE:
         L.call("moe_forward", C.byref(self.cfg), T, _p(x), _p(self.norm_w), _p(self.w_router),
                _p(self.bias), _p(self.packed), _p(out), _p(ws), ws.numel(), _stream())
         return out
+
+    def capture_forward(self, x: torch.Tensor, out: torch.Tensor) -> torch.cuda.CUDAGraph:
+        """Record moe_forward(x) -> out into a HIP graph (replay with .replay()).
+
+        The workspace for x's token count is allocated before capture; moe_forward
+        enqueues kernels only (no allocation, memset or synchronisation), so the
+        graph replays the same launches with the same buffers.
+        """
+        self.workspace(x.shape[0], L.MOE_WS_FORWARD)
+        side = torch.cuda.Stream(device=self.device)
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):            # one eager call off the default stream
+            self.forward(x, out)
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.forward(x, out)
+        return g

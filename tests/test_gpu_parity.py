@@ -279,6 +279,27 @@ def test_k2_skewed(k2):
     check_layer(inp, g, tokens=toks)
 
 
+def test_k2_decode_graph_replay(k2):
+    """moe_forward captured in a HIP graph: every replay equals the eager call,
+    with eager work on other inputs and synchronisations between replays."""
+    base, layer = k2
+    layer.use_router(base)
+    x = base.x
+    eager = layer.forward(x).clone()
+    other = torch.flip(x, dims=[0]).contiguous()
+    out = torch.empty_like(eager)
+    g = layer.capture_forward(x, out)
+    for r in range(3):
+        out.zero_()
+        layer.forward(other)                  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        _log(f"graph replay {r}")
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {r}"
+    del g
+
+
 def test_k2_dense_ffn():
     inp = synth.generate(synth.K2_DENSE, seed=0, device="cuda")
     layer = _layer(inp)
