@@ -215,10 +215,17 @@ int gemm_tt(const Dims& D) {
   return 8;
 }
 
+// upper bound of the GEMM m-tiles of a call (the device-side count is exact):
+// each non-empty group adds at most bm - 1 padding rows, plus the shared group
+int64_t mtile_bound(const Dims& D, int bm) {
+  const int64_t nz = std::min<int64_t>(D.E, D.P);
+  return (D.P + (int64_t)(bm - 1) * nz) / bm + 1 + (D.S ? ((int64_t)D.T + bm - 1) / bm : 0);
+}
+
 struct Layout {
   size_t hbuf = 0, xq = 0, xs = 0, zpart = 0, ids = 0, w = 0, gap = 0, ccount = 0, cbase = 0,
-         offsets = 0, row_pair = 0, pair_row = 0, mt_start = 0, aq = 0, as = 0, rows = 0,
-         shared = 0, total = 0;
+         offsets = 0, row_pair = 0, pair_row = 0, mt_start = 0, tile_group = 0, aq = 0, as = 0,
+         rows = 0, shared = 0, total = 0;
   int ksplit = 1, nchunk = 1;
 };
 
@@ -259,6 +266,7 @@ Layout layout(const Dims& D, int entry) {
   }
   if (fwd || entry == MOE_WS_SWIGLU) {
     L.mt_start = take(((size_t)D.G + 1) * 4);
+    if (D.fp8) L.tile_group = take((size_t)mtile_bound(D, 16 * gemm_tt(D)) * 4);
     const size_t nrows = P + (D.S ? T : 0);
     if (D.fp8) {
       L.aq = take(nrows * I);
@@ -354,13 +362,13 @@ moe_status run_experts(const Dims& D, const Layout& L, void* ws, const void* xq,
   const int tt = gemm_tt(D);
   const int bm = 16 * tt;
   int32_t* mt_start = at<int32_t>(ws, L.mt_start);
+  int32_t* tile_group = at<int32_t>(ws, L.tile_group);
+  const int64_t mt_bound = mtile_bound(D, bm);
   {
     Stage st(MOE_STAGE_TILES, s);
-    K2_HIP(k2::launch_build_tiles(D.E, D.S, T, D.k, bm, offsets, mt_start, s));
+    K2_HIP(k2::launch_build_tiles(D.E, D.S, T, D.k, bm, (int)mt_bound, offsets, mt_start,
+                                  tile_group, s));
   }
-  // upper bound of the m-tiles actually present (device-side count)
-  const int64_t nz = std::min<int64_t>(D.E, D.P);
-  const int64_t mt_bound = (D.P + (int64_t)(bm - 1) * nz) / bm + 1 + (D.S ? (T + bm - 1) / bm : 0);
   auto grid_of = [&](int nc) {
     const int64_t g = (mt_bound * nc + 7) / 8 * 8;
     return (int)std::min<int64_t>(g, (int64_t)1 << 30);
@@ -373,6 +381,7 @@ moe_status run_experts(const Dims& D, const Layout& L, void* ws, const void* xq,
   a.offsets = offsets;
   a.row_pair = row_pair;
   a.mt_start = mt_start;
+  a.tile_group = tile_group;
   a.E = D.E;
   a.G = D.G;
   a.T = T;

@@ -68,11 +68,7 @@ __device__ __forceinline__ WorkItem decode_work(const GemmArgs& g, int BM) {
   const int L = (b & 7) * (Wp >> 3) + (b >> 3);
   if (L >= Wtot) return w;
   const int q = L / g.NC;
-  int lo = 0, hi = g.G;                    // mt_start[lo] <= q < mt_start[hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (g.mt_start[mid] <= q) lo = mid; else hi = mid;
-  }
+  const int lo = min(max(g.tile_group[q], 0), g.G - 1);   // mt_start[lo] <= q < mt_start[lo+1]
   w.grp = lo;
   w.shared_grp = lo >= g.E;
   int row0_g, m_g;

@@ -25,8 +25,9 @@ int perm_chunk_tokens(int E);
 hipError_t launch_permute(int T, int E, int k, const int32_t* ids, int32_t* chunk_counts,
                           int32_t* chunk_base, int32_t* offsets, int32_t* row_pair,
                           int32_t* pair_row, hipStream_t s);
-hipError_t launch_build_tiles(int E, int n_shared, int T, int k, int bm, const int32_t* offsets,
-                              int32_t* mt_start, hipStream_t s);
+hipError_t launch_build_tiles(int E, int n_shared, int T, int k, int bm, int max_tiles,
+                              const int32_t* offsets, int32_t* mt_start, int32_t* tile_group,
+                              hipStream_t s);
 
 // ---- grouped FP8 GEMMs (gemm_fp8.hip)
 struct GemmArgs {
@@ -41,6 +42,7 @@ struct GemmArgs {
   const int32_t* offsets;   // expert_offsets [E+1]
   const int32_t* row_pair;  // [P]
   const int32_t* mt_start;  // [G+1] prefix of m-tiles per group
+  const int32_t* tile_group;  // [mt_start[G]] group of each m-tile
   int E, G, T, k, P, NC;    // NC: 256-row weight chunks per expert
   // gate/up outputs
   uint8_t* aq;              // [P+T, I]

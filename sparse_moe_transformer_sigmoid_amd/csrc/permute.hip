@@ -116,10 +116,13 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(int T, int E, int k, 
 // mt_start[g] = sum over groups before g of ceil(m_g / bm); groups are the
 // routed experts 0..E-1 (m = expert count) and then the shared expert (m = T).
 // Row ranges are clamped into [0, P) exactly as the GEMM kernels clamp them.
+// tile_group[q] = the group of m-tile q, so a GEMM workgroup finds its group
+// with one load (q < mt_start[G] <= max_tiles).
 __global__ __launch_bounds__(1024) void build_tiles_kernel(int E, int n_shared, int T, int P,
-                                                          int bm,
+                                                          int bm, int max_tiles,
                                                           const int32_t* __restrict__ offsets,
-                                                          int32_t* __restrict__ mt_start) {
+                                                          int32_t* __restrict__ mt_start,
+                                                          int32_t* __restrict__ tile_group) {
   const int G = E + n_shared;
   block_exclusive_scan<2>(
       G,
@@ -132,6 +135,12 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(int E, int n_shared, 
         return (m + bm - 1) / bm;
       },
       mt_start);
+  __syncthreads();
+  if (tile_group == nullptr) return;
+  for (int g = threadIdx.x; g < G; g += 1024) {
+    const int q1 = min(mt_start[g + 1], max_tiles);
+    for (int q = mt_start[g]; q < q1; ++q) tile_group[q] = g;
+  }
 }
 
 }  // namespace
@@ -161,9 +170,11 @@ hipError_t launch_permute(int T, int E, int k, const int32_t* ids, int32_t* chun
   return hipGetLastError();
 }
 
-hipError_t launch_build_tiles(int E, int n_shared, int T, int k, int bm, const int32_t* offsets,
-                              int32_t* mt_start, hipStream_t s) {
-  build_tiles_kernel<<<1, 1024, 0, s>>>(E, n_shared, T, T * k, bm, offsets, mt_start);
+hipError_t launch_build_tiles(int E, int n_shared, int T, int k, int bm, int max_tiles,
+                              const int32_t* offsets, int32_t* mt_start, int32_t* tile_group,
+                              hipStream_t s) {
+  build_tiles_kernel<<<1, 1024, 0, s>>>(E, n_shared, T, T * k, bm, max_tiles, offsets, mt_start,
+                                        tile_group);
   return hipGetLastError();
 }
 
