@@ -279,6 +279,18 @@ def test_k2_skewed(k2):
     check_layer(inp, g, tokens=toks)
 
 
+@pytest.mark.parametrize("T", [1, 5, 257, 1000, 2000, 5000])
+def test_k2_ragged_token_counts(k2, T):
+    """K2 dimensions at token counts that select every m-tile width (16, 32,
+    64 and 128 rows) and leave ragged last tiles in most experts."""
+    base, layer = k2
+    inp = synth.with_workload(base, synth.K2_DECODE, seed=100 + T, tokens=T)
+    g = gpu_chain(layer, inp)
+    counts = np.diff(g["offsets"])
+    _log(f"T={T}: mean rows per routed expert {T * 8 / 384:.1f}, max {counts.max()}")
+    check_layer(inp, g, tokens=_sample(T, 3, seed=T))
+
+
 def test_k2_decode_graph_replay(k2):
     """moe_forward captured in a HIP graph: every replay equals the eager call,
     with eager work on other inputs and synchronisations between replays."""
