@@ -33,7 +33,8 @@ FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA
 # the factor a 1 GiB copy probe gives) + WRITE_SIZE (x1.000), see
 # profiles/gemm_gateup_k2_decode.md; valid only for the GEMM sources whose combined
 # sha256 starts with the recorded prefix (null otherwise).
-MEASURED_TRAFFIC = {"k2_decode": ("5b152551a76d0812", 7.928e9)}
+MEASURED_TRAFFIC = {"k2_decode": ("9f3044eabec2249e", 7.921e9),
+                    "k2_prefill": ("9f3044eabec2249e", 14.066e9)}
 GEMM_SRCS = [os.path.join(ROOT, "sparse_moe_transformer_sigmoid_amd", "csrc", f)
              for f in ("gemm_fp8_kernel.h", "gemm_fp8.hip")]
 
@@ -255,7 +256,8 @@ def main():
             "frac_fp8_peak_layer": rp["total_flops"] / (rp["ms"] * 1e-3) / 1e12 / FP8_PEAK_TFLOPS,
             "gateup_tflops": rp["gu_tflops"], "gateup_frac_fp8_peak":
                 rp["gu_tflops"] / FP8_PEAK_TFLOPS,
-            "gateup_gbs": rp["gu_gbs"], "stage_ms": rp["stage"]}
+            "gateup_gbs": rp["gu_gbs"], "gateup_traffic": measured_traffic(pre.shape.name),
+            "stage_ms": rp["stage"]}
         del pre
     if args.copy_probe:
         n = args.copy_probe // 4
