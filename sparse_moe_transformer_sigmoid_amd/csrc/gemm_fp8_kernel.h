@@ -83,8 +83,15 @@ __device__ __forceinline__ WorkItem decode_work(const GemmArgs& g, int BM) {
   // (at most BM rows each), so the last tile of a group is not mostly padding
   const int mtiles = (m_g + BM - 1) / BM;
   const int rr = L - g.mt_start[lo] * g.NC;
-  w.nc = rr / mtiles;
-  const int mt = rr - w.nc * mtiles;
+  // order inside a group: blocks of up to SUPER m-tiles; within a block,
+  // weight chunks outer and m-tiles inner, so a run of consecutive work items
+  // (one XCD's L2) shares both the weight chunks and the activation tiles
+  constexpr int SUPER = 8;
+  const int blk = rr / (g.NC * SUPER);
+  const int sm = min(SUPER, mtiles - blk * SUPER);        // m-tiles in this block
+  const int r2 = rr - blk * g.NC * SUPER;
+  w.nc = r2 / sm;
+  const int mt = blk * SUPER + (r2 - w.nc * sm);
   const int r_lo = (int)(((int64_t)mt * m_g) / mtiles);
   const int r_hi = (int)(((int64_t)(mt + 1) * m_g) / mtiles);
   w.row0 = row0_g + r_lo;
