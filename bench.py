@@ -33,8 +33,8 @@ FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA
 # the factor a 1 GiB copy probe gives) + WRITE_SIZE (x1.000), see
 # profiles/gemm_gateup_k2_decode.md; valid only for the GEMM sources whose combined
 # sha256 starts with the recorded prefix (null otherwise).
-MEASURED_TRAFFIC = {"k2_decode": ("9f3044eabec2249e", 7.921e9),
-                    "k2_prefill": ("9f3044eabec2249e", 14.066e9)}
+MEASURED_TRAFFIC = {"k2_decode": ("1bf6fcda2a063bef", 7.921e9),
+                    "k2_prefill": ("1bf6fcda2a063bef", 13.501e9)}
 GEMM_SRCS = [os.path.join(ROOT, "sparse_moe_transformer_sigmoid_amd", "csrc", f)
              for f in ("gemm_fp8_kernel.h", "gemm_fp8.hip")]
 
