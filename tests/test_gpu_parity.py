@@ -185,6 +185,18 @@ def test_small_fp8_layer(T, d, E, S, k, I, seed):
     check_layer(inp, g)
 
 
+@pytest.mark.parametrize("T,d,I,seed", [(9, 16384, 256, 11), (3, 256, 65536, 12)])
+def test_small_fp8_largest_k(T, d, I, seed):
+    """The largest supported contraction lengths: d_model 16384 (gate/up K
+    = 128 blocks) and d_ff 65536 (down K = 512 blocks, the scale table's
+    capacity)."""
+    _log(f"largest K: T={T} d={d} I={I}")
+    shape = synth.small_fp8(tokens=T, d_model=d, n_experts=16, n_shared=0, top_k=1, d_ff=I)
+    inp = synth.generate(shape, seed=seed, device="cuda")
+    g = gpu_chain(_layer(inp), inp)
+    check_layer(inp, g)
+
+
 def test_small_fp8_one_hot_expert_spans_many_tiles():
     # a large bias forces every token onto experts 3 and 11: m = T rows each,
     # several m-tiles per expert and most experts empty
