@@ -241,11 +241,18 @@ def main():
                      "kernel_ms": gu_ms, "algorithmic_bytes": res["gu_bytes"]},
         "stage_ms": res["stage"],
     }
-    if args.workload in ("prefill", "skewed", "dense"):
+    # the kernel's bound follows its arithmetic intensity: below the ridge point
+    # (peak flops / peak bandwidth) HBM bounds it, above it the FP8 MFMA peak
+    ai = res["gu_flops"] / res["gu_bytes"]
+    attainable_tflops = min(FP8_PEAK_TFLOPS, ai * HBM_PEAK_GBS / 1e3)
+    line["roofline"].update({"arithmetic_intensity": ai, "algorithmic_flops": res["gu_flops"],
+                             "fp8_tflops": res["gu_tflops"],
+                             "frac_fp8_peak": res["gu_tflops"] / FP8_PEAK_TFLOPS,
+                             "frac_attainable": res["gu_tflops"] / attainable_tflops})
+    if ai > FP8_PEAK_TFLOPS * 1e3 / HBM_PEAK_GBS:
         line["roofline"].update({"bound": "mfma", "achieved": res["gu_tflops"],
                                  "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-                                 "frac": res["gu_tflops"] / FP8_PEAK_TFLOPS,
-                                 "algorithmic_flops": res["gu_flops"]})
+                                 "frac": res["gu_tflops"] / FP8_PEAK_TFLOPS})
     if args.workload == "decode" and not args.no_secondary:
         pre = synth.with_workload(base, synth.K2_PREFILL, seed=0)
         rp = run_workload(layer, pre, max(3, args.steps // 2), 2)
@@ -256,7 +263,9 @@ def main():
             "frac_fp8_peak_layer": rp["total_flops"] / (rp["ms"] * 1e-3) / 1e12 / FP8_PEAK_TFLOPS,
             "gateup_tflops": rp["gu_tflops"], "gateup_frac_fp8_peak":
                 rp["gu_tflops"] / FP8_PEAK_TFLOPS,
-            "gateup_gbs": rp["gu_gbs"], "gateup_traffic": measured_traffic(pre.shape.name),
+            "gateup_gbs": rp["gu_gbs"], "gateup_frac_hbm_peak": rp["gu_gbs"] / HBM_PEAK_GBS,
+            "gateup_arithmetic_intensity": rp["gu_flops"] / rp["gu_bytes"],
+            "gateup_traffic": measured_traffic(pre.shape.name),
             "stage_ms": rp["stage"]}
         del pre
     if args.copy_probe:
