@@ -69,7 +69,7 @@ K2_PREFILL = replace(K2_PREFILL, name="k2_prefill")
 # 16384 tokens with a correction bias that gives Zipf-like (s = 1.1) expert
 # popularity.  beta is fitted by oracle/fit_zipf_beta.py and frozen here.
 K2_SKEWED = replace(K2_DECODE, name="k2_skewed", tokens=16384, bias_recipe="zipf",
-                    zipf_beta=0.0445)
+                    zipf_beta=0.0434)
 
 # The first block's dense SwiGLU (7168 -> 18432 -> 7168) run as one expert.
 K2_DENSE = MoEShape("k2_dense", tokens=4096, d_model=7168, n_experts=1, n_shared=0,

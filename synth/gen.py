@@ -106,6 +106,18 @@ def bias_vector(shape: MoEShape, seed: int, device) -> torch.Tensor:
     raise ValueError(shape.bias_recipe)
 
 
+def generate_router_inputs(shape: MoEShape, seed: int = 0, device="cpu",
+                           tokens: Optional[int] = None):
+    """(x, norm_w, w_router) exactly as generate() draws them, without experts."""
+    T = shape.tokens if tokens is None else tokens
+    act_dtype = torch.bfloat16 if shape.fmt == FMT_FP8 else torch.float32
+    x = _randn((T, shape.d_model), shape.x_std, device, seed, ROLE_X).to(act_dtype)
+    norm_w = torch.ones(shape.d_model, dtype=act_dtype, device=device)
+    w_router = _randn((shape.n_experts, shape.d_model), shape.weight_std, device, seed,
+                      ROLE_ROUTER).to(act_dtype)
+    return x, norm_w, w_router
+
+
 def generate(shape: MoEShape, seed: int = 0, device="cpu", tokens: Optional[int] = None) -> MoEInputs:
     """Seeded inputs for ``shape`` (optionally with a different token count)."""
     T = shape.tokens if tokens is None else tokens

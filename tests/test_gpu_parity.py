@@ -303,6 +303,28 @@ def test_k2_ragged_token_counts(k2, T):
     check_layer(inp, g, tokens=_sample(T, 3, seed=T))
 
 
+@pytest.mark.parametrize("workload", ["decode", "prefill"])
+def test_k2_repeats_with_poisoned_buffers(k2, workload):
+    """Ten forwards with the workspace and the output filled with 0xFF bytes
+    (NaN in every float view, -1 in every index view) before each call are
+    bitwise equal to a clean run: nothing is read before it is written."""
+    from sparse_moe_transformer_sigmoid_amd import _lib as L
+    base, layer = k2
+    inp = base if workload == "decode" else synth.with_workload(base, synth.K2_PREFILL, seed=0)
+    layer.use_router(inp)
+    x = inp.x
+    ref = layer.forward(x).clone()
+    ws = layer.workspace(x.shape[0], L.MOE_WS_FORWARD)
+    out = torch.empty_like(ref)
+    for r in range(10):
+        ws.fill_(0xFF)
+        out.view(torch.int16).fill_(-1)
+        layer.forward(x, out)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"run {r}"
+    _log(f"{workload}: 10 poisoned runs bitwise equal")
+
+
 def test_k2_decode_graph_replay(k2):
     """moe_forward captured in a HIP graph: every replay equals the eager call,
     with eager work on other inputs and synchronisations between replays."""
