@@ -173,6 +173,10 @@ SMALL = [
     (200, 256, 16, 1, 2, 128, 3),
     (300, 256, 16, 1, 3, 256, 4),
     (700, 512, 16, 1, 2, 384, 5),
+    # more than 96 rows per expert (several 128-row tiles per group): an odd number of
+    # down K blocks (d_ff 384), a one-block down K (d_ff 128)
+    (900, 256, 16, 1, 2, 384, 6),
+    (2000, 256, 16, 0, 1, 128, 9),
 ]
 
 
@@ -197,15 +201,18 @@ def test_small_fp8_largest_k(T, d, I, seed):
     check_layer(inp, g)
 
 
-def test_small_fp8_one_hot_expert_spans_many_tiles():
+@pytest.mark.parametrize("T", [333, 800])
+def test_small_fp8_one_hot_expert_spans_many_tiles(T):
     # a large bias forces every token onto experts 3 and 11: m = T rows each,
-    # several m-tiles per expert and most experts empty
-    shape = synth.small_fp8(tokens=333, n_experts=16, top_k=2, d_ff=256)
+    # several m-tiles per expert and the other experts empty (64- and 128-row
+    # tiles)
+    i, j = 3, 11
+    shape = synth.small_fp8(tokens=T, n_experts=16, top_k=2, d_ff=256)
     inp = synth.generate(shape, seed=7, device="cuda")
-    inp.bias[3] = 5.0
-    inp.bias[11] = 5.0
+    inp.bias[i] = 5.0
+    inp.bias[j] = 5.0
     g = gpu_chain(_layer(inp), inp)
-    assert np.all(g["ids"] == np.array([3, 11]))
+    assert np.all(g["ids"] == np.array([i, j]))
     check_layer(inp, g)
 
 
@@ -291,7 +298,7 @@ def test_k2_skewed(k2):
     check_layer(inp, g, tokens=toks)
 
 
-@pytest.mark.parametrize("T", [1, 5, 257, 1000, 2000, 5000])
+@pytest.mark.parametrize("T", [1, 5, 257, 1000, 2000, 3000, 5000])
 def test_k2_ragged_token_counts(k2, T):
     """K2 dimensions at token counts that select every m-tile width (16, 32,
     64 and 128 rows) and leave ragged last tiles in most experts."""
