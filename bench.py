@@ -12,7 +12,8 @@ Prints one JSON line: tokens/s for the named workload (default: the 64-token
 decode step, its timed steps replayed from a HIP graph of moe_forward; --eager
 times plain launches), the dominant kernel's roofline fraction measured with
 HIP events inside an eager timed region, the same for the 8192-token prefill,
-and the CPU oracle timed on a bounded sample of the same workload.
+the shader clock rocm-smi reports while each runs (sampled after the timed
+steps), and the CPU oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -62,6 +63,8 @@ def parse():
     ap.add_argument("--eager", action="store_true",
                     help="time decode with eager launches instead of a HIP graph")
     ap.add_argument("--cpu-tokens", type=int, default=16)
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the shader-clock sample (rocm-smi) after the timed steps")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="also run a plain fp32 copy of BYTES (counter calibration)")
     return ap.parse_args()
@@ -151,6 +154,48 @@ def run_workload(layer, inp, steps, warmup, graph=False):
                 gu_bytes=gu_bytes, gu_flops=gu_flops, total_flops=gu_flops + dn_flops,
                 gu_gbs=gu_bytes / gu_s / 1e9 if gu_s > 0 else 0.0,
                 gu_tflops=gu_flops / gu_s / 1e12 if gu_s > 0 else 0.0)
+
+
+def sclk_during(layer, x, seconds=1.5):
+    """Median shader clock (MHz) read by rocm-smi while the step runs back to
+    back, outside the timed region; None if rocm-smi is absent.  The FP8 and
+    bf16 peaks assume 2.4 GHz, which sustained MFMA work does not hold."""
+    import re
+    import shutil
+    import statistics
+    import subprocess
+    import threading
+
+    import torch
+    exe = shutil.which("rocm-smi")
+    if exe is None:
+        return None
+    vals, stop = [], threading.Event()
+
+    def sample():
+        while not stop.is_set():
+            try:
+                r = subprocess.run([exe, "--showclocks"], capture_output=True, text=True,
+                                   timeout=20)
+            except (OSError, subprocess.SubprocessError):
+                return
+            m = re.search(r"sclk clock level: \d+: \((\d+)Mhz\)", r.stdout)
+            if m:
+                vals.append(int(m.group(1)))
+            stop.wait(0.2)
+
+    th = threading.Thread(target=sample, daemon=True)
+    t0 = time.time()
+    th.start()
+    while time.time() - t0 < seconds or (th.is_alive() and len(vals) < 3 and
+                                         time.time() - t0 < 4 * seconds):
+        for _ in range(10):
+            layer.forward(x)
+        torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    vals = vals[1:] if len(vals) > 1 else vals     # the first may precede the load
+    return int(statistics.median(vals)) if vals else None
 
 
 def cpu_baseline(inp, n_tokens):
@@ -256,6 +301,7 @@ def main():
     if args.workload == "decode" and not args.no_secondary:
         pre = synth.with_workload(base, synth.K2_PREFILL, seed=0)
         rp = run_workload(layer, pre, max(3, args.steps // 2), 2)
+        pre_sclk = None if args.no_clock else sclk_during(layer, pre.x)
         line["prefill"] = {
             "tokens": rp["T"], "value": rp["T"] / (rp["ms"] * 1e-3), "unit": "tokens/s",
             "ms_per_step": rp["ms"],
@@ -266,8 +312,15 @@ def main():
             "gateup_gbs": rp["gu_gbs"], "gateup_frac_hbm_peak": rp["gu_gbs"] / HBM_PEAK_GBS,
             "gateup_arithmetic_intensity": rp["gu_flops"] / rp["gu_bytes"],
             "gateup_traffic": measured_traffic(pre.shape.name),
+            "sclk_mhz": pre_sclk,
+            # the published FP8 peak assumes 2400 MHz; at the measured clock:
+            "gateup_frac_fp8_peak_at_sclk":
+                rp["gu_tflops"] / (FP8_PEAK_TFLOPS * pre_sclk / 2400.0) if pre_sclk else None,
             "stage_ms": rp["stage"]}
         del pre
+    if not args.no_clock:
+        layer.use_router(inp)
+        line["sclk_mhz"] = sclk_during(layer, inp.x)
     if args.copy_probe:
         n = args.copy_probe // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda")
