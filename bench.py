@@ -1,6 +1,7 @@
 """Benchmark of the Kimi K2 MoE feed-forward layer on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload decode|prefill|skewed|dense]
+    python bench.py [--steps K] [--warmup W]
+                    [--workload decode|prefill|skewed|dense|ep8_shard]
 
 One step = one moe_forward over one batch: RMSNorm + activation
 quantisation, router, top-k, permutation, grouped gate/up GEMM + SwiGLU +
@@ -57,7 +58,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "prefill", "skewed", "dense"])
+                    choices=["decode", "prefill", "skewed", "dense", "ep8_shard"])
     ap.add_argument("--no-secondary", action="store_true", help="skip the prefill line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true",
@@ -73,7 +74,8 @@ def parse():
 def shapes():
     import synth
     return {"decode": synth.K2_DECODE, "prefill": synth.K2_PREFILL,
-            "skewed": synth.K2_SKEWED, "dense": synth.K2_DENSE}
+            "skewed": synth.K2_SKEWED, "dense": synth.K2_DENSE,
+            "ep8_shard": synth.K2_EP8_SHARD}
 
 
 def timed(layer, x, steps, warmup):
@@ -252,7 +254,7 @@ def main():
         sys.exit(1)
     shp = shapes()[args.workload]
     t0 = time.time()
-    if args.workload == "dense":
+    if args.workload in ("dense", "ep8_shard"):
         base = synth.generate(shp, seed=0, device="cuda")
         inp = base
     else:

@@ -1,10 +1,11 @@
 """Seeded synthetic workloads for the K2 MoE layer (shapes and input recipe only)."""
-from .configs import (ALL, FMT_F32, FMT_FP8, K2_DECODE, K2_DENSE, K2_PREFILL, K2_SKEWED,
-                      TINY, MoEShape, small_fp8)
+from .configs import (ALL, FMT_F32, FMT_FP8, K2_DECODE, K2_DENSE, K2_EP8_SHARD, K2_PREFILL,
+                      K2_SKEWED, TINY, MoEShape, small_fp8)
 from .gen import (MoEInputs, bias_vector, block_quantize_weight, generate,
                   generate_router_inputs, with_workload)
 
-__all__ = ["ALL", "FMT_F32", "FMT_FP8", "K2_DECODE", "K2_DENSE", "K2_PREFILL", "K2_SKEWED",
+__all__ = ["ALL", "FMT_F32", "FMT_FP8", "K2_DECODE", "K2_DENSE", "K2_EP8_SHARD", "K2_PREFILL",
+           "K2_SKEWED",
            "TINY", "MoEShape", "small_fp8", "MoEInputs", "block_quantize_weight", "generate",
            "generate_router_inputs", "bias_vector",
            "with_workload"]

@@ -75,7 +75,14 @@ K2_SKEWED = replace(K2_DECODE, name="k2_skewed", tokens=16384, bias_recipe="zipf
 K2_DENSE = MoEShape("k2_dense", tokens=4096, d_model=7168, n_experts=1, n_shared=0,
                     top_k=1, d_ff=18432, fmt=FMT_FP8, routed_scaling=1.0, dense=True)
 
-ALL = {s.name: s for s in (TINY, K2_DECODE, K2_PREFILL, K2_SKEWED, K2_DENSE)}
+# One GPU's share of the layer under 8-way expert parallelism: 48 of the 384
+# routed experts per GPU, and 8192 tokens on each of 8 GPUs send on average
+# 8 * 8192 * 8 / 384 = 1365 rows to each local expert.  Modelled as a
+# 48-expert layer with 8192 tokens and top-8, so the grouped GEMMs see the
+# same rows per expert (the shared expert runs over the GPU's own 8192 tokens).
+K2_EP8_SHARD = replace(K2_DECODE, name="k2_ep8_shard", tokens=8192, n_experts=48)
+
+ALL = {s.name: s for s in (TINY, K2_DECODE, K2_PREFILL, K2_SKEWED, K2_DENSE, K2_EP8_SHARD)}
 
 
 def small_fp8(tokens=48, d_model=256, n_experts=8, n_shared=1, top_k=2, d_ff=256,

@@ -353,6 +353,18 @@ def test_k2_decode_graph_replay(k2):
     del g
 
 
+def test_k2_ep8_shard():
+    """One GPU's share under 8-way expert parallelism: 48 experts with about
+    1365 rows each (eleven 128-row tiles per expert)."""
+    inp = synth.generate(synth.K2_EP8_SHARD, seed=0, device="cuda")
+    layer = _layer(inp)
+    g = gpu_chain(layer, inp)
+    counts = np.diff(g["offsets"])
+    _log(f"ep8 shard: rows per expert min {counts.min()} max {counts.max()}")
+    check_layer(inp, g, tokens=_sample(8192, 3, seed=4))
+    del layer
+
+
 def test_k2_dense_ffn():
     inp = synth.generate(synth.K2_DENSE, seed=0, device="cuda")
     layer = _layer(inp)
