@@ -13,8 +13,8 @@ Prints one JSON line: tokens/s for the named workload (default: the 64-token
 decode step, its timed steps replayed from a HIP graph of moe_forward; --eager
 times plain launches), the dominant kernel's roofline fraction measured with
 HIP events inside an eager timed region, the same for the 8192-token prefill,
-the shader clock rocm-smi reports while each runs (sampled after the timed
-steps), and the CPU oracle timed on a bounded sample of the same workload.
+the shader clock the driver reports while each runs (sampled from sysfs
+after the timed steps), and the CPU oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -35,8 +35,8 @@ FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA
 # the factor a 1 GiB copy probe gives) + WRITE_SIZE (x1.000), see
 # profiles/gemm_gateup_k2_decode.md; valid only for the GEMM sources whose combined
 # sha256 starts with the recorded prefix (null otherwise).
-MEASURED_TRAFFIC = {"k2_decode": ("1bf6fcda2a063bef", 7.921e9),
-                    "k2_prefill": ("1bf6fcda2a063bef", 13.501e9)}
+MEASURED_TRAFFIC = {"k2_decode": ("c77f5287356c6c6f", 7.919e9),
+                    "k2_prefill": ("c77f5287356c6c6f", 13.777e9)}
 GEMM_SRCS = [os.path.join(ROOT, "sparse_moe_transformer_sigmoid_amd", "csrc", f)
              for f in ("gemm_fp8_kernel.h", "gemm_fp8.hip")]
 
@@ -65,7 +65,7 @@ def parse():
                     help="time decode with eager launches instead of a HIP graph")
     ap.add_argument("--cpu-tokens", type=int, default=16)
     ap.add_argument("--no-clock", action="store_true",
-                    help="skip the shader-clock sample (rocm-smi) after the timed steps")
+                    help="skip the shader-clock sample (sysfs) after the timed steps")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="also run a plain fp32 copy of BYTES (counter calibration)")
     return ap.parse_args()
@@ -158,45 +158,54 @@ def run_workload(layer, inp, steps, warmup, graph=False):
                 gu_tflops=gu_flops / gu_s / 1e12 if gu_s > 0 else 0.0)
 
 
+def sclk_file():
+    """The amdgpu driver's shader-clock table of the GPU torch uses (sysfs
+    pp_dpm_sclk, found by the device's PCI address), or None."""
+    import torch
+    p = torch.cuda.get_device_properties(torch.cuda.current_device())
+    path = (f"/sys/bus/pci/devices/{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:"
+            f"{p.pci_device_id:02x}.0/pp_dpm_sclk")
+    return path if os.path.exists(path) else None
+
+
 def sclk_during(layer, x, seconds=1.5):
-    """Median shader clock (MHz) read by rocm-smi while the step runs back to
-    back, outside the timed region; None if rocm-smi is absent.  The FP8 and
-    bf16 peaks assume 2.4 GHz, which sustained MFMA work does not hold."""
+    """Median shader clock (MHz) while the step runs back to back, outside the
+    timed region: the level the driver marks current in pp_dpm_sclk, read
+    from sysfs every 50 ms (no child process).  None if the file is absent.
+    The FP8 and bf16 peaks assume 2.4 GHz, which sustained MFMA work does
+    not hold."""
     import re
-    import shutil
     import statistics
-    import subprocess
     import threading
 
     import torch
-    exe = shutil.which("rocm-smi")
-    if exe is None:
+    path = sclk_file()
+    if path is None:
         return None
     vals, stop = [], threading.Event()
 
     def sample():
         while not stop.is_set():
             try:
-                r = subprocess.run([exe, "--showclocks"], capture_output=True, text=True,
-                                   timeout=20)
-            except (OSError, subprocess.SubprocessError):
+                with open(path) as f:
+                    for line in f:
+                        m = re.search(r"(\d+)\s*Mhz\s*\*", line, re.IGNORECASE)
+                        if m:
+                            vals.append(int(m.group(1)))
+            except OSError:
                 return
-            m = re.search(r"sclk clock level: \d+: \((\d+)Mhz\)", r.stdout)
-            if m:
-                vals.append(int(m.group(1)))
-            stop.wait(0.2)
+            stop.wait(0.05)
 
     th = threading.Thread(target=sample, daemon=True)
     t0 = time.time()
     th.start()
-    while time.time() - t0 < seconds or (th.is_alive() and len(vals) < 3 and
-                                         time.time() - t0 < 4 * seconds):
+    while time.time() - t0 < seconds:
         for _ in range(10):
             layer.forward(x)
         torch.cuda.synchronize()
     stop.set()
     th.join()
-    vals = vals[1:] if len(vals) > 1 else vals     # the first may precede the load
+    vals = vals[2:] if len(vals) > 4 else vals     # the first may precede the load
     return int(statistics.median(vals)) if vals else None
 
 

@@ -23,7 +23,7 @@ hipError_t launch_tt(int tt, const GemmArgs& a, int grid, hipStream_t s) {
       if constexpr (GATEUP) {
         return launch_gateup_tt8(a, grid, s);
       } else {
-        gemm_fp8_kernel<GATEUP, 8, 2, false, 1, 2><<<grid, 256, 0, s>>>(a);
+        gemm_fp8_kernel<GATEUP, 8, 2, false, 1, 2, 0, 1><<<grid, 256, 0, s>>>(a);
       }
       break;
     default: return hipErrorInvalidValue;

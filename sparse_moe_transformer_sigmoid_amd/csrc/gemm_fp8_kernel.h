@@ -49,6 +49,22 @@ __device__ __forceinline__ v4f mfma_fp8(v8i a, v8i b) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 127, 0, 127);
 }
 
+// Direct global -> LDS loads (global_load_lds_dword / _dwordx4): lane l's
+// 4 or 16 bytes from global [base + voff] land at LDS byte address
+// M0 + l * size.  Completion is tracked by vmcnt like any vector load, in
+// issue order; the compiler knows nothing of them (see BMODE).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+__device__ __forceinline__ void lds_load16(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               : : "v"(voff), "s"(base), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_load4(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+               : : "v"(voff), "s"(base), "s"(lds) : "memory", "m0");
+}
+
 struct WorkItem {
   bool valid;
   bool shared_grp;
@@ -197,7 +213,8 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, v4f (&acc)[4][TT], f
 // BSETS: activation register sets (2: loaded two K blocks ahead; 1: one block
 // ahead, saving registers); MINW: waves per SIMD the register budget must allow.
 // GRPX: token tiles per scheduling group (0: the default for TT and MINW).
-template <bool GATEUP, int TT, int NBUF, bool NT, int BSETS = 2, int MINW = 1, int GRPX = 0>
+template <bool GATEUP, int TT, int NBUF, bool NT, int BSETS = 2, int MINW = 1, int GRPX = 0,
+          int BMODE = 0>
 __global__ __launch_bounds__(256, MINW) void gemm_fp8_kernel(const GemmArgs g) {
   static_assert(NBUF >= 2 && NBUF <= 4, "NBUF must be 2, 3 or 4");
   static_assert(BSETS == 1 || BSETS == 2, "BSETS must be 1 or 2");
@@ -207,8 +224,12 @@ __global__ __launch_bounds__(256, MINW) void gemm_fp8_kernel(const GemmArgs g) {
   // stages its chunk unconditionally, keeping the K loop free of branches
   constexpr int LDS_B = (TT * 2048 > 256 * 16 * ((TT * 128 + 255) / 256)) ? TT * 2048
                                                                           : 256 * 16 * ((TT * 128 + 255) / 256);
-  __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][LDS_B];
-  __shared__ float lds_sa[2][256];
+  // LDS double buffers as separate objects, so that the compiler can tell a
+  // read of one buffer from a direct load into the other
+  __shared__ __attribute__((aligned(16))) uint8_t lds_b0[LDS_B], lds_b1[LDS_B];
+  __shared__ float lds_sa0[256], lds_sa1[256];
+  auto lds_b = [&](int buf) -> uint8_t* { return buf ? lds_b1 : lds_b0; };
+  auto lds_sa = [&](int buf) -> float* { return buf ? lds_sa1 : lds_sa0; };
   // this chunk's weight scales for every K block, loaded once: scalar loads in
   // the loop would share lgkmcnt with the LDS reads and stall each step on
   // a memory round trip
@@ -278,11 +299,23 @@ __global__ __launch_bounds__(256, MINW) void gemm_fp8_kernel(const GemmArgs g) {
       breg[set][i] = *reinterpret_cast<const v4i*>(g.act + boff[i] + kb * 128);
     sareg[set] = g.act_s[saoff + kb];
   };
+  // BMODE 1: activation tiles go straight from global memory into LDS
+  // (global_load_lds, no staging registers).  They are issued from inline
+  // assembly: the compiler inserts no waits for them (its own tracking of
+  // such loads waits for every outstanding load, the weight prefetch
+  // included), and the step that issues them ends with an explicit wait and
+  // barrier.  Byte offsets are 32-bit: rows * act_ld < 2^32.
+  auto dma_b = [&](int buf, int kb) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i)
+      lds_load16(g.act, boff[i] + kb * 128, lds_addr(&lds_b(buf)[(256 * i + 64 * wave) * 16]));
+    lds_load4(g.act_s, (saoff + kb) * 4, lds_addr(&lds_sa(buf)[64 * wave]));
+  };
   auto store_b = [&](int set, int buf) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i)
-      *reinterpret_cast<v4i*>(&lds_b[buf][(tid + 256 * i) * 16]) = breg[set][i];
-    lds_sa[buf][tid] = sareg[set];
+      *reinterpret_cast<v4i*>(&lds_b(buf)[(tid + 256 * i) * 16]) = breg[set][i];
+    lds_sa(buf)[tid] = sareg[set];
   };
   auto weight_scales = [&](int kb, float& s_gate_or_down, float& s_up) {
     if constexpr (GATEUP) {
@@ -300,7 +333,44 @@ __global__ __launch_bounds__(256, MINW) void gemm_fp8_kernel(const GemmArgs g) {
   // every B fragment at once (register pressure at large TT; one tile per
   // group when the register budget is sized for 2 waves/SIMD).
   constexpr int GRP = GRPX ? GRPX : (TT < 4 ? TT : (MINW > 1 ? 1 : 4));
+  // BMODE 1: one token tile at a time, the next tile's B fragment and scale
+  // read from LDS before the current tile's MFMAs (its latency hides behind
+  // them), promotion FMAs one MFMA behind
+  auto compute_la = [&](const v8i (&w)[4], int buf, int kb) {
+    float swg, swu;
+    weight_scales(kb, swg, swu);
+    auto read_b = [&](int t, v8i& b, float& sa) {
+      const uint8_t* bp = &lds_b(buf)[t * 2048 + lane * 16];
+      b = join8(*reinterpret_cast<const v4i*>(bp), *reinterpret_cast<const v4i*>(bp + 1024));
+      sa = lds_sa(buf)[t * 16 + (lane & 15)];
+    };
+    v8i bc;
+    float sac;
+    read_b(0, bc, sac);
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+      v8i bn = bc;
+      float san = sac;
+      if (t + 1 < TT) read_b(t + 1, bn, san);
+      const float s0 = sac * swg, s1 = sac * swu;
+      v4f prev = mfma_fp8(w[0], bc);
+#pragma unroll
+      for (int rt = 1; rt < 4; ++rt) {
+        const v4f cur = mfma_fp8(w[rt], bc);
+        acc[rt - 1][t] += prev * (rt - 1 < 2 ? s0 : s1);
+        prev = cur;
+      }
+      acc[3][t] += prev * s1;
+      bc = bn;
+      sac = san;
+      if (t + 1 < TT) __builtin_amdgcn_sched_barrier(0);
+    }
+  };
   auto compute = [&](const v8i (&w)[4], int buf, int kb) {
+    if constexpr (BMODE == 1) {
+      compute_la(w, buf, kb);
+      return;
+    }
     float swg, swu;
     weight_scales(kb, swg, swu);
 #pragma unroll
@@ -309,9 +379,9 @@ __global__ __launch_bounds__(256, MINW) void gemm_fp8_kernel(const GemmArgs g) {
       float s0[GRP], s1[GRP];
 #pragma unroll
       for (int u = 0; u < GRP; ++u) {
-        const uint8_t* bp = &lds_b[buf][(t0 + u) * 2048 + lane * 16];
+        const uint8_t* bp = &lds_b(buf)[(t0 + u) * 2048 + lane * 16];
         bf[u] = join8(*reinterpret_cast<const v4i*>(bp), *reinterpret_cast<const v4i*>(bp + 1024));
-        const float sa_t = lds_sa[buf][(t0 + u) * 16 + (lane & 15)];
+        const float sa_t = lds_sa(buf)[(t0 + u) * 16 + (lane & 15)];
         s0[u] = sa_t * swg;
         s1[u] = sa_t * swu;
       }
@@ -336,12 +406,17 @@ __global__ __launch_bounds__(256, MINW) void gemm_fp8_kernel(const GemmArgs g) {
   // before the weights of block kb+NBUF-1, and ends by waiting only for the
   // activations of block kb+1 (issued one step earlier).
   const int nkb = g.nkb;
-  load_b(0, 0);
-  if (BSETS == 2 && nkb > 1) load_b(BSETS - 1, 1);
+  if constexpr (BMODE == 1) {
+    dma_b(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" : : : "memory");   // block 0, before the barrier below
+  } else {
+    load_b(0, 0);
+    if (BSETS == 2 && nkb > 1) load_b(BSETS - 1, 1);
+  }
 #pragma unroll
   for (int i = 0; i < NBUF - 1; ++i)
     if (i < nkb) load_w(wbuf[i], i);
-  store_b(0, 0);
+  if constexpr (BMODE != 1) store_b(0, 0);
   __syncthreads();
   // One step: prefetch (activations of kb+2, weights of kb+NBUF-1; indices
   // clamped to the last block, so the tail re-reads a block instead of
@@ -351,15 +426,30 @@ __global__ __launch_bounds__(256, MINW) void gemm_fp8_kernel(const GemmArgs g) {
   constexpr int STEP = (NBUF & 1) ? 2 * NBUF : NBUF;
   auto step = [&](const int j, const int kb) {
     const int cur = j & 1;
-    if constexpr (BSETS == 2) load_b(cur, min(kb + 2, nkb - 1));
-    else load_b(0, min(kb + 1, nkb - 1));
+    if constexpr (BMODE == 1) {
+      // LDS buffer cur ^ 1 was last read in the previous step, before its barrier
+      dma_b(cur ^ 1, min(kb + 1, nkb - 1));
+      __builtin_amdgcn_sched_barrier(0);
+    } else if constexpr (BSETS == 2) {
+      load_b(cur, min(kb + 2, nkb - 1));
+    } else {
+      load_b(0, min(kb + 1, nkb - 1));
+    }
     load_w(wbuf[(j + NBUF - 1) % NBUF], min(kb + NBUF - 1, nkb - 1));
     // keep the prefetches issued here: the scheduler would otherwise sink
     // them next to their use to save registers, undoing the ring
     __builtin_amdgcn_sched_barrier(0);
     compute(wbuf[j % NBUF], cur, kb);
-    store_b(BSETS == 2 ? cur ^ 1 : 0, cur ^ 1);
-    __syncthreads();
+    if constexpr (BMODE == 1) {
+      // This wave's direct loads of block kb+1 are older than the 8 weight
+      // loads issued after them, so vmcnt(8) completes them without waiting
+      // for those weights (a barrier with a release fence would wait for
+      // every load); then the barrier publishes block kb+1 to all waves.
+      asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" : : : "memory");
+    } else {
+      store_b(BSETS == 2 ? cur ^ 1 : 0, cur ^ 1);
+      __syncthreads();
+    }
   };
   int kb0 = 0;
   for (; kb0 + STEP <= nkb; kb0 += STEP) {
