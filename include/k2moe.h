@@ -30,7 +30,9 @@
  *  - Arguments are validated on the host before any HIP call; on error
  *    nothing is enqueued and moe_last_error() describes the problem.
  *  - T (tokens) = 0 is valid: tensor pointers are not examined and nothing
- *    is enqueued.
+ *    is enqueued.  The kernels use 32-bit row offsets: T <= 2^24 and
+ *    T * (top_k + 1) * max(d_model, d_ff) < 2^32 (K2: T <= 66,576 per call);
+ *    larger T gives MOE_ERR_UNSUPPORTED.
  *  - Results are bitwise deterministic: no floating-point atomics.
  *
  * Formats (moe_config.fmt):
