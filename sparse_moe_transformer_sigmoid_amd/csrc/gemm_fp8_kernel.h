@@ -213,19 +213,25 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, v4f (&acc)[4][TT], f
 // BSETS: activation register sets (2: loaded two K blocks ahead; 1: one block
 // ahead, saving registers); MINW: waves per SIMD the register budget must allow.
 // GRPX: token tiles per scheduling group (0: the default for TT and MINW).
+// BMODE: activation staging.  0: through BSETS register sets, stored to LDS
+// at the end of each step.  1: loaded straight into LDS (no staging
+// registers) and each token tile's B fragment read one tile ahead.
 template <bool GATEUP, int TT, int NBUF, bool NT, int BSETS = 2, int MINW = 1, int GRPX = 0,
           int BMODE = 0>
 __global__ __launch_bounds__(256, MINW) void gemm_fp8_kernel(const GemmArgs g) {
   static_assert(NBUF >= 2 && NBUF <= 4, "NBUF must be 2, 3 or 4");
   static_assert(BSETS == 1 || BSETS == 2, "BSETS must be 1 or 2");
+  // BMODE 1 ends each step with a wait that counts the 8 weight loads of one
+  // ring slot issued after the step's direct loads (one slot per step)
+  static_assert(BMODE == 0 || (BMODE == 1 && NBUF == 2), "BMODE 1 needs NBUF 2");
   constexpr int BM = 16 * TT;
   constexpr int CPT = (TT * 128 + 255) / 256;   // 16-byte staging chunks per thread
   // LDS rows past the tile (TT < 2) are write-only padding: every thread
   // stages its chunk unconditionally, keeping the K loop free of branches
   constexpr int LDS_B = (TT * 2048 > 256 * 16 * ((TT * 128 + 255) / 256)) ? TT * 2048
                                                                           : 256 * 16 * ((TT * 128 + 255) / 256);
-  // LDS double buffers as separate objects, so that the compiler can tell a
-  // read of one buffer from a direct load into the other
+  // LDS double buffers of the activation tiles and their scales (the buffer
+  // of each step is a compile-time choice in the unrolled K loop)
   __shared__ __attribute__((aligned(16))) uint8_t lds_b0[LDS_B], lds_b1[LDS_B];
   __shared__ float lds_sa0[256], lds_sa1[256];
   auto lds_b = [&](int buf) -> uint8_t* { return buf ? lds_b1 : lds_b0; };
@@ -401,10 +407,11 @@ __global__ __launch_bounds__(256, MINW) void gemm_fp8_kernel(const GemmArgs g) {
 
   // ---------------------------------------------------------------- K loop
   // Block kb: weights in wbuf[kb % NBUF] with scales sw[kb % NBUF]; activations
-  // in LDS buffer kb & 1, staged from register set (kb & 1).  Vector loads
-  // retire in issue order, so each step issues the activations of block kb+2
-  // before the weights of block kb+NBUF-1, and ends by waiting only for the
-  // activations of block kb+1 (issued one step earlier).
+  // in LDS buffer kb & 1, staged from register set (kb & 1) (BMODE 0) or
+  // loaded there directly (BMODE 1).  Vector loads retire in issue order, so
+  // each step issues the activations before the weights of block
+  // kb+NBUF-1, and ends by waiting only for the activations (BMODE 0: those
+  // of block kb+1, issued one step earlier).
   const int nkb = g.nkb;
   if constexpr (BMODE == 1) {
     dma_b(0, 0);
