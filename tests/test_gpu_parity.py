@@ -180,7 +180,26 @@ SMALL = [
 ]
 
 
-@pytest.mark.parametrize("T,d,E,S,k,I,seed", SMALL)
+# Twelve mixed shapes (drawn once from a seeded generator, then frozen): every
+# m-tile width, d_model 256/512/768 (3-block down chunks), 16-64 experts,
+# top-1..8, d_ff 128-512, with and without the shared expert.
+MIXED = [
+    (7, 768, 16, 0, 2, 256, 100),
+    (777, 768, 64, 0, 8, 128, 101),
+    (777, 256, 16, 0, 2, 512, 102),
+    (7, 256, 32, 1, 5, 512, 103),
+    (1500, 256, 32, 0, 5, 384, 104),
+    (3, 512, 16, 1, 8, 384, 105),
+    (64, 512, 32, 0, 3, 128, 106),
+    (250, 512, 64, 1, 3, 384, 107),
+    (511, 256, 32, 1, 3, 512, 108),
+    (33, 256, 16, 0, 3, 128, 109),
+    (511, 512, 64, 1, 3, 256, 110),
+    (129, 256, 32, 0, 7, 256, 111),
+]
+
+
+@pytest.mark.parametrize("T,d,E,S,k,I,seed", SMALL + MIXED)
 def test_small_fp8_layer(T, d, E, S, k, I, seed):
     _log(f"small fp8 T={T} d={d} E={E} S={S} k={k} I={I}")
     shape = synth.small_fp8(tokens=T, d_model=d, n_experts=E, n_shared=S, top_k=k, d_ff=I)
