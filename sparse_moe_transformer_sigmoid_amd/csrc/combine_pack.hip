@@ -11,6 +11,14 @@ namespace k2 {
 
 namespace {
 
+typedef float f4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u2v __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float4 load_nt(const float4* p) {
+  const f4v v = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+
 template <bool XBF16, bool OUTF32>
 __global__ __launch_bounds__(256) void combine_kernel(int T, int d, int k,
                                                      const float* __restrict__ rows,
@@ -21,7 +29,8 @@ __global__ __launch_bounds__(256) void combine_kernel(int T, int d, int k,
                                                      void* __restrict__ out) {
   // one token per blockIdx.x, 1024 columns per blockIdx.y: small batches
   // still spread over the chip, and the k row reads of a thread are issued
-  // together (the sum itself stays in slot order)
+  // together (the sum itself stays in slot order).  Expert rows and the
+  // shared output are read once and the output written once: non-temporal.
   const int t = blockIdx.x;
   const int P = T * k;
   const int d4 = d >> 2;
@@ -32,7 +41,7 @@ __global__ __launch_bounds__(256) void combine_kernel(int T, int d, int k,
     for (int slot = 0; slot < k; ++slot) {
       const int p = t * k + slot;
       const int r = min(max(pair_row[p], 0), P - 1);
-      float4 v = reinterpret_cast<const float4*>(rows + (size_t)r * d)[n4];
+      float4 v = load_nt(reinterpret_cast<const float4*>(rows + (size_t)r * d) + n4);
       if (mul_w) {
         const float w = topk_w[p];
         // rounded products, as the fused path stores them (no fma contraction)
@@ -42,7 +51,7 @@ __global__ __launch_bounds__(256) void combine_kernel(int T, int d, int k,
       acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
     }
     if (shared) {
-      const float4 v = reinterpret_cast<const float4*>(shared + (size_t)t * d)[n4];
+      const float4 v = load_nt(reinterpret_cast<const float4*>(shared + (size_t)t * d) + n4);
       acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
     }
     if (residual) {
@@ -60,12 +69,13 @@ __global__ __launch_bounds__(256) void combine_kernel(int T, int d, int k,
       }
     }
     if constexpr (OUTF32) {
-      reinterpret_cast<float4*>(static_cast<float*>(out) + (size_t)t * d)[n4] = acc;
+      f4v* o = reinterpret_cast<f4v*>(static_cast<float*>(out) + (size_t)t * d) + n4;
+      __builtin_nontemporal_store(f4v{acc.x, acc.y, acc.z, acc.w}, o);
     } else {
       const uint32_t lo = f32_to_bf16_rne(acc.x) | (f32_to_bf16_rne(acc.y) << 16);
       const uint32_t hi = f32_to_bf16_rne(acc.z) | (f32_to_bf16_rne(acc.w) << 16);
-      reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + (size_t)t * d)[n4] =
-          make_uint2(lo, hi);
+      u2v* o = reinterpret_cast<u2v*>(static_cast<uint16_t*>(out) + (size_t)t * d) + n4;
+      __builtin_nontemporal_store(u2v{lo, hi}, o);
     }
   }
 }

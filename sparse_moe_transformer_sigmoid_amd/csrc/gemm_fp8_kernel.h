@@ -132,7 +132,9 @@ __device__ __forceinline__ int act_row_of(const GemmArgs& g, const WorkItem& w, 
 
 // Accumulators -> outputs.  acc[rt][tt] lane l holds weight rows
 // 64 wave + 16 rt + 4 (l / 16) + r of token row 16 tt + l % 16.
-template <bool GATEUP, int TT>
+// NTS: write the down rows with non-temporal stores (the launches that stream
+// each weight chunk once; at larger tiles ordinary stores measure faster).
+template <bool GATEUP, int TT, bool NTS>
 __device__ __forceinline__ void epilogue(const GemmArgs& g, v4f (&acc)[4][TT], float* lds_red,
                                          const WorkItem& wi, int wave, int lane) {
   const int nc = wi.nc, row0 = wi.row0, mcount = wi.mcount, ntt = wi.ntt;
@@ -199,7 +201,10 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, v4f (&acc)[4][TT], f
           for (int rt = 0; rt < 4; ++rt) {
             v4f o = acc[rt][tt];
             if (mul) o = o * wt;
-            *reinterpret_cast<float4*>(dst + 16 * rt) = make_float4(o[0], o[1], o[2], o[3]);
+            if constexpr (NTS)
+              __builtin_nontemporal_store(o, reinterpret_cast<v4f*>(dst + 16 * rt));
+            else
+              *reinterpret_cast<float4*>(dst + 16 * rt) = make_float4(o[0], o[1], o[2], o[3]);
           }
         }
       }
@@ -467,7 +472,7 @@ __global__ __launch_bounds__(256, MINW) void gemm_fp8_kernel(const GemmArgs g) {
   for (int j = 0; j < STEP; ++j)
     if (kb0 + j < nkb) step(j, kb0 + j);
 
-  epilogue<GATEUP, TT>(g, acc, lds_red, wi, wave, lane);
+  epilogue<GATEUP, TT, NT>(g, acc, lds_red, wi, wave, lane);
 }
 
 }  // namespace
