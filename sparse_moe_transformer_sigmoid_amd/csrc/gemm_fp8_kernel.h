@@ -12,7 +12,8 @@
 // workgroup has 4 waves; wave w streams 64 weight rows (four 16x128 MFMA
 // fragments per K block, 8 KiB, contiguous in the packed layout) straight
 // into registers, double-buffered one K block ahead.  The m-tile's activation
-// rows are gathered into LDS in fragment order (double-buffered).  MFMA:
+// rows are gathered into LDS (double-buffered) as whole 128-byte lines, in an
+// XOR-swizzled layout that keeps stores and fragment reads conflict-free.  MFMA:
 // v_mfma_scale_f32_16x16x128_f8f6f4 with unit scales, A = 16 weight rows,
 // B = 16 tokens, so lane l of the 16x16 result holds weight rows
 // 4*(l/16)..+3 of token l%16.
@@ -221,8 +222,11 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, v4f (&acc)[4][TT], f
 // BMODE: activation staging.  0: through BSETS register sets, stored to LDS
 // at the end of each step.  1: loaded straight into LDS (no staging
 // registers) and each token tile's B fragment read one tile ahead.
+// ILV (BMODE 0): if nonzero, the issue order inside a scheduling group is
+// fixed: its LDS reads, two MFMAs, then each further MFMA after ILV VALU
+// instructions (the promotion FMAs of the MFMA two back).
 template <bool GATEUP, int TT, int NBUF, bool NT, int BSETS = 2, int MINW = 1, int GRPX = 0,
-          int BMODE = 0>
+          int BMODE = 0, int ILV = 0>
 __global__ __launch_bounds__(256, MINW) void gemm_fp8_kernel(const GemmArgs g) {
   static_assert(NBUF >= 2 && NBUF <= 4, "NBUF must be 2, 3 or 4");
   static_assert(BSETS == 1 || BSETS == 2, "BSETS must be 1 or 2");
@@ -256,24 +260,37 @@ __global__ __launch_bounds__(256, MINW) void gemm_fp8_kernel(const GemmArgs g) {
 
   auto act_row = [&](int m) { return act_row_of<GATEUP>(g, wi, m); };
 
-  // staging of the activation tile into LDS in fragment order
-  // [tt][half p][lane][16 B]: LDS chunk q = tid + 256 i holds, for
-  // tt = q / 128, p = (q / 64) % 2, lane = q % 64, the 16 bytes of row
-  // 16 tt + lane % 16 at column 32 (lane / 16) + 16 p.  Consecutive lanes
-  // write consecutive 16-byte LDS chunks (no bank conflicts).
+  // Activation tiles in LDS: row j of token tile t at byte 2048 t + 128 j, its 16-byte
+  // chunk c (columns 16c..16c+15) at position c ^ ((j / 2) % 8) of the row.
+  // Thread (wave w, lane l) stages, in instruction i, 16 bytes of tile row
+  // 32 i + 8 w + l / 8 into LDS chunk 256 i + 64 w + l (the destination
+  // that direct-to-LDS loads require: lane l of a wave's instruction lands
+  // at 16 l), which under the swizzle is chunk (l % 8) ^ (4 (w % 2) + l / 16)
+  // of that row.  Every load instruction thus reads 8 whole 128-byte lines.
+  // Stores (8 rows x 8 positions per wave) and fragment reads (16 rows, one
+  // chunk each) both hit 16 distinct positions modulo 256 bytes.
   uint32_t boff[CPT];
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
-    const int q = tid + 256 * i;
-    const int m = (q >> 7) * 16 + (q & 15);   // past the tile for q >= TT*128: clamped row
-    const int col = 32 * ((q & 63) >> 4) + 16 * ((q >> 6) & 1);
-    boff[i] = (uint32_t)act_row(m) * (uint32_t)g.act_ld + col;
+    // tid / 8 = 8 w + l / 8 and (tid / 16) % 8 = 4 (w % 2) + l / 16
+    const int r = 32 * i + (tid >> 3);   // past the tile: clamped row
+    const int c = (tid & 7) ^ ((tid >> 4) & 7);
+    boff[i] = (uint32_t)act_row(r) * (uint32_t)g.act_ld + 16 * c;
   }
+  // byte offsets, within a token tile, of this lane's two 16-byte halves of
+  // its B fragment (token row lane % 16, columns 32 (lane / 16) + 16 p)
+  const int bj = lane & 15, bsw = (bj >> 1) & 7;
+  const uint32_t brd0 = 128u * bj + 16u * ((2 * (lane >> 4)) ^ bsw);
+  const uint32_t brd1 = 128u * bj + 16u * ((2 * (lane >> 4) + 1) ^ bsw);
   // thread tid stages the activation scale of tile row tid (clamped past the tile)
   const uint32_t saoff = (uint32_t)act_row(tid) * g.nkb;
 
+  // wave-uniform base of this wave's weight rows; per-lane 32-bit offsets
+  // (the wave's rows span nkb * 8 KiB <= 4 MiB), so loads take the
+  // scalar-base + vector-offset form and no 64-bit address registers
   const uint8_t* wp = g.wpk + (size_t)grp * g.expert_stride +
-                      (size_t)(nc * 4 + wave) * (size_t)g.nkb * 8192 + lane * 16;
+                      (size_t)(nc * 4 + wave) * (size_t)g.nkb * 8192;
+  const uint32_t wlane = lane * 16;
   const float* swp_base = g.wscale + (size_t)grp * g.wscale_stride + (size_t)nc * g.nkb * 2;
 
   // gate/up: [kb][gate, up] of chunk nc; down: [row block 2nc + h][kb], h = 0, 1
@@ -293,7 +310,7 @@ __global__ __launch_bounds__(256, MINW) void gemm_fp8_kernel(const GemmArgs g) {
   float sareg[2] = {0.f, 0.f};
 
   auto load_w = [&](v8i (&w)[4], int kb) {
-    const uint8_t* p = wp + (size_t)kb * 8192;
+    const uint8_t* p = wp + (uint32_t)(wlane + kb * 8192);
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
       const v4i* p4 = reinterpret_cast<const v4i*>(p + rt * 2048);
@@ -307,8 +324,9 @@ __global__ __launch_bounds__(256, MINW) void gemm_fp8_kernel(const GemmArgs g) {
   auto load_b = [&](int set, int kb) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i)
-      breg[set][i] = *reinterpret_cast<const v4i*>(g.act + boff[i] + kb * 128);
-    sareg[set] = g.act_s[saoff + kb];
+      breg[set][i] = *reinterpret_cast<const v4i*>(g.act + (uint32_t)(boff[i] + kb * 128));
+    sareg[set] = *reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(g.act_s) +
+                                                 (uint32_t)((saoff + kb) * 4));
   };
   // BMODE 1: activation tiles go straight from global memory into LDS
   // (global_load_lds, no staging registers).  They are issued from inline
@@ -351,8 +369,8 @@ __global__ __launch_bounds__(256, MINW) void gemm_fp8_kernel(const GemmArgs g) {
     float swg, swu;
     weight_scales(kb, swg, swu);
     auto read_b = [&](int t, v8i& b, float& sa) {
-      const uint8_t* bp = &lds_b(buf)[t * 2048 + lane * 16];
-      b = join8(*reinterpret_cast<const v4i*>(bp), *reinterpret_cast<const v4i*>(bp + 1024));
+      const uint8_t* bp = &lds_b(buf)[t * 2048];
+      b = join8(*reinterpret_cast<const v4i*>(bp + brd0), *reinterpret_cast<const v4i*>(bp + brd1));
       sa = lds_sa(buf)[t * 16 + (lane & 15)];
     };
     v8i bc;
@@ -390,8 +408,9 @@ __global__ __launch_bounds__(256, MINW) void gemm_fp8_kernel(const GemmArgs g) {
       float s0[GRP], s1[GRP];
 #pragma unroll
       for (int u = 0; u < GRP; ++u) {
-        const uint8_t* bp = &lds_b(buf)[(t0 + u) * 2048 + lane * 16];
-        bf[u] = join8(*reinterpret_cast<const v4i*>(bp), *reinterpret_cast<const v4i*>(bp + 1024));
+        const uint8_t* bp = &lds_b(buf)[(t0 + u) * 2048];
+        bf[u] = join8(*reinterpret_cast<const v4i*>(bp + brd0),
+                      *reinterpret_cast<const v4i*>(bp + brd1));
         const float sa_t = lds_sa(buf)[(t0 + u) * 16 + (lane & 15)];
         s0[u] = sa_t * swg;
         s1[u] = sa_t * swu;
@@ -406,6 +425,19 @@ __global__ __launch_bounds__(256, MINW) void gemm_fp8_kernel(const GemmArgs g) {
         prev = cur;
       }
       acc[3][t0 + GRP - 1] += prev * s1[GRP - 1];
+      if constexpr (ILV) {
+        // issue order inside the group: its LDS reads, two MFMAs, then each
+        // further MFMA after the four promotion FMAs of the MFMA two back
+        __builtin_amdgcn_sched_group_barrier(0x100, 3 * GRP, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+#pragma unroll
+        for (int i = 2; i < 4 * GRP; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x002, ILV, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x002, 8 + 2 * GRP, 0);
+      }
       if (t0 + GRP < TT) __builtin_amdgcn_sched_barrier(0);
     }
   };
