@@ -35,10 +35,10 @@ FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA
 # the factor a 1 GiB copy probe gives) + WRITE_SIZE (x1.000), see
 # profiles/gemm_gateup_k2_decode.md; valid only for the GEMM sources whose combined
 # sha256 starts with the recorded prefix (null otherwise).
-MEASURED_TRAFFIC = {"k2_decode": ("d141686040f3a9e6", 7.918e9),
-                    "k2_prefill": ("d141686040f3a9e6", 13.457e9)}
+MEASURED_TRAFFIC = {"k2_decode": ("707da746324a8448", 7.920e9),
+                    "k2_prefill": ("707da746324a8448", 14.037e9)}
 GEMM_SRCS = [os.path.join(ROOT, "sparse_moe_transformer_sigmoid_amd", "csrc", f)
-             for f in ("gemm_fp8_kernel.h", "gemm_fp8.hip")]
+             for f in ("gemm_fp8_kernel.h", "gemm_fp8.hip", "gemm_fp8_wide.hip")]
 
 
 def measured_traffic(workload: str):

@@ -466,7 +466,8 @@ __global__ __launch_bounds__(256, MINW) void gemm_fp8_kernel(const GemmArgs g) {
   // clamped to the last block, so the tail re-reads a block instead of
   // branching), compute block kb, stage block kb+1 into LDS, barrier.  STEP is
   // a multiple of NBUF and of 2, so every buffer index is a compile-time
-  // constant; full STEPs run without guards, the tail with them.
+  // constant; full STEPs run without guards, the tail with them (BMODE 1:
+  // one loop, the later steps of each STEP guarded).
   constexpr int STEP = (NBUF & 1) ? 2 * NBUF : NBUF;
   auto step = [&](const int j, const int kb) {
     const int cur = j & 1;
@@ -495,14 +496,25 @@ __global__ __launch_bounds__(256, MINW) void gemm_fp8_kernel(const GemmArgs g) {
       __syncthreads();
     }
   };
-  int kb0 = 0;
-  for (; kb0 + STEP <= nkb; kb0 += STEP) {
+  if constexpr (BMODE == 1) {
+    // one loop with a uniform guard on the later steps of a STEP: a separate
+    // tail would keep the prologue's weight block alive across the loop (for
+    // the case of no full STEP), which spills at this register budget
+    for (int kb0 = 0; kb0 < nkb; kb0 += STEP) {
 #pragma unroll
-    for (int j = 0; j < STEP; ++j) step(j, kb0 + j);
+      for (int j = 0; j < STEP; ++j)
+        if (j == 0 || kb0 + j < nkb) step(j, kb0 + j);
+    }
+  } else {
+    int kb0 = 0;
+    for (; kb0 + STEP <= nkb; kb0 += STEP) {
+#pragma unroll
+      for (int j = 0; j < STEP; ++j) step(j, kb0 + j);
+    }
+#pragma unroll
+    for (int j = 0; j < STEP; ++j)
+      if (kb0 + j < nkb) step(j, kb0 + j);
   }
-#pragma unroll
-  for (int j = 0; j < STEP; ++j)
-    if (kb0 + j < nkb) step(j, kb0 + j);
 
   epilogue<GATEUP, TT, NT>(g, acc, lds_red, wi, wave, lane);
 }
