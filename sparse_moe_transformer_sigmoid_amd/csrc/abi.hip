@@ -338,17 +338,19 @@ moe_status run_router(const Dims& D, const Layout& L, void* ws, const void* x, c
 }
 
 moe_status run_permute(const Dims& D, const Layout& L, void* ws, const int32_t* ids,
-                       int32_t* offsets, int32_t* row_pair, int32_t* pair_row, hipStream_t s) {
+                       int32_t* offsets, int32_t* row_pair, int32_t* pair_row, hipStream_t s,
+                       const k2::TileReq* tiles = nullptr, bool* tiles_built = nullptr) {
   Stage st(MOE_STAGE_PERMUTE, s);
   K2_HIP(k2::launch_permute((int)D.T, D.E, D.k, ids, at<int32_t>(ws, L.ccount),
-                            at<int32_t>(ws, L.cbase), offsets, row_pair, pair_row, s));
+                            at<int32_t>(ws, L.cbase), offsets, row_pair, pair_row, s, tiles,
+                            tiles_built));
   return MOE_OK;
 }
 
 moe_status run_experts(const Dims& D, const Layout& L, void* ws, const void* xq, const float* xs,
                        const int32_t* offsets, const int32_t* row_pair, const void* packed_w,
                        float* rows, float* shared_out, const float* topk_w, int weighted,
-                       void* act_q, float* act_s, hipStream_t s) {
+                       void* act_q, float* act_s, hipStream_t s, bool tiles_ready = false) {
   const int T = (int)D.T, P = (int)D.P;
   const Packed pk = packed_layout(D);
   if (!D.fp8) {
@@ -364,7 +366,7 @@ moe_status run_experts(const Dims& D, const Layout& L, void* ws, const void* xq,
   int32_t* mt_start = at<int32_t>(ws, L.mt_start);
   int32_t* tile_group = at<int32_t>(ws, L.tile_group);
   const int64_t mt_bound = mtile_bound(D, bm);
-  {
+  if (!tiles_ready) {
     Stage st(MOE_STAGE_TILES, s);
     K2_HIP(k2::launch_build_tiles(D.E, D.S, T, D.k, bm, (int)mt_bound, offsets, mt_start,
                                   tile_group, s));
@@ -669,9 +671,22 @@ moe_status moe_forward(const moe_config* cfg, int64_t T, const void* x, const vo
   float* shared = D.S ? at<float>(ws, L.shared) : nullptr;
   if ((st = run_router(D, L, ws, x, norm_w, w_router, bias, ids, w, gap, xq, xs, s)) != MOE_OK)
     return st;
-  if ((st = run_permute(D, L, ws, ids, offsets, row_pair, pair_row, s)) != MOE_OK) return st;
+  // the FP8 GEMMs' m-tile table, built by the permutation itself when all
+  // tokens fit one chunk (decode-sized batches)
+  k2::TileReq treq{};
+  bool tiles_ready = false;
+  if (D.fp8) {
+    treq.bm = 16 * gemm_tt(D);
+    treq.max_tiles = (int)mtile_bound(D, treq.bm);
+    treq.n_shared = D.S;
+    treq.mt_start = at<int32_t>(ws, L.mt_start);
+    treq.tile_group = at<int32_t>(ws, L.tile_group);
+  }
+  if ((st = run_permute(D, L, ws, ids, offsets, row_pair, pair_row, s, D.fp8 ? &treq : nullptr,
+                        &tiles_ready)) != MOE_OK)
+    return st;
   if ((st = run_experts(D, L, ws, xq, xs, offsets, row_pair, packed_w, rows, shared, w, 1,
-                        nullptr, nullptr, s)) !=
+                        nullptr, nullptr, s, tiles_ready)) !=
       MOE_OK)
     return st;
   Stage stg(MOE_STAGE_COMBINE, s);

@@ -22,9 +22,18 @@ hipError_t launch_dense_route(int T, float scaling, int32_t* ids, float* w, floa
 
 // ---- permutation (permute.hip)
 int perm_chunk_tokens(int E);
+// GEMM m-tile table wanted together with the permutation (see launch_build_tiles)
+struct TileReq {
+  int bm, max_tiles, n_shared;
+  int32_t* mt_start;
+  int32_t* tile_group;
+};
+// With tiles non-null, *tiles_built says whether the table was built too (it
+// is when all tokens fit one chunk); otherwise launch_build_tiles builds it.
 hipError_t launch_permute(int T, int E, int k, const int32_t* ids, int32_t* chunk_counts,
                           int32_t* chunk_base, int32_t* offsets, int32_t* row_pair,
-                          int32_t* pair_row, hipStream_t s);
+                          int32_t* pair_row, hipStream_t s, const TileReq* tiles = nullptr,
+                          bool* tiles_built = nullptr);
 hipError_t launch_build_tiles(int E, int n_shared, int T, int k, int bm, int max_tiles,
                               const int32_t* offsets, int32_t* mt_start, int32_t* tile_group,
                               hipStream_t s);

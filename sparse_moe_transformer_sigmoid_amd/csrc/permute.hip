@@ -113,6 +113,71 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(int T, int E, int k, 
   }
 }
 
+// All tokens in one chunk (decode-sized batches): the three passes above in
+// one workgroup.  Counts are the popcounts of each expert's token mask, their
+// exclusive scan gives the offsets, and a token's rank is again the number
+// of set bits before it, so the rows equal those of the three-pass path.
+// With mt_start non-null it also builds the GEMM m-tile table, as
+// build_tiles_kernel does.
+__global__ __launch_bounds__(1024) void perm_small_kernel(int T, int E, int k, int words,
+                                                         const int32_t* __restrict__ ids,
+                                                         int32_t* __restrict__ offsets,
+                                                         int32_t* __restrict__ row_pair,
+                                                         int32_t* __restrict__ pair_row,
+                                                         int n_shared, int bm, int max_tiles,
+                                                         int32_t* __restrict__ mt_start,
+                                                         int32_t* __restrict__ tile_group) {
+  __shared__ uint32_t mask[MASK_WORDS];
+  __shared__ int32_t off[1025];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < E * words; i += 1024) mask[i] = 0u;
+  __syncthreads();
+  for (int p = tid; p < T * k; p += 1024) {
+    const int t = p / k;
+    const int e = min(max(ids[p], 0), E - 1);
+    atomicOr(&mask[e * words + (t >> 5)], 1u << (t & 31));
+  }
+  __syncthreads();
+  block_exclusive_scan<1>(
+      E,
+      [&](int e) {
+        int c = 0;
+        for (int w = 0; w < words; ++w) c += __popc(mask[e * words + w]);
+        return c;
+      },
+      off);
+  __syncthreads();
+  for (int e = tid; e <= E; e += 1024) offsets[e] = off[e];
+  for (int p = tid; p < T * k; p += 1024) {
+    const int e = min(max(ids[p], 0), E - 1);
+    const int t = p / k;
+    const uint32_t* me = mask + e * words;
+    int rank = __popc(me[t >> 5] & ((1u << (t & 31)) - 1u));
+    for (int w = 0; w < (t >> 5); ++w) rank += __popc(me[w]);
+    const int row = off[e] + rank;
+    row_pair[row] = p;
+    pair_row[p] = row;
+  }
+  if (mt_start == nullptr) return;
+  const int P = T * k, G = E + n_shared;
+  block_exclusive_scan<2>(
+      G,
+      [&](int g) {
+        int m = T;
+        if (g < E) {
+          const int r0 = min(max(off[g], 0), P);
+          m = min(max(off[g + 1] - r0, 0), P - r0);
+        }
+        return (m + bm - 1) / bm;
+      },
+      mt_start);
+  __syncthreads();
+  for (int g = tid; g < G; g += 1024) {
+    const int q1 = min(mt_start[g + 1], max_tiles);
+    for (int q = mt_start[g]; q < q1; ++q) tile_group[q] = g;
+  }
+}
+
 // mt_start[g] = sum over groups before g of ceil(m_g / bm); groups are the
 // routed experts 0..E-1 (m = expert count) and then the shared expert (m = T).
 // Row ranges are clamped into [0, P) exactly as the GEMM kernels clamp them.
@@ -156,9 +221,20 @@ int perm_chunk_tokens(int E) {
 
 hipError_t launch_permute(int T, int E, int k, const int32_t* ids, int32_t* chunk_counts,
                           int32_t* chunk_base, int32_t* offsets, int32_t* row_pair,
-                          int32_t* pair_row, hipStream_t s) {
+                          int32_t* pair_row, hipStream_t s, const TileReq* tiles,
+                          bool* tiles_built) {
   const int chunk = perm_chunk_tokens(E);
   const int nchunk = (T + chunk - 1) / chunk;
+  if (tiles_built) *tiles_built = false;
+  if (nchunk == 1) {
+    perm_small_kernel<<<1, 1024, 0, s>>>(T, E, k, chunk >> 5, ids, offsets, row_pair, pair_row,
+                                         tiles ? tiles->n_shared : 0, tiles ? tiles->bm : 1,
+                                         tiles ? tiles->max_tiles : 0,
+                                         tiles ? tiles->mt_start : nullptr,
+                                         tiles ? tiles->tile_group : nullptr);
+    if (tiles && tiles_built) *tiles_built = true;
+    return hipGetLastError();
+  }
   perm_count_kernel<<<nchunk, 256, 0, s>>>(T, E, k, chunk, ids, chunk_counts);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
