@@ -37,19 +37,34 @@ FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA
 # sha256 starts with the recorded prefix (null otherwise).
 MEASURED_TRAFFIC = {"k2_decode": ("707da746324a8448", 7.920e9),
                     "k2_prefill": ("707da746324a8448", 14.037e9)}
+# FP8 MFMA busy fraction of the gate/up launch (SQ_VALU_MFMA_BUSY_CYCLES over
+# GRBM_GUI_ACTIVE x SIMDs) and its executed/algorithmic MFMA work
+# (SQ_INSTS_VALU_MFMA_MOPS_F8 x 512), from rocprofv3 counters, see
+# profiles/gemm_mfma_k2_prefill_dense.md; same source-hash rule as the traffic.
+MEASURED_MFMA = {"k2_prefill": ("707da746324a8448", 0.424, 1.335),
+                 "k2_dense": ("707da746324a8448", 0.437, 1.000)}
 GEMM_SRCS = [os.path.join(ROOT, "sparse_moe_transformer_sigmoid_amd", "csrc", f)
              for f in ("gemm_fp8_kernel.h", "gemm_fp8.hip", "gemm_fp8_wide.hip")]
 
 
-def measured_traffic(workload: str):
+def _sources_match(prefix: str) -> bool:
     import hashlib
-    rec = MEASURED_TRAFFIC.get(workload)
-    if rec is None:
-        return None
     h = hashlib.sha256()
     for f in GEMM_SRCS:
         h.update(open(f, "rb").read())
-    return rec[1] if h.hexdigest().startswith(rec[0]) else None
+    return h.hexdigest().startswith(prefix)
+
+
+def measured_traffic(workload: str):
+    rec = MEASURED_TRAFFIC.get(workload)
+    return rec[1] if rec is not None and _sources_match(rec[0]) else None
+
+
+def measured_mfma(workload: str):
+    """(MFMA busy fraction, executed / algorithmic MFMA work) or None."""
+    rec = MEASURED_MFMA.get(workload)
+    return {"mfma_busy": rec[1], "executed_over_algorithmic": rec[2]} \
+        if rec is not None and _sources_match(rec[0]) else None
 
 
 def parse():
@@ -294,6 +309,7 @@ def main():
                      "achieved": res["gu_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": res["gu_gbs"] / HBM_PEAK_GBS,
                      "traffic": measured_traffic(shp.name),
+                     "mfma_counters": measured_mfma(shp.name),
                      "kernel_ms": gu_ms, "algorithmic_bytes": res["gu_bytes"]},
         "stage_ms": res["stage"],
     }
@@ -323,6 +339,7 @@ def main():
             "gateup_gbs": rp["gu_gbs"], "gateup_frac_hbm_peak": rp["gu_gbs"] / HBM_PEAK_GBS,
             "gateup_arithmetic_intensity": rp["gu_flops"] / rp["gu_bytes"],
             "gateup_traffic": measured_traffic(pre.shape.name),
+            "gateup_mfma_counters": measured_mfma(pre.shape.name),
             "sclk_mhz": pre_sclk,
             # the published FP8 peak assumes 2400 MHz; at the measured clock:
             "gateup_frac_fp8_peak_at_sclk":
