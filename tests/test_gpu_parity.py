@@ -235,8 +235,9 @@ def test_small_fp8_one_hot_expert_spans_many_tiles(T):
     check_layer(inp, g)
 
 
-def test_small_dense_ffn():
-    shape = synth.MoEShape("dense_small", tokens=150, d_model=256, n_experts=1, n_shared=0,
+@pytest.mark.parametrize("T", [150, 40])   # 40 tokens: the one-workgroup permutation path
+def test_small_dense_ffn(T):
+    shape = synth.MoEShape("dense_small", tokens=T, d_model=256, n_experts=1, n_shared=0,
                            top_k=1, d_ff=384, fmt="fp8", routed_scaling=1.0, dense=True)
     inp = synth.generate(shape, seed=8, device="cuda")
     g = gpu_chain(_layer(inp), inp)
