@@ -330,6 +330,20 @@ def test_k2_ragged_token_counts(k2, T):
     check_layer(inp, g, tokens=_sample(T, 3, seed=T))
 
 
+def test_k2_maximum_token_count(k2):
+    """The largest batch one call accepts at the K2 shape: T (top_k + 1)
+    max(d_model, d_ff) < 2^32 gives 66,576 tokens (1,041 permutation chunks,
+    599,184 GEMM rows); one more is rejected on the host."""
+    base, layer = k2
+    T = 66576
+    inp = synth.with_workload(base, synth.K2_DECODE, seed=4242, tokens=T)
+    g = gpu_chain(layer, inp)
+    counts = np.diff(g["offsets"])
+    _log(f"T={T}: rows per routed expert min {counts.min()} max {counts.max()}")
+    toks = np.unique(np.concatenate([_sample(T, 3, seed=5), [0, T - 1]]))
+    check_layer(inp, g, tokens=toks)
+
+
 @pytest.mark.parametrize("workload", ["decode", "prefill"])
 def test_k2_repeats_with_poisoned_buffers(k2, workload):
     """Ten forwards with the workspace and the output filled with 0xFF bytes
