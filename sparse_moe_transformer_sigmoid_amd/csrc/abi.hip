@@ -210,7 +210,7 @@ int router_ksplit(const Dims& D) {
 int gemm_tt(const Dims& D) {
   const double avg = D.dense ? (double)D.T : (double)D.P / D.E;
   if (avg <= 12) return 1;
-  if (avg <= 24) return 2;
+  if (avg <= 16) return 2;
   if (avg <= 48) return 4;
   return 8;
 }

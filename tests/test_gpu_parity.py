@@ -318,7 +318,7 @@ def test_k2_skewed(k2):
     check_layer(inp, g, tokens=toks)
 
 
-@pytest.mark.parametrize("T", [1, 5, 257, 1000, 2000, 3000, 5000])
+@pytest.mark.parametrize("T", [1, 5, 257, 700, 1000, 2000, 3000, 5000])
 def test_k2_ragged_token_counts(k2, T):
     """K2 dimensions at token counts that select every m-tile width (16, 32,
     64 and 128 rows) and leave ragged last tiles in most experts."""
