@@ -427,7 +427,8 @@ __global__ __launch_bounds__(256, MINW) void gemm_fp8_kernel(const GemmArgs g) {
       acc[3][t0 + GRP - 1] += prev * s1[GRP - 1];
       if constexpr (ILV) {
         // issue order inside the group: its LDS reads, two MFMAs, then each
-        // further MFMA after the four promotion FMAs of the MFMA two back
+        // further MFMA after ILV VALU instructions (the four promotion FMAs
+        // of the MFMA two back, and a scale product)
         __builtin_amdgcn_sched_group_barrier(0x100, 3 * GRP, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
