@@ -16,7 +16,9 @@ namespace {
 template <bool GATEUP>
 hipError_t launch_tt(int tt, const GemmArgs& a, int grid, hipStream_t s) {
   switch (tt) {
-    case 1: gemm_fp8_kernel<GATEUP, 1, 2, true, 2, 1><<<grid, 256, 0, s>>>(a); break;
+    case 1:   // uneven split over the XCDs: more workgroups than items
+      gemm_fp8_kernel<GATEUP, 1, 2, true, 2, 1><<<split_grid(grid), 256, 0, s>>>(a);
+      break;
     case 2: gemm_fp8_kernel<GATEUP, 2, 2, false, 2, 1><<<grid, 256, 0, s>>>(a); break;
     case 4: gemm_fp8_kernel<GATEUP, 4, 3, false, 2, 1><<<grid, 256, 0, s>>>(a); break;
     case 8:

@@ -40,6 +40,16 @@ namespace {
 // largest K / 128 of either GEMM (d_model <= 16384, d_ff <= 65536)
 constexpr int MAX_NKB = 512;
 
+// work-item shares of even and odd XCDs in the 16-row (TT = 1) launches
+constexpr int XCD_EVEN_SHARE = 15, XCD_ODD_SHARE = 13;
+
+// workgroups that cover W <= grid items under the uneven split: 8 quotas of
+// at most ceil(W * 15 / 112) each, for any W up to the even-split grid
+inline int split_grid(int grid) {
+  return (int)(((int64_t)grid * 2 * XCD_EVEN_SHARE / (XCD_EVEN_SHARE + XCD_ODD_SHARE) + 15) /
+               8 * 8 + 8);
+}
+
 __device__ __forceinline__ v8i join8(v4i a, v4i b) {
   return v8i{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 }
@@ -75,14 +85,33 @@ struct WorkItem {
 // Work item L (after the XCD remap) -> (group, weight chunk, m-tile).  The
 // grid is a host-side upper bound; workgroups past the device-side m-tile
 // count get valid = false.
+//
+// RE : RO is the share of work items an even : odd XCD gets.  Workgroups on
+// odd-numbered XCDs run about 10% longer than on even ones (measured on every
+// box, in both GEMMs), so the streaming (one m-tile per group) launches give
+// even XCDs XCD_EVEN_SHARE items for every XCD_ODD_SHARE of an odd one, and
+// all XCDs finish together; the grid must then hold 8 * ceil(quota_even)
+// workgroups (see split_grid).
+template <int RE = 1, int RO = 1>
 __device__ __forceinline__ WorkItem decode_work(const GemmArgs& g, int BM) {
   WorkItem w{};
   const int Wtot = g.mt_start[g.G] * g.NC;
-  const int Wp = (Wtot + 7) & ~7;
   const int b = blockIdx.x;
   w.valid = false;
-  if (b >= Wp) return w;
-  const int L = (b & 7) * (Wp >> 3) + (b >> 3);
+  int L;
+  if constexpr (RE == RO) {
+    const int Wp = (Wtot + 7) & ~7;
+    if (b >= Wp) return w;
+    L = (b & 7) * (Wp >> 3) + (b >> 3);
+  } else {
+    // XCD x takes items [start_x, start_x + quota_x): pairs of (even, odd)
+    // XCDs in order, quota qe for the even one and qo for the odd one
+    const int x = b & 7, i = b >> 3;
+    const int qe = (int)(((int64_t)Wtot * RE + 4 * (RE + RO) - 1) / (4 * (RE + RO)));
+    const int qo = (int)(((int64_t)Wtot * RO + 4 * (RE + RO) - 1) / (4 * (RE + RO)));
+    if (i >= ((x & 1) ? qo : qe)) return w;
+    L = (x >> 1) * (qe + qo) + (x & 1) * qe + i;
+  }
   if (L >= Wtot) return w;
   const int q = L / g.NC;
   const int lo = min(max(g.tile_group[q], 0), g.G - 1);   // mt_start[lo] <= q < mt_start[lo+1]
@@ -253,7 +282,8 @@ __global__ __launch_bounds__(256, MINW) void gemm_fp8_kernel(const GemmArgs g) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  const WorkItem wi = decode_work(g, BM);
+  const WorkItem wi = TT == 1 ? decode_work<XCD_EVEN_SHARE, XCD_ODD_SHARE>(g, BM)
+                              : decode_work(g, BM);
   if (!wi.valid) return;
   const int grp = wi.grp, nc = wi.nc, row0 = wi.row0, mcount = wi.mcount, ntt = wi.ntt;
   const bool shared_grp = wi.shared_grp;
