@@ -23,7 +23,9 @@
  *    shared_out, residual, out, packed weights, workspace, expert codes) must
  *    be 16-byte aligned; scales, bias, ids, weights, gap and index arrays
  *    4-byte aligned.  Nothing here allocates device memory except through
- *    the caller's workspace, and nothing is kept between calls.
+ *    the caller's workspace, and nothing is kept between calls.  Calls that
+ *    may run at the same time (on different streams) need their own
+ *    workspaces and outputs; read-only inputs (weights, x) may be shared.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
  *    enqueues work on it and returns without synchronising; device faults
  *    surface at the caller's next synchronisation.
