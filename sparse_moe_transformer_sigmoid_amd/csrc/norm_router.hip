@@ -250,6 +250,42 @@ __device__ __forceinline__ float unordered_bits(uint32_t o) {
 
 constexpr int TK_WAVES = 4;
 
+// One DPP row shift of a 64-bit value: lane i of each 16-lane row gets lane
+// i - S of the same row, and 0 where that lane is outside the row.
+template <int S>
+__device__ __forceinline__ uint64_t row_shr_u64(uint64_t v) {
+  constexpr int ctrl = 0x110 + S;   // DPP row_shr:S
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, ctrl, 0xF, 0xF, true);
+  const uint32_t hi =
+      (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), ctrl, 0xF, 0xF, true);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t lane_u64(uint64_t v, int lane) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, lane);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Wave maximum of non-negative 64-bit keys, the same value in every lane.
+// Shifts by 1, 2, 4 and 8 within each row leave lane 16r + 15 with the
+// maximum of row r; the four row maxima are then read as scalars.  Register
+// moves only: no LDS round trips as with a shuffle per step.
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t v) {
+  uint64_t o;
+  o = row_shr_u64<1>(v); v = o > v ? o : v;
+  o = row_shr_u64<2>(v); v = o > v ? o : v;
+  o = row_shr_u64<4>(v); v = o > v ? o : v;
+  o = row_shr_u64<8>(v); v = o > v ? o : v;
+  uint64_t m = lane_u64(v, 15);
+#pragma unroll
+  for (int r = 1; r < 4; ++r) {
+    o = lane_u64(v, 16 * r + 15);
+    m = o > m ? o : m;
+  }
+  return m;
+}
+
 // One wavefront per token.  Key = (ordered biased score << 32) | ~expert, so
 // the wave maximum is the highest score and, on equal scores, the lower id.
 template <int MAXJ, int MAXK>
@@ -288,7 +324,7 @@ __global__ __launch_bounds__(TK_WAVES * 64) void topk_kernel(int T, int E, int k
       uint64_t best = 0;
 #pragma unroll
       for (int j = 0; j < MAXJ; ++j) best = key[j] > best ? key[j] : best;
-      best = wave_max(best);
+      best = wave_max_key(best);
 #pragma unroll
       for (int j = 0; j < MAXJ; ++j)
         if (key[j] == best) key[j] = 0;
@@ -311,7 +347,14 @@ __global__ __launch_bounds__(TK_WAVES * 64) void topk_kernel(int T, int E, int k
     s_me = s_sh[wave][my_e];
     my_s = (double)s_me;
   }
-  const float denom = (float)wave_sum(my_s);
+  // sum of the k chosen scores (lanes 0..k-1) in fp64: exact, so in any order,
+  // while the scores lie within 2^29 of one another
+  double ssum = 0.0;
+#pragma unroll
+  for (int r = 0; r < MAXK; ++r)
+    if (r < k) ssum += __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(my_s), r),
+                                        __builtin_amdgcn_readlane(__double2loint(my_s), r));
+  const float denom = (float)ssum;
   if (t_raw < T) {
     if (lane < k) {
       const float wv = renorm ? (s_me / denom) * scaling : s_me * scaling;
