@@ -43,16 +43,6 @@ __device__ __forceinline__ float fp8_scale(float amax) {
 }
 
 template <typename T>
-__device__ __forceinline__ T wave_max(T v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    T o = __shfl_xor(v, m);
-    v = o > v ? o : v;
-  }
-  return v;
-}
-
-template <typename T>
 __device__ __forceinline__ T wave_sum(T v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
