@@ -29,6 +29,8 @@
 // items: the m-tiles of one weight chunk, and the chunks of one expert, then
 // share that XCD's L2.
 #pragma once
+#include <type_traits>
+
 #include "k2_common.h"
 #include "k2_launch.h"
 
@@ -339,12 +341,13 @@ __global__ __launch_bounds__(256, MINW) void gemm_fp8_kernel(const GemmArgs g) {
   v4i breg[BSETS][CPT];
   float sareg[2] = {0.f, 0.f};
 
-  auto load_w = [&](v8i (&w)[4], int kb) {
+  // ntc: std::true_type for non-temporal weight loads
+  auto load_w = [&](v8i (&w)[4], int kb, auto ntc) {
     const uint8_t* p = wp + (uint32_t)(wlane + kb * 8192);
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
       const v4i* p4 = reinterpret_cast<const v4i*>(p + rt * 2048);
-      if constexpr (NT) {
+      if constexpr (decltype(ntc)::value) {
         w[rt] = join8(__builtin_nontemporal_load(p4), __builtin_nontemporal_load(p4 + 64));
       } else {
         w[rt] = join8(p4[0], p4[64]);
@@ -480,6 +483,7 @@ __global__ __launch_bounds__(256, MINW) void gemm_fp8_kernel(const GemmArgs g) {
   // each step issues the activations before the weights of block
   // kb+NBUF-1, and ends by waiting only for the activations (BMODE 0: those
   // of block kb+1, issued one step earlier).
+  auto kloop = [&](auto ntc) {
   const int nkb = g.nkb;
   if constexpr (BMODE == 1) {
     dma_b(0, 0);
@@ -490,7 +494,7 @@ __global__ __launch_bounds__(256, MINW) void gemm_fp8_kernel(const GemmArgs g) {
   }
 #pragma unroll
   for (int i = 0; i < NBUF - 1; ++i)
-    if (i < nkb) load_w(wbuf[i], i);
+    if (i < nkb) load_w(wbuf[i], i, ntc);
   if constexpr (BMODE != 1) store_b(0, 0);
   __syncthreads();
   // One step: prefetch (activations of kb+2, weights of kb+NBUF-1; indices
@@ -511,7 +515,7 @@ __global__ __launch_bounds__(256, MINW) void gemm_fp8_kernel(const GemmArgs g) {
     } else {
       load_b(0, min(kb + 1, nkb - 1));
     }
-    load_w(wbuf[(j + NBUF - 1) % NBUF], min(kb + NBUF - 1, nkb - 1));
+    load_w(wbuf[(j + NBUF - 1) % NBUF], min(kb + NBUF - 1, nkb - 1), ntc);
     // keep the prefetches issued here: the scheduler would otherwise sink
     // them next to their use to save registers, undoing the ring
     __builtin_amdgcn_sched_barrier(0);
@@ -545,6 +549,17 @@ __global__ __launch_bounds__(256, MINW) void gemm_fp8_kernel(const GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < STEP; ++j)
       if (kb0 + j < nkb) step(j, kb0 + j);
+  }
+
+  };
+  // The shared expert's group has several m-tiles in the launches whose
+  // routed groups have one: its weight chunks are read once per m-tile, so
+  // that group loads them through L2 while routed chunks stream past it.
+  if constexpr (NT) {
+    if (wi.shared_grp) kloop(std::false_type{});
+    else kloop(std::true_type{});
+  } else {
+    kloop(std::false_type{});
   }
 
   epilogue<GATEUP, TT, NT>(g, acc, lds_red, wi, wave, lane);
