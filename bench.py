@@ -35,14 +35,14 @@ FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA
 # the factor a 1 GiB copy probe gives) + WRITE_SIZE (x1.000), see
 # profiles/gemm_gateup_k2_decode.md; valid only for the GEMM sources whose combined
 # sha256 starts with the recorded prefix (null otherwise).
-MEASURED_TRAFFIC = {"k2_decode": ("3d7860c3e8f85e33", 7.922e9),
-                    "k2_prefill": ("3d7860c3e8f85e33", 14.009e9)}
+MEASURED_TRAFFIC = {"k2_decode": ("703de7b0d8f61124", 7.886e9),
+                    "k2_prefill": ("703de7b0d8f61124", 13.892e9)}
 # FP8 MFMA busy fraction of the gate/up launch (SQ_VALU_MFMA_BUSY_CYCLES over
 # GRBM_GUI_ACTIVE x SIMDs) and its executed/algorithmic MFMA work
 # (SQ_INSTS_VALU_MFMA_MOPS_F8 x 512), from rocprofv3 counters, see
 # profiles/gemm_mfma_k2_prefill_dense.md; same source-hash rule as the traffic.
-MEASURED_MFMA = {"k2_prefill": ("3d7860c3e8f85e33", 0.420, 1.335),
-                 "k2_dense": ("3d7860c3e8f85e33", 0.437, 1.000)}
+MEASURED_MFMA = {"k2_prefill": ("703de7b0d8f61124", 0.423, 1.335),
+                 "k2_dense": ("703de7b0d8f61124", 0.441, 1.000)}
 GEMM_SRCS = [os.path.join(ROOT, "sparse_moe_transformer_sigmoid_amd", "csrc", f)
              for f in ("gemm_fp8_kernel.h", "gemm_fp8.hip", "gemm_fp8_wide.hip")]
 
