@@ -29,12 +29,11 @@ class ExpertFetcher:
         return out
 
 
-def run_oracle(inputs, tokens=None, ids_override=None, act_override=None) -> dict:
+def run_oracle(inputs, tokens=None) -> dict:
     """Oracle forward on generated inputs (any device)."""
     p: LayerParams = params_from_shape(inputs.shape)
     x = to_f32(inputs.x)
     norm_w = to_f32(inputs.norm_w)
     wr = None if inputs.w_router is None else to_f32(inputs.w_router)
     bias = None if inputs.bias is None else to_f32(inputs.bias)
-    return moe_layer(p, x, norm_w, wr, bias, ExpertFetcher(inputs), tokens=tokens,
-                     ids_override=ids_override, act_override=act_override)
+    return moe_layer(p, x, norm_w, wr, bias, ExpertFetcher(inputs), tokens=tokens)

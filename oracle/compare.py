@@ -8,17 +8,16 @@ TEST INFRASTRUCTURE ONLY.
   1e-5.
 * Permutation: bit-exact against the oracle's grouping applied to the GPU's
   own ids.
+* Outputs of a token are compared only where the GPU chose the oracle's
+  expert set (every unflagged token; a flagged token with another valid set
+  has no unique output and is reported, not compared).
 * Floating-point outputs: max |gpu - ref| <= 2e-2 * RMS(ref) and
   mean |gpu - ref| / mean |ref| <= 5e-3, both in fp64 over the compared set.
-  The fp32 MoE output y is held to this as is; the bf16 layer output
-  out = bf16(x + y) may in addition differ by one bf16 step where the two
-  fp32 values round to different neighbours (at |out| >= 8 one step, 2^-4,
-  is larger than 2e-2 * RMS(out) by itself).
-* Requantised SwiGLU activations: each e4m3 code is decided on an fp32 value
-  that gfx950's FP8 MFMA sums at reduced precision, so a GPU code may sit
-  one step from the oracle's exact code; the tests check that, then evaluate
-  the down projections on the GPU's codes (like the expert choice of a
-  near-tie token).
+  The fp32 MoE output y is held to this as is.  The bf16 layer output
+  out = bf16(x + y) too, with one relief in its max-abs part: where the two
+  fp32 values round to different bf16 neighbours the results differ by one
+  bf16 step, which is not counted (at |out| >= 8 one step, 2^-4, exceeds
+  2e-2 * RMS(out) by itself); its mean-relative part is on the raw difference.
 """
 from __future__ import annotations
 
@@ -39,17 +38,17 @@ def bf16_ulp(r: np.ndarray) -> np.ndarray:
 def close_report(gpu, ref, max_abs_frac: float = MAX_ABS_FRAC, bf16_out: bool = False) -> dict:
     """Tolerance report.  bf16_out: the compared values were each rounded once
     to bf16 from fp32, so one bf16 step of difference is the rounding decision
-    falling the other way and is not counted against the bound."""
+    falling the other way; it is not counted against the max-abs bound (the
+    mean-relative figure is taken on the raw difference)."""
     g = np.asarray(gpu, dtype=np.float64)
     r = np.asarray(ref, dtype=np.float64)
     assert g.shape == r.shape, (g.shape, r.shape)
     diff = np.abs(g - r)
-    if bf16_out:
-        diff = np.maximum(diff - bf16_ulp(r), 0.0)
+    dmax = np.maximum(diff - bf16_ulp(r), 0.0) if bf16_out else diff
     rms = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
-    max_abs = float(diff.max()) if r.size else 0.0
+    max_abs = float(dmax.max()) if r.size else 0.0
     mean_ref = float(np.mean(np.abs(r))) if r.size else 0.0
-    mean_rel = float(diff.mean() / mean_ref) if mean_ref > 0 else float(diff.mean())
+    mean_rel = float(diff.mean() / mean_ref) if mean_ref > 0 else float(diff.mean() if r.size else 0.0)
     finite = bool(np.all(np.isfinite(g)))
     ok = finite and max_abs <= max_abs_frac * rms and mean_rel <= MEAN_REL
     return dict(max_abs=max_abs, rms=rms, mean_rel=mean_rel, finite=finite, ok=ok)
@@ -78,6 +77,6 @@ def check_routing(gpu_ids, gpu_w, ref: dict, w_rtol: float = 2e-5) -> dict:
         assert len(set(gpu_ids[t].tolist())) == k
         assert np.all(sb[t][gpu_ids[t]] >= kth - GAP_FLAG), f"token {t}"
     assert np.all(np.diff(gpu_ids, axis=1) > 0), "ids not ascending"
-    ok_w = same
-    np.testing.assert_allclose(gpu_w[ok_w], w[ok_w], rtol=w_rtol, atol=0)
-    return dict(tokens=T, flagged=int(flagged.sum()), differing_flagged=int((flagged & ~same).sum()))
+    np.testing.assert_allclose(gpu_w[same], w[same], rtol=w_rtol, atol=0)
+    return dict(tokens=T, flagged=int(flagged.sum()), differing_flagged=int((flagged & ~same).sum()),
+                agree=same)

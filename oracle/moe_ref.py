@@ -151,14 +151,13 @@ def routing_weights(s: np.ndarray, ids: np.ndarray, scaling: float, renorm: bool
     return f32(w * np.float32(scaling))
 
 
-def route(h, w_router, bias, k, scaling, renorm, ids_override=None):
+def route(h, w_router, bias, k, scaling, renorm):
     z = router_logits(h, w_router)
     s = sigmoid_scores(z)
     sb = f32(s + f32(bias)[None, :])
     ids, gap = select_topk(sb, k)
-    use = ids if ids_override is None else np.sort(ids_override, axis=1).astype(np.int32)
-    w = routing_weights(s, use, scaling, renorm)
-    return dict(z=z, s=s, sb=sb, ids=ids, gap=gap, w=w, used_ids=use)
+    w = routing_weights(s, ids, scaling, renorm)
+    return dict(z=z, s=s, sb=sb, ids=ids, gap=gap, w=w)
 
 
 # ------------------------------------------------------------ permutation ---
@@ -223,9 +222,7 @@ def _expert_f64(wts: dict, fp8: bool):
 
 def moe_layer(p: LayerParams, x: np.ndarray, norm_w: np.ndarray,
               w_router: Optional[np.ndarray], bias: Optional[np.ndarray],
-              expert: Callable[[int], dict], tokens: Optional[np.ndarray] = None,
-              ids_override: Optional[np.ndarray] = None,
-              act_override: Optional[dict] = None) -> dict:
+              expert: Callable[[int], dict], tokens: Optional[np.ndarray] = None) -> dict:
     """Full sub-layer: out = x + MoE(RMSNorm(x)).
 
     x, norm_w, w_router: float32 arrays holding the (exact) values of the
@@ -233,16 +230,6 @@ def moe_layer(p: LayerParams, x: np.ndarray, norm_w: np.ndarray,
     (codes + scales, or fp32), e = n_experts .. n_experts+n_shared-1 being
     the shared experts.  Routing and the permutation cover every token;
     expert outputs, y and out are computed for ``tokens`` (default: all).
-    ids_override replaces the selected sets (weights still come from the
-    oracle's own unbiased scores).
-
-    act_override (FP8 layer) gives requantised SwiGLU activations to feed the
-    down projections instead of the oracle's own: a dict with "codes"
-    [n, k, d_ff], "scales" [n, k, d_ff/128] for the routed pairs of the
-    selected tokens and "shared_codes" / "shared_scales" [n, ...] for the
-    shared expert.  Each e4m3 code is a decision taken on an fp32 value; this
-    evaluates the rest of the layer on another implementation's decisions.
-    The results then also hold o_pairs_ov, shared_ov, y_ov and out_ov.
     """
     T = x.shape[0]
     k, E = p.top_k, p.n_experts
@@ -254,10 +241,9 @@ def moe_layer(p: LayerParams, x: np.ndarray, norm_w: np.ndarray,
     if p.dense:
         ids = np.zeros((T, 1), dtype=np.int32)
         w = np.ones((T, 1), dtype=np.float32) * np.float32(p.routed_scaling)
-        res.update(ids=ids, w=w, gap=np.full(T, np.inf, np.float32), used_ids=ids)
+        res.update(ids=ids, w=w, gap=np.full(T, np.inf, np.float32))
     else:
-        res.update(route(h, w_router, bias, k, p.routed_scaling, p.norm_topk_prob,
-                         ids_override))
+        res.update(route(h, w_router, bias, k, p.routed_scaling, p.norm_topk_prob))
     offsets, row_pair, pair_row = permute(res["ids"], E)
     res.update(offsets=offsets, row_pair=row_pair, pair_row=pair_row)
 
@@ -269,50 +255,59 @@ def moe_layer(p: LayerParams, x: np.ndarray, norm_w: np.ndarray,
     else:
         hin = hs.astype(np.float64)
 
-    used = res["used_ids"][sel]
+    used = res["ids"][sel]
     wsel = res["w"][sel]
     n = len(sel)
     kk = used.shape[1]
-    ov = act_override is not None
     o_pairs = np.zeros((n, kk, p.d_model), dtype=np.float32)
     a_pairs = np.zeros((n, kk, p.d_ff), dtype=np.float32)
-    o_pairs_ov = np.zeros_like(o_pairs) if ov else None
     for e in np.unique(used):
         ti, si = np.nonzero(used == e)
         wg, wu, wd = _expert_f64(expert(int(e)), p.fp8)
         o, a, _, _ = swiglu_expert(hin[ti], wg, wu, wd, p.fp8)
         o_pairs[ti, si] = o
         a_pairs[ti, si] = a
-        if ov:
-            o_pairs_ov[ti, si] = down_projection(act_override["codes"][ti, si],
-                                                 act_override["scales"][ti, si], wd)
         del wg, wu, wd
-    shared_parts, shared_parts_ov = [], []
+    shared_parts = []
     for j in range(p.n_shared):
         wg, wu, wd = _expert_f64(expert(E + j), p.fp8)
         o, _, _, _ = swiglu_expert(hin, wg, wu, wd, p.fp8)
         shared_parts.append(o)
-        if ov:
-            shared_parts_ov.append(down_projection(act_override["shared_codes"],
-                                                   act_override["shared_scales"], wd))
         del wg, wu, wd
 
-    def combine(o_pairs_, parts):
-        y64 = np.einsum("ts,tsd->td", wsel.astype(np.float64), o_pairs_.astype(np.float64))
-        for o in parts:
-            y64 = y64 + o.astype(np.float64)
-        sh = (f32(np.sum([o.astype(np.float64) for o in parts], axis=0)) if parts
+    # y = sum over the token's experts in ascending id of w * o, then the
+    # shared expert(s) with weight 1; out = x + y rounded once
+    y64 = np.einsum("ts,tsd->td", wsel.astype(np.float64), o_pairs.astype(np.float64))
+    for o in shared_parts:
+        y64 = y64 + o.astype(np.float64)
+    shared = (f32(np.sum([o.astype(np.float64) for o in shared_parts], axis=0)) if shared_parts
               else np.zeros((n, p.d_model), dtype=np.float32))
-        y_ = f32(y64)
-        out_ = f32(f32(x[sel]) + y_)
-        return sh, y_, (bf16_round(out_) if p.fp8 else out_)
-
-    shared, y, out = combine(o_pairs, shared_parts)
+    y = f32(y64)
+    out = f32(f32(x[sel]) + y)
+    out = bf16_round(out) if p.fp8 else out
     res.update(tokens=sel, o_pairs=o_pairs, a_pairs=a_pairs, shared=shared, y=y, out=out)
-    if ov:
-        shared_ov, y_ov, out_ov = combine(o_pairs_ov, shared_parts_ov)
-        res.update(o_pairs_ov=o_pairs_ov, shared_ov=shared_ov, y_ov=y_ov, out_ov=out_ov)
     return res
+
+
+def expert_rows(p: LayerParams, x: np.ndarray, norm_w: np.ndarray, wts: dict,
+                tokens: np.ndarray) -> np.ndarray:
+    """One expert's unweighted output o for the given tokens (fp32 [n, d]).
+
+    The same steps as the layer for those tokens alone: RMSNorm, activation
+    quantisation (FP8 layer), then the SwiGLU expert.  Each token's row
+    depends only on that token, so any subset of an expert's tokens can be
+    checked without running the rest of the layer.
+    """
+    tokens = np.asarray(tokens, dtype=np.int64)
+    h = rmsnorm(x[tokens], norm_w, p.rms_eps, round_bf16=p.fp8)
+    if p.fp8:
+        xq, xs = quantize_1x128(h)
+        hin = dequantize_1x128(xq, xs)
+    else:
+        hin = h.astype(np.float64)
+    wg, wu, wd = _expert_f64(wts, p.fp8)
+    o, _, _, _ = swiglu_expert(hin, wg, wu, wd, p.fp8)
+    return o
 
 
 def params_from_shape(shape) -> LayerParams:

@@ -68,9 +68,9 @@ def _pin_calls():
 def _biased_weights(mp):
     route = R.route
 
-    def mutated(h, w_router, bias, k, scaling, renorm, ids_override=None):
-        r = route(h, w_router, bias, k, scaling, renorm, ids_override)
-        r["w"] = R.routing_weights(r["sb"], r["used_ids"], scaling, renorm)
+    def mutated(h, w_router, bias, k, scaling, renorm):
+        r = route(h, w_router, bias, k, scaling, renorm)
+        r["w"] = R.routing_weights(r["sb"], r["ids"], scaling, renorm)
         return r
     _plant(mp, "route", mutated)
 
@@ -219,8 +219,8 @@ def _router_rows_shifted(mp):
 def _bias_ignored(mp):
     route = R.route
 
-    def mutated(h, w_router, bias, k, scaling, renorm, ids_override=None):
-        return route(h, w_router, np.zeros_like(bias), k, scaling, renorm, ids_override)
+    def mutated(h, w_router, bias, k, scaling, renorm):
+        return route(h, w_router, np.zeros_like(bias), k, scaling, renorm)
     _plant(mp, "route", mutated)
 
 

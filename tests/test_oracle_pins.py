@@ -400,26 +400,24 @@ def test_doubling_down_scales_doubles_output_exactly():
     assert np.array_equal(r1["y"], r0["y"] * 2)
 
 
-def test_act_override_with_own_codes_reproduces_layer():
+def test_expert_rows_match_the_layer_per_token():
+    """expert_rows (one expert on a subset of tokens) gives, for each token,
+    the row the whole layer computes for that (token, expert) pair, and the
+    shared expert's output; a token's row does not depend on the others."""
+    from oracle.adapt import to_f32
     shape = synth.small_fp8(tokens=20, n_experts=8, top_k=2)
     inp = synth.generate(shape, seed=5)
     r0 = run_oracle(inp)
-    n, k, I = 20, 2, shape.d_ff
-    codes, scales = R.quantize_1x128(r0["a_pairs"].reshape(-1, I))
-    hin = R.dequantize_1x128(r0["xq"], r0["xs"])
-    w = inp.expert_numpy(8)
-    g = R.f32(hin @ R.dequantize_weight(w["w_gate"], w["s_gate"]).T)
-    u = R.f32(hin @ R.dequantize_weight(w["w_up"], w["s_up"]).T)
-    sc, ss = R.quantize_1x128(R.silu_mul(g, u))
-    ov = dict(codes=codes.reshape(n, k, I), scales=scales.reshape(n, k, -1),
-              shared_codes=sc, shared_scales=ss)
-    r1 = run_oracle(inp, act_override=ov)
-    assert np.array_equal(r1["o_pairs_ov"], r0["o_pairs"])
-    assert np.array_equal(r1["shared_ov"], r0["shared"])
-    assert np.array_equal(r1["y_ov"], r0["y"]) and np.array_equal(r1["out_ov"], r0["out"])
-    # a different code in one pair changes only that pair's row
-    ov2 = dict(ov, codes=ov["codes"].copy())
-    ov2["codes"][3, 1, 0] ^= 1
-    r2 = run_oracle(inp, act_override=ov2)
-    diff = np.any(r2["o_pairs_ov"] != r0["o_pairs"], axis=2)
-    assert diff[3, 1] and diff.sum() == 1
+    p = R.params_from_shape(shape)
+    x, g = to_f32(inp.x), to_f32(inp.norm_w)
+    for e in range(8):
+        ti, si = np.nonzero(r0["ids"] == e)
+        if ti.size == 0:
+            continue
+        o = R.expert_rows(p, x, g, inp.expert_numpy(e), ti)
+        assert np.array_equal(o, r0["o_pairs"][ti, si]), e
+        # reversed order and a single token give the same rows
+        assert np.array_equal(R.expert_rows(p, x, g, inp.expert_numpy(e), ti[::-1]), o[::-1])
+        assert np.array_equal(R.expert_rows(p, x, g, inp.expert_numpy(e), ti[-1:]), o[-1:])
+    sh = R.expert_rows(p, x, g, inp.expert_numpy(8), np.arange(20))
+    assert np.array_equal(sh, r0["shared"])
