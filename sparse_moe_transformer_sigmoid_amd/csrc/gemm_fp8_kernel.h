@@ -62,6 +62,34 @@ __device__ __forceinline__ v4f mfma_fp8(v8i a, v8i b) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 127, 0, 127);
 }
 
+// Eight e4m3 codes (two dwords, lowest byte first) -> eight bf16, exactly:
+// every e4m3 value, subnormals included, is a bf16 value.
+__device__ __forceinline__ v8bf e4m3x8_to_bf16(int lo, int hi) {
+  typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+  const v2bf a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.f, false);
+  const v2bf b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.f, true);
+  const v2bf c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.f, false);
+  const v2bf d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.f, true);
+  return v8bf{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// The same 16x16x128 e4m3 product as mfma_fp8, summed to fp32 precision:
+// gfx950's FP8 MFMA adds its 128 products at reduced precision (about 11% of
+// sums correctly rounded, errors up to 2^-15.6 of the sum of |products|, in
+// an in-bounds probe), while the bf16 MFMA on the exactly converted codes
+// rounds 99% of them correctly (worst 2^-24.9).  Instruction j takes bytes
+// 8j..8j+7 of every lane's 32-byte fragment: the same K indices in A and B,
+// so the four instructions cover each of the 128 products once.
+__device__ __forceinline__ v4f mfma_fp8_exact(v8i a, v8i b) {
+  v4f d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16(a[2 * j], a[2 * j + 1]),
+                                                e4m3x8_to_bf16(b[2 * j], b[2 * j + 1]), d,
+                                                0, 0, 0);
+  return d;
+}
+
 // Direct global -> LDS loads (global_load_lds_dword / _dwordx4): lane l's
 // 4 or 16 bytes from global [base + voff] land at LDS byte address
 // M0 + l * size.  Completion is tracked by vmcnt like any vector load, in
@@ -256,14 +284,18 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, v4f (&acc)[4][TT], f
 // ILV (BMODE 0): if nonzero, the issue order inside a scheduling group is
 // fixed: its LDS reads, two MFMAs, then each further MFMA after ILV VALU
 // instructions (the promotion FMAs of the MFMA two back).
+// EXACT (BMODE 0): each 128-wide block product is summed by mfma_fp8_exact
+// (twice the MFMA cycles), so the gate/up values the requantisation decides
+// on are correct to fp32 rounding; for launches that wait on HBM, not MFMA.
 template <bool GATEUP, int TT, int NBUF, bool NT, int BSETS = 2, int MINW = 1, int GRPX = 0,
-          int BMODE = 0, int ILV = 0>
+          int BMODE = 0, int ILV = 0, bool EXACT = false>
 __global__ __launch_bounds__(256, MINW) void gemm_fp8_kernel(const GemmArgs g) {
   static_assert(NBUF >= 2 && NBUF <= 4, "NBUF must be 2, 3 or 4");
   static_assert(BSETS == 1 || BSETS == 2, "BSETS must be 1 or 2");
   // BMODE 1 ends each step with a wait that counts the 8 weight loads of one
   // ring slot issued after the step's direct loads (one slot per step)
   static_assert(BMODE == 0 || (BMODE == 1 && NBUF == 2), "BMODE 1 needs NBUF 2");
+  static_assert(!EXACT || (BMODE == 0 && ILV == 0), "EXACT is implemented for BMODE 0 only");
   constexpr int BM = 16 * TT;
   constexpr int CPT = (TT * 128 + 255) / 256;   // 16-byte staging chunks per thread
   // LDS rows past the tile (TT < 2) are write-only padding: every thread
@@ -448,11 +480,15 @@ __global__ __launch_bounds__(256, MINW) void gemm_fp8_kernel(const GemmArgs g) {
         s0[u] = sa_t * swg;
         s1[u] = sa_t * swu;
       }
-      v4f prev = mfma_fp8(w[0], bf[0]);
+      auto mm = [](const v8i& a, const v8i& b) {
+        if constexpr (EXACT) return mfma_fp8_exact(a, b);
+        else return mfma_fp8(a, b);
+      };
+      v4f prev = mm(w[0], bf[0]);
 #pragma unroll
       for (int i = 1; i < 4 * GRP; ++i) {
         const int u = i >> 2, rt = i & 3;
-        const v4f cur = mfma_fp8(w[rt], bf[u]);
+        const v4f cur = mm(w[rt], bf[u]);
         const int pu = (i - 1) >> 2, pr = (i - 1) & 3;
         acc[pr][t0 + pu] += prev * (pr < 2 ? s0[pu] : s1[pu]);
         prev = cur;
