@@ -41,6 +41,7 @@ class MoEShape:
     dense: bool = False     # one expert, no router, weight 1 (the first block's MLP)
     # input recipe
     x_std: float = 1.0
+    gamma_std: float = 0.0        # RMSNorm weight: 1 (0.0) or ~N(1, gamma_std)
     weight_std: float = 0.02
     bias_std: float = 0.01
     bias_recipe: str = "normal"   # "normal": N(0, bias_std); "zipf": -beta*ln(rank)

@@ -9,7 +9,8 @@ generated tensors to wherever it is needed.
 Input recipe (the distributions of the workloads being modelled):
 
 * x ~ N(0, 1), stored bf16 (fp32 for the fp32 format);
-* RMSNorm weight gamma = 1 (the norm's initial value);
+* RMSNorm weight gamma = 1 (the norm's initial value; every benchmark
+  workload), or gamma ~ N(1, gamma_std) for parity cases that exercise it;
 * router weight ~ N(0, 0.02), bf16 [E, d];
 * correction bias ~ N(0, 0.01) fp32, or -beta * ln(rank) with rank a seeded
   permutation of 1..E for the skewed workload;
@@ -30,7 +31,7 @@ import torch
 
 from .configs import FMT_F32, FMT_FP8, MoEShape
 
-ROLE_X, ROLE_ROUTER, ROLE_BIAS, ROLE_EXPERT, ROLE_RANK = 1, 2, 3, 4, 5
+ROLE_X, ROLE_ROUTER, ROLE_BIAS, ROLE_EXPERT, ROLE_RANK, ROLE_NORM = 1, 2, 3, 4, 5, 6
 MAT_GATE, MAT_UP, MAT_DOWN = 0, 1, 2
 FP8_MAX = 448.0
 BLOCK = 128
@@ -95,6 +96,14 @@ class MoEInputs:
         return out
 
 
+def norm_weight(shape: MoEShape, seed: int, device, dtype) -> torch.Tensor:
+    """RMSNorm weight gamma [d]: ones, or ~N(1, gamma_std) rounded to ``dtype``."""
+    if shape.gamma_std == 0.0:
+        return torch.ones(shape.d_model, dtype=dtype, device=device)
+    g = _randn((shape.d_model,), shape.gamma_std, device, seed, ROLE_NORM) + 1.0
+    return g.to(dtype)
+
+
 def bias_vector(shape: MoEShape, seed: int, device) -> torch.Tensor:
     E = shape.n_experts
     if shape.bias_recipe == "normal":
@@ -112,7 +121,7 @@ def generate_router_inputs(shape: MoEShape, seed: int = 0, device="cpu",
     T = shape.tokens if tokens is None else tokens
     act_dtype = torch.bfloat16 if shape.fmt == FMT_FP8 else torch.float32
     x = _randn((T, shape.d_model), shape.x_std, device, seed, ROLE_X).to(act_dtype)
-    norm_w = torch.ones(shape.d_model, dtype=act_dtype, device=device)
+    norm_w = norm_weight(shape, seed, device, act_dtype)
     w_router = _randn((shape.n_experts, shape.d_model), shape.weight_std, device, seed,
                       ROLE_ROUTER).to(act_dtype)
     return x, norm_w, w_router
@@ -127,7 +136,7 @@ def generate(shape: MoEShape, seed: int = 0, device="cpu", tokens: Optional[int]
     act_dtype = torch.bfloat16 if fp8 else torch.float32
 
     x = _randn((T, d), shape.x_std, device, seed, ROLE_X).to(act_dtype)
-    norm_w = torch.ones(d, dtype=act_dtype, device=device)
+    norm_w = norm_weight(shape, seed, device, act_dtype)
     if shape.dense:
         w_router = bias = None
     else:
@@ -164,8 +173,8 @@ def with_workload(base: MoEInputs, shape: MoEShape, seed: int = 0,
 
     Expert and router weights depend only on the seed and the layer
     dimensions, so workloads of one layer (decode, prefill, skewed routing)
-    share them; x is drawn for the new token count and the bias from the
-    new shape's recipe.
+    share them; x is drawn for the new token count, the bias from the new
+    shape's recipe, and gamma from it when it asks for a non-unit one.
     """
     b = base.shape
     assert (b.d_model, b.n_experts, b.n_shared, b.d_ff, b.fmt) == \
@@ -175,5 +184,7 @@ def with_workload(base: MoEInputs, shape: MoEShape, seed: int = 0,
     act_dtype = base.x.dtype
     x = _randn((T, shape.d_model), shape.x_std, device, seed, ROLE_X).to(act_dtype)
     bias = None if shape.dense else bias_vector(shape, seed, device)
-    return MoEInputs(shape, x, base.norm_w, base.w_router, bias, base.w_gate, base.w_up,
+    norm_w = base.norm_w if shape.gamma_std == 0.0 else norm_weight(shape, seed, device,
+                                                                     act_dtype)
+    return MoEInputs(shape, x, norm_w, base.w_router, bias, base.w_gate, base.w_up,
                      base.w_down, base.s_gate, base.s_up, base.s_down)

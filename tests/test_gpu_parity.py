@@ -3,8 +3,11 @@
 Small shapes are compared on every token; the Kimi K2 shapes (decode 64,
 prefill 8192, skewed 16384, dense 4096 tokens) are run whole on the GPU in
 the launch configuration the benchmark times, and compared on every token's
-routing and permutation and on the outputs of sampled tokens, which the
-oracle computes one expert at a time.
+routing and permutation, on every row of chosen experts (the hottest, a
+median one, one with fewer than 16 rows), on shared-expert rows spread over
+every m-tile and tile position, and on y and out of sampled tokens (all 64
+at decode); the oracle computes one expert at a time.  The exact oracle is
+the only reference: nothing the GPU computes is fed back into it.
 """
 import os
 
@@ -16,7 +19,6 @@ import synth
 from oracle import moe_ref as R
 from oracle.adapt import run_oracle, to_f32
 from oracle.compare import MEAN_REL, assert_close, check_routing, close_report
-from oracle.fp8 import bf16_round
 
 pytestmark = pytest.mark.gpu
 
@@ -61,63 +63,147 @@ def _gather(t, idx):
     return t[torch.from_numpy(np.asarray(idx).reshape(-1)).to(t.device).long()].cpu().numpy()
 
 
-def check_requantised_codes(gpu_codes, gpu_scales, a_ref):
-    """GPU SwiGLU codes against the oracle's exact quantisation of its own a.
+def _host(inp):
+    """x and gamma as host fp32 (exact values of the bf16 inputs), cached on inp."""
+    if not hasattr(inp, "_host_xg"):
+        inp._host_xg = (to_f32(inp.x), to_f32(inp.norm_w))
+    return inp._host_xg
 
-    The codes are decided on fp32 values whose sums gfx950's FP8 MFMA forms at
-    reduced precision (about 2^-16 of the sum of |products|).  A GPU code is
-    accepted when its value is within one e4m3 step of the exact code's value,
-    or within 1e-4 of the block maximum (values near zero, where cancellation
-    makes the relative error large); at least 99% must be identical.
-    """
+
+def check_codes(gpu_codes, gpu_scales, a_ref):
+    """The GPU's requantised SwiGLU activations against the oracle's
+    quantisation of its own exact a (both outputs, nothing fed back): at
+    least 99% of the codes identical, every other one a neighbouring e4m3
+    value (a rounding decision on an fp32 value near the midpoint between
+    two codes), scales within 1e-3.  Returns the fraction that differ."""
     I = a_ref.shape[-1]
     codes, scales = R.quantize_1x128(a_ref.reshape(-1, I))
     gc = gpu_codes.reshape(codes.shape)
     gs = gpu_scales.reshape(scales.shape)
-    same = float(np.mean(gc == codes))
-    dq_g = R.dequantize_1x128(gc, scales)      # both codes in the oracle's scale;
-    dq_r = R.dequantize_1x128(codes, scales)   # the scales are compared on their own
+    diff = gc != codes
+    dq_g = R.dequantize_1x128(gc, scales)      # both in the oracle's scale
+    dq_r = R.dequantize_1x128(codes, scales)
     amax = np.repeat(scales.astype(np.float64) * 448.0, 128, axis=1)
-    step = np.abs(dq_r) * 2.0 ** -3
+    step = np.abs(dq_r) * 2.0 ** -3            # one e4m3 step (3 mantissa bits)
     excess = np.abs(dq_g - dq_r) - np.maximum(step, 1e-4 * amax)
-    srel = float(np.max(np.abs(gs.astype(np.float64) / scales - 1.0)))
-    _log(f"  swiglu codes: equal {same:.5f}, worst excess {excess.max():.2e}, "
+    srel = float(np.max(np.abs(gs.astype(np.float64) / scales - 1.0))) if scales.size else 0.0
+    frac = float(diff.mean()) if diff.size else 0.0
+    _log(f"  requantised codes differing from the oracle's: {int(diff.sum())} of {diff.size} "
+         f"({frac:.2e}); worst excess over one step {excess.max() if excess.size else 0:.2e}; "
          f"scale rel diff {srel:.2e}")
-    assert same >= 0.99 and excess.max() <= 0 and srel <= 1e-3
+    assert frac <= 0.01 and (excess.size == 0 or excess.max() <= 0) and srel <= 1e-3
+    return frac
 
 
-def check_layer(inp, g, tokens=None, end_to_end=None):
-    """Compare a gpu_chain result with the oracle on ``tokens`` (default all).
+def row_rel_l2(gpu, ref):
+    """Per-row relative L2 error ||gpu - ref|| / ||ref|| of [n, d] arrays."""
+    g = np.asarray(gpu, np.float64).reshape(-1, gpu.shape[-1])
+    r = np.asarray(ref, np.float64).reshape(-1, ref.shape[-1])
+    num = np.sqrt(np.sum((g - r) ** 2, axis=1))
+    den = np.sqrt(np.sum(r * r, axis=1))
+    return num / np.maximum(den, 1e-30)
 
-    Routing and the permutation are checked on every token.  Expert outputs
-    of the compared tokens are evaluated by the oracle under the GPU's expert
-    choice and, in the FP8 layer, on the GPU's requantised SwiGLU codes (each
-    checked to be the exact code or one step from it); those are held to the
-    output tolerance.  With end_to_end (default: d_ff >= 2048) the oracle's
-    own exact path must also meet the output tolerance.
+
+# per-row relative L2 error allowed on expert rows and the shared expert's
+# output (intermediates before the combine); a wrong tile, scale or row
+# gives O(1)
+ROW_L2 = 2e-2
+
+# The output tolerance (max-abs <= 2e-2 RMS, mean-rel <= 5e-3 against the exact
+# oracle) is asserted on y and out whenever the gate/up launch sums its block
+# products exactly (the instances of up to 64-row tiles: mean rows per expert <= 48,
+# the host's rule for the tile width) and at the K2 dimensions.  The 128-row
+# instance sums with the FP8 MFMA, whose reduced-precision addition puts about 0.5%
+# of the requantised SwiGLU codes one e4m3 step from the exact ones; on the small
+# shapes a single such code moves a top-1..3 token's y by 2-11% of RMS, so there
+# only the mean-relative part is asserted, with the per-row and code checks below.
+def full_gate(shape, T):
+    if shape.fmt != "fp8" or shape.d_model == 7168:
+        return True
+    mean_rows = T if shape.dense else T * shape.top_k / shape.n_experts
+    return mean_rows <= 48
+
+
+def intermediate_check(gpu, ref, what, full):
+    """Expert rows / shared output: mean-rel asserted; per-row relative L2
+    asserted (when ``full``); max-abs reported.  A requantisation near-tie
+    moves one row by one e4m3 step of one activation, well under ROW_L2 of
+    the row's norm; a wrong tile, scale or row moves it by O(1)."""
+    rep = close_report(gpu, ref)
+    l2 = float(row_rel_l2(gpu, ref).max()) if np.asarray(ref).size else 0.0
+    _log(f"  {what}: max_abs/rms {rep['max_abs'] / max(rep['rms'], 1e-30):.3e} "
+         f"mean_rel {rep['mean_rel']:.3e} worst row rel L2 {l2:.3e}")
+    assert rep["finite"] and rep["mean_rel"] <= MEAN_REL, f"{what}: {rep}"
+    if full:
+        assert l2 <= ROW_L2, f"{what}: worst row relative L2 error {l2:.3e}"
+    return rep
+
+
+def check_expert_rows(inp, g, e, agree, what):
+    """Every row of expert e (the shared expert when e == n_experts) against
+    the oracle's expert alone on the same tokens.  Routed experts: the rows
+    the GPU permutation gives e, of tokens whose expert set is the oracle's
+    (agree: bool [T]).  Shared expert: agree is the token list itself."""
+    shape = inp.shape
+    k, E = shape.top_k, shape.n_experts
+    p = R.params_from_shape(shape)
+    x, gamma = _host(inp)
+    if e == E:
+        toks = np.asarray(agree, dtype=np.int64)
+        gpu = _gather(g["shared"], toks)
+    else:
+        lo, hi = int(g["offsets"][e]), int(g["offsets"][e + 1])
+        toks = g["row_pair"][lo:hi] // k
+        keep = agree[toks]
+        toks = toks[keep]
+        gpu = _gather(g["rows"], np.arange(lo, hi)[keep])
+    ref = R.expert_rows(p, x, gamma, inp.expert_numpy(e), toks)
+    return intermediate_check(gpu, ref, f"{what}: expert {e}, {len(toks)} rows", True)
+
+
+def strided_rows(n, tile=128, count=128):
+    """Row indices of [0, n) that land in every m-tile of `tile` rows and in
+    every position inside a tile (stride 37, coprime with 128), plus both ends."""
+    ntiles = max(1, (n + tile - 1) // tile)
+    rows = [(i % ntiles) * tile + (i * 37) % tile for i in range(max(count, ntiles))]
+    return np.unique(np.array([r for r in rows if r < n] + [0, n - 1], dtype=np.int64))
+
+
+def pick_experts(offsets, n_experts):
+    """The hottest expert, one of median load and the fullest one under 16 rows."""
+    counts = np.diff(offsets)[:n_experts]
+    order = np.argsort(counts, kind="stable")
+    nz = order[counts[order] > 0]
+    small = [int(e) for e in nz if counts[e] < 16]
+    out = [int(order[-1]), int(nz[len(nz) // 2])] + small[-1:]
+    return list(dict.fromkeys(out))
+
+
+def check_layer(inp, g, tokens=None, experts=(), shared_tokens=None):
+    """Compare a gpu_chain result with the oracle.
+
+    Routing and the permutation are checked on every token.  Expert rows,
+    the shared expert's output, y and out are compared on ``tokens``
+    (default: all) against the oracle's own evaluation of the layer, for
+    every token whose expert set is the oracle's; a near-tie token with
+    another valid set has no unique output and is counted, not compared.
+    ``experts``: routed experts compared on all their rows; ``shared_tokens``:
+    tokens on which the shared expert's output is compared as well.
     """
     shape = inp.shape
-    k, I = shape.top_k, shape.d_ff
+    k, d = shape.top_k, shape.d_model
     fp8 = shape.fmt == "fp8"
     T = inp.x.shape[0]
-    P = T * k
     sel = np.arange(T) if tokens is None else np.asarray(tokens)
-    if end_to_end is None:
-        end_to_end = I >= 2048
-    pidx = g["pair_row"].reshape(T, k)[sel]                        # [n, k] permuted rows
-    ov = None
-    if fp8:
-        ov = dict(codes=_gather(g["act_q"], pidx).reshape(len(sel), k, I),
-                  scales=_gather(g["act_s"], pidx).reshape(len(sel), k, -1))
-        if shape.n_shared:
-            ov["shared_codes"] = _gather(g["act_q"], P + sel)
-            ov["shared_scales"] = _gather(g["act_s"], P + sel)
-    ref = run_oracle(inp, tokens=sel, ids_override=g["ids"], act_override=ov)
+    ref = run_oracle(inp, tokens=sel)
     if not shape.dense:
-        rep = check_routing(g["ids"], g["w"], ref)
-        _log(f"  routing: {rep}")
+        rt = check_routing(g["ids"], g["w"], ref)
+        agree = rt["agree"]
+        _log(f"  routing: tokens {rt['tokens']}, flagged {rt['flagged']}, "
+             f"flagged with another valid set {rt['differing_flagged']}")
     else:
         assert np.all(g["ids"] == 0) and np.all(g["w"] == np.float32(shape.routed_scaling))
+        agree = np.ones(T, dtype=bool)
     # permutation: bit-exact against the oracle's grouping of the GPU's ids
     off, rp, pr = R.permute(g["ids"], shape.n_experts)
     assert np.array_equal(g["offsets"], off)
@@ -125,30 +211,39 @@ def check_layer(inp, g, tokens=None, end_to_end=None):
     assert np.array_equal(g["pair_row"], pr)
     # fused forward is the unfused chain, bit for bit
     assert np.array_equal(g["out_f"].view(np.uint32), g["out_u"].view(np.uint32))
-    rows = _gather(g["rows"], pidx).reshape(len(sel), k, -1)
-    sh = _gather(g["shared"], sel) if shape.n_shared else None
     if fp8:
         assert np.array_equal(g["xs"][sel], ref["xs"]), "activation scales differ"
-        xq_eq = np.mean(g["xq"][sel] == ref["xq"])
-        assert xq_eq >= 0.9999, f"activation codes equal on {xq_eq:.6f}"
-        check_requantised_codes(ov["codes"], ov["scales"], ref["a_pairs"])
-        sfx = "_ov"
+        nq = int(np.sum(g["xq"][sel] != ref["xq"]))
+        assert nq == 0, f"activation codes differ in {nq} places"
     else:
         assert_close(g["xq"][sel], ref["h"][sel], "h")
-        sfx = ""
-    rep_rows = assert_close(rows, ref["o_pairs" + sfx], "expert rows")
-    if shape.n_shared:
-        assert_close(sh, ref["shared" + sfx], "shared expert")
-    rep_y = assert_close(g["y"][sel], ref["y" + sfx], "y (MoE output)")
-    rep_o = assert_close(g["out_f"][sel], ref["out" + sfx], "out", bf16_out=fp8)
-    _log(f"  rows {rep_rows}\n  y {rep_y}\n  out {rep_o}")
+    keep = agree[sel]
+    s2 = sel[keep]
+    full = full_gate(shape, T)
+    _log(f"  tokens compared {len(s2)} of {len(sel)}; full output gate {full}")
+    pidx = g["pair_row"].reshape(T, k)[s2]
+    rows = _gather(g["rows"], pidx).reshape(len(s2), k, d)
     if fp8:
-        e2e_y = close_report(g["y"][sel], ref["y"])
-        e2e_o = close_report(g["out_f"][sel], ref["out"], bf16_out=True)
-        _log(f"  end to end vs exact oracle: y {e2e_y}\n  out {e2e_o}")
-        assert e2e_y["mean_rel"] <= MEAN_REL and e2e_o["mean_rel"] <= MEAN_REL
-        if end_to_end:
-            assert e2e_y["ok"] and e2e_o["ok"], "end-to-end tolerance"
+        P_rows = len(s2) * k
+        codes = _gather(g["act_q"], pidx).reshape(P_rows, -1)
+        scales = _gather(g["act_s"], pidx).reshape(P_rows, -1)
+        check_codes(codes, scales, ref["a_pairs"][keep])
+    intermediate_check(rows, ref["o_pairs"][keep], "expert rows", full)
+    if shape.n_shared:
+        intermediate_check(_gather(g["shared"], s2), ref["shared"][keep], "shared expert", full)
+    for name, gv, rv, b16 in (("y", g["y"][s2], ref["y"][keep], False),
+                              ("out", g["out_f"][s2], ref["out"][keep], fp8)):
+        rep = close_report(gv, rv, bf16_out=b16)
+        _log(f"  {name}: max_abs/rms {rep['max_abs'] / max(rep['rms'], 1e-30):.3e} "
+             f"mean_rel {rep['mean_rel']:.3e} ok {rep['ok']}")
+        if full:
+            assert rep["ok"], f"{name} outside the output tolerance: {rep}"
+        else:
+            assert rep["finite"] and rep["mean_rel"] <= MEAN_REL, f"{name}: {rep}"
+    for e in experts:
+        check_expert_rows(inp, g, int(e), agree, "whole expert")
+    if shared_tokens is not None and shape.n_shared:
+        check_expert_rows(inp, g, shape.n_experts, shared_tokens, "shared expert rows")
     return ref
 
 
@@ -160,6 +255,15 @@ def _layer(inp):
 # ------------------------------------------------------------- small shapes
 def test_tiny_fp32_layer():
     inp = synth.generate(synth.TINY, seed=0, device="cuda")
+    g = gpu_chain(_layer(inp), inp)
+    check_layer(inp, g)
+
+
+def test_tiny_fp32_layer_random_gamma():
+    """RMSNorm weight gamma ~ N(1, 0.1): the kernel's gamma load and product."""
+    from dataclasses import replace
+    inp = synth.generate(replace(synth.TINY, gamma_std=0.1), seed=1, device="cuda")
+    assert float(inp.norm_w.float().std()) > 0.05
     g = gpu_chain(_layer(inp), inp)
     check_layer(inp, g)
 
@@ -199,11 +303,40 @@ MIXED = [
 ]
 
 
-@pytest.mark.parametrize("T,d,E,S,k,I,seed", SMALL + MIXED)
+# The same kinds of shape with d_ff >= 2048 (down K of 16, 17 and 18 blocks), where
+# the full output gate applies.
+SMALL_WIDE = [
+    (1, 256, 16, 1, 2, 2048, 30),
+    (37, 256, 16, 1, 4, 2048, 31),
+    (200, 256, 16, 1, 2, 2176, 33),
+    (300, 256, 16, 1, 3, 2304, 34),
+    (700, 512, 16, 1, 2, 2048, 35),
+    (900, 256, 16, 1, 2, 2176, 36),
+    (2000, 256, 16, 0, 1, 2048, 39),
+    (777, 768, 64, 0, 8, 2176, 41),
+    (129, 256, 32, 0, 7, 2304, 42),
+    (511, 512, 64, 1, 3, 2048, 43),
+    (1500, 256, 32, 0, 5, 2176, 44),
+    (7, 256, 32, 1, 5, 2304, 45),
+]
+
+
+@pytest.mark.parametrize("T,d,E,S,k,I,seed", SMALL + MIXED + SMALL_WIDE)
 def test_small_fp8_layer(T, d, E, S, k, I, seed):
     _log(f"small fp8 T={T} d={d} E={E} S={S} k={k} I={I}")
     shape = synth.small_fp8(tokens=T, d_model=d, n_experts=E, n_shared=S, top_k=k, d_ff=I)
     inp = synth.generate(shape, seed=seed, device="cuda")
+    g = gpu_chain(_layer(inp), inp)
+    check_layer(inp, g)
+
+
+def test_small_fp8_layer_random_gamma():
+    """A bf16 gamma ~ N(1, 0.1) through the FP8 layer: h and its codes stay
+    bit-exact, outputs within the tolerance."""
+    shape = synth.small_fp8(tokens=300, d_model=512, n_experts=32, n_shared=1, top_k=4,
+                            d_ff=2048, gamma_std=0.1)
+    inp = synth.generate(shape, seed=21, device="cuda")
+    assert float(inp.norm_w.float().std()) > 0.05
     g = gpu_chain(_layer(inp), inp)
     check_layer(inp, g)
 
@@ -220,13 +353,13 @@ def test_small_fp8_largest_k(T, d, I, seed):
     check_layer(inp, g)
 
 
-@pytest.mark.parametrize("T", [333, 800])
-def test_small_fp8_one_hot_expert_spans_many_tiles(T):
+@pytest.mark.parametrize("T,I", [(333, 256), (800, 256), (800, 2048)])
+def test_small_fp8_one_hot_expert_spans_many_tiles(T, I):
     # a large bias forces every token onto experts 3 and 11: m = T rows each,
     # several m-tiles per expert and the other experts empty (64- and 128-row
     # tiles)
     i, j = 3, 11
-    shape = synth.small_fp8(tokens=T, n_experts=16, top_k=2, d_ff=256)
+    shape = synth.small_fp8(tokens=T, n_experts=16, top_k=2, d_ff=I)
     inp = synth.generate(shape, seed=7, device="cuda")
     inp.bias[i] = 5.0
     inp.bias[j] = 5.0
@@ -235,10 +368,11 @@ def test_small_fp8_one_hot_expert_spans_many_tiles(T):
     check_layer(inp, g)
 
 
-@pytest.mark.parametrize("T", [150, 40])   # 40 tokens: the one-workgroup permutation path
-def test_small_dense_ffn(T):
+# 40 tokens: the one-workgroup permutation path
+@pytest.mark.parametrize("T,I", [(150, 384), (40, 384), (150, 2304)])
+def test_small_dense_ffn(T, I):
     shape = synth.MoEShape("dense_small", tokens=T, d_model=256, n_experts=1, n_shared=0,
-                           top_k=1, d_ff=384, fmt="fp8", routed_scaling=1.0, dense=True)
+                           top_k=1, d_ff=I, fmt="fp8", routed_scaling=1.0, dense=True)
     inp = synth.generate(shape, seed=8, device="cuda")
     g = gpu_chain(_layer(inp), inp)
     check_layer(inp, g)
@@ -253,7 +387,7 @@ def test_quantiser_codes_over_wide_range():
     inp.x = (inp.x.float() * scale).to(torch.bfloat16)
     inp.x[5, :128] = 0               # an all-zero 1x128 block in one token
     g = gpu_chain(_layer(inp), inp)
-    ref = run_oracle(inp, tokens=np.arange(96), ids_override=g["ids"])
+    ref = run_oracle(inp, tokens=np.arange(96))
     assert np.array_equal(g["xs"], ref["xs"])
     assert np.array_equal(g["xq"], ref["xq"])
 
@@ -286,11 +420,22 @@ def _sample(T, n, seed=0):
 
 
 def test_k2_decode(k2):
+    """The 64-token decode batch, every token compared."""
     base, layer = k2
     inp = base
     g = gpu_chain(layer, inp)
     _log(f"decode: touched experts {int(np.sum(np.diff(g['offsets']) > 0))}")
-    check_layer(inp, g, tokens=_sample(64, 8))
+    check_layer(inp, g)
+
+
+def test_k2_decode_random_gamma(k2):
+    """Decode shape with a bf16 RMSNorm weight gamma ~ N(1, 0.1)."""
+    from dataclasses import replace
+    base, layer = k2
+    inp = synth.with_workload(base, replace(synth.K2_DECODE, gamma_std=0.1), seed=7)
+    assert float(inp.norm_w.float().std()) > 0.05
+    g = gpu_chain(layer, inp)
+    check_layer(inp, g, tokens=_sample(64, 16, seed=7))
 
 
 def test_k2_prefill(k2):
@@ -299,7 +444,8 @@ def test_k2_prefill(k2):
     g = gpu_chain(layer, inp)
     counts = np.diff(g["offsets"])
     _log(f"prefill: tokens per expert min {counts.min()} max {counts.max()}")
-    check_layer(inp, g, tokens=_sample(8192, 4, seed=1))
+    check_layer(inp, g, tokens=_sample(8192, 4, seed=1),
+                experts=pick_experts(g["offsets"], 384), shared_tokens=strided_rows(8192))
     a = layer.forward(inp.x).clone()
     torch.cuda.synchronize()
     assert np.array_equal(to_f32(a).view(np.uint32), g["out_f"].view(np.uint32))
@@ -315,7 +461,8 @@ def test_k2_skewed(k2):
          f"{int(np.sum(counts < 10))}, empty {int(np.sum(counts == 0))}")
     hot_tok = int(g["row_pair"][g["offsets"][hot]] // 8)
     toks = np.unique(np.concatenate([_sample(16384, 3, seed=2), [hot_tok]]))
-    check_layer(inp, g, tokens=toks)
+    check_layer(inp, g, tokens=toks, experts=pick_experts(g["offsets"], 384),
+                shared_tokens=strided_rows(16384))
 
 
 @pytest.mark.parametrize("T", [1, 5, 257, 700, 1000, 2000, 3000, 5000])
@@ -395,7 +542,8 @@ def test_k2_ep8_shard():
     g = gpu_chain(layer, inp)
     counts = np.diff(g["offsets"])
     _log(f"ep8 shard: rows per expert min {counts.min()} max {counts.max()}")
-    check_layer(inp, g, tokens=_sample(8192, 3, seed=4))
+    check_layer(inp, g, tokens=_sample(8192, 3, seed=4), experts=pick_experts(g["offsets"], 48),
+                shared_tokens=strided_rows(8192))
     del layer
 
 
@@ -403,5 +551,5 @@ def test_k2_dense_ffn():
     inp = synth.generate(synth.K2_DENSE, seed=0, device="cuda")
     layer = _layer(inp)
     g = gpu_chain(layer, inp)
-    check_layer(inp, g, tokens=_sample(4096, 3, seed=3))
+    check_layer(inp, g, tokens=strided_rows(4096))
     del layer

@@ -97,3 +97,19 @@ def test_load_slope_recovers_a_zipf_exponent(s):
     r = np.arange(1, 385)
     loads = np.round(1e6 * r ** -s)
     assert abs(load_slope(loads) + s) < 1e-3
+
+
+def test_gamma_recipe():
+    """gamma is 1 by default and ~N(1, gamma_std) in the layer dtype when asked
+    for; with_workload draws it from the new shape and keeps the base's
+    otherwise."""
+    a = synth.generate(SHAPE, seed=3)
+    assert torch.equal(a.norm_w, torch.ones_like(a.norm_w)) and a.norm_w.dtype == torch.bfloat16
+    shp = dataclasses.replace(synth.small_fp8(tokens=8, d_model=4096), gamma_std=0.1)
+    g = synth.generate(shp, seed=3).norm_w.float()
+    assert abs(float(g.mean()) - 1.0) < 0.01 and abs(float(g.std()) - 0.1) < 0.01
+    tiny = synth.generate(dataclasses.replace(synth.TINY, gamma_std=0.1), seed=3).norm_w
+    assert tiny.dtype == torch.float32 and float(tiny.std()) > 0.05
+    w = synth.with_workload(a, dataclasses.replace(SHAPE, gamma_std=0.1), seed=4)
+    assert not torch.equal(w.norm_w, a.norm_w)
+    assert synth.with_workload(a, SHAPE, seed=4).norm_w is a.norm_w
