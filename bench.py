@@ -12,9 +12,11 @@ synthetic tensors already resident in HBM; weights are random-init FP8 with
 Prints one JSON line: tokens/s for the named workload (default: the 64-token
 decode step, its timed steps replayed from a HIP graph of moe_forward; --eager
 times plain launches), the dominant kernel's roofline fraction measured with
-HIP events inside an eager timed region, the same for the 8192-token prefill,
-the shader clock the driver reports while each runs (sampled from sysfs
-after the timed steps), and the CPU oracle timed on a bounded sample of the same workload.
+HIP events inside an eager timed region, the whole layer's compulsory bytes
+over the step time, the same for the 8192-token prefill, the 16384-token
+skewed-routing step and the 4096-token dense FFN, the shader clock the driver
+reports while decode and prefill run (sampled from sysfs after the timed
+steps), and the CPU oracle timed on the whole decode batch.
 """
 from __future__ import annotations
 
@@ -74,11 +76,14 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode",
                     choices=["decode", "prefill", "skewed", "dense", "ep8_shard"])
-    ap.add_argument("--no-secondary", action="store_true", help="skip the prefill line")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the prefill, skewed-routing and dense-FFN lines")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true",
                     help="time decode with eager launches instead of a HIP graph")
-    ap.add_argument("--cpu-tokens", type=int, default=16)
+    ap.add_argument("--cpu-tokens", type=int, default=64,
+                    help="tokens of the decode batch the CPU oracle is timed on")
+    ap.add_argument("--cpu-runs", type=int, default=3)
     ap.add_argument("--no-clock", action="store_true",
                     help="skip the shader-clock sample (sysfs) after the timed steps")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -148,6 +153,16 @@ def routing_stats(layer, x):
     return int(np.sum(counts > 0)), counts
 
 
+def layer_bytes(shape, T, touched_all):
+    """Compulsory HBM bytes of one forward: the FP8 codes and scales of every
+    touched expert (the shared one included), the bf16 router and the fp32
+    bias, gamma, x read once and out written once."""
+    d, I = shape.d_model, shape.d_ff
+    expert = 3 * I * d + 3 * (I // 128) * (d // 128) * 4
+    router = 0 if shape.dense else shape.n_experts * d * 2 + shape.n_experts * 4
+    return touched_all * expert + router + d * 2 + 2 * T * d * 2
+
+
 def run_workload(layer, inp, steps, warmup, graph=False):
     shape = inp.shape
     T = inp.x.shape[0]
@@ -167,10 +182,34 @@ def run_workload(layer, inp, steps, warmup, graph=False):
     gu_flops = 2.0 * rows * (2 * I) * d
     dn_flops = 2.0 * rows * I * d
     gu_s = stage["gateup"] * 1e-3
+    lb = layer_bytes(shape, T, touched_all)
     return dict(T=T, ms=ms, eager_ms=eager_ms, stage=stage, touched=touched_all, counts=counts,
                 gu_bytes=gu_bytes, gu_flops=gu_flops, total_flops=gu_flops + dn_flops,
+                layer_bytes=lb, layer_gbs=lb / (ms * 1e-3) / 1e9,
                 gu_gbs=gu_bytes / gu_s / 1e9 if gu_s > 0 else 0.0,
                 gu_tflops=gu_flops / gu_s / 1e12 if gu_s > 0 else 0.0)
+
+
+def secondary_line(r, workload, sclk=None):
+    """Summary of one more workload's run (prefill, skewed routing, dense FFN)."""
+    tfl = r["total_flops"] / (r["ms"] * 1e-3) / 1e12
+    return {
+        "workload": workload, "tokens": r["T"], "value": r["T"] / (r["ms"] * 1e-3),
+        "unit": "tokens/s", "ms_per_step": r["ms"], "touched_experts": r["touched"],
+        "fp8_tflops_layer": tfl, "frac_fp8_peak_layer": tfl / FP8_PEAK_TFLOPS,
+        "layer_bytes": r["layer_bytes"], "layer_gbs": r["layer_gbs"],
+        "layer_frac_hbm": r["layer_gbs"] / HBM_PEAK_GBS,
+        "gateup_ms": r["stage"]["gateup"],
+        "gateup_tflops": r["gu_tflops"], "gateup_frac_fp8_peak": r["gu_tflops"] / FP8_PEAK_TFLOPS,
+        "gateup_gbs": r["gu_gbs"], "gateup_frac_hbm_peak": r["gu_gbs"] / HBM_PEAK_GBS,
+        "gateup_arithmetic_intensity": r["gu_flops"] / r["gu_bytes"],
+        "gateup_traffic": measured_traffic(workload),
+        "gateup_mfma_counters": measured_mfma(workload),
+        "sclk_mhz": sclk,
+        # the published FP8 peak assumes 2400 MHz; at the measured clock:
+        "gateup_frac_fp8_peak_at_sclk":
+            r["gu_tflops"] / (FP8_PEAK_TFLOPS * sclk / 2400.0) if sclk else None,
+        "stage_ms": r["stage"]}
 
 
 def sclk_file():
@@ -224,13 +263,17 @@ def sclk_during(layer, x, seconds=1.5):
     return int(statistics.median(vals)) if vals else None
 
 
-def cpu_baseline(inp, n_tokens):
-    """The oracle on the host cores: routing of the batch, experts of n tokens."""
+def cpu_baseline(inp, n_tokens, runs=3):
+    """The oracle on the host cores, end to end on the first n_tokens of the
+    batch (routing of the batch, every expert those tokens use): median of
+    `runs` runs, one run if the first takes over 60 s."""
+    import statistics
+
     import numpy as np
     from threadpoolctl import threadpool_info
 
     from oracle.adapt import to_f32
-    from oracle.moe_ref import moe_layer, params_from_shape
+    from oracle.moe_ref import moe_layer, params_from_shape, rmsnorm, route
 
     p = params_from_shape(inp.shape)
     T = inp.x.shape[0]
@@ -239,8 +282,8 @@ def cpu_baseline(inp, n_tokens):
     norm_w = to_f32(inp.norm_w)
     wr = None if inp.w_router is None else to_f32(inp.w_router)
     bias = None if inp.bias is None else to_f32(inp.bias)
-    # host copies of every expert the sample needs, made before the clock starts
-    from oracle.moe_ref import rmsnorm, route
+    # host copies of every expert the sample needs (the FP8 codes and scales as
+    # they sit in memory), made before the clock starts
     h = rmsnorm(x[sel], norm_w, p.rms_eps, round_bf16=p.fp8)
     need = set(range(p.n_experts, p.n_experts + p.n_shared))
     if p.dense:
@@ -252,14 +295,23 @@ def cpu_baseline(inp, n_tokens):
     for e in need:
         cache[e] = {n: (None if getattr(inp, n) is None else getattr(inp, n)[e].cpu().numpy())
                     for n in ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down")}
-    t0 = time.perf_counter()
-    moe_layer(p, x, norm_w, wr, bias, lambda e: cache[e], tokens=sel)
-    dt = time.perf_counter() - t0
+    times = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        moe_layer(p, x, norm_w, wr, bias, lambda e: cache[e], tokens=sel)
+        times.append(time.perf_counter() - t0)
+        if times[0] > 60.0:
+            break
+    dt = statistics.median(times)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    whole = len(sel) == T
+    what = (f"the whole {T}-token {inp.shape.name} batch" if whole else
+            f"the first {len(sel)} of {T} tokens of the {inp.shape.name} batch")
     return {"value": len(sel) / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {len(sel)} of {T} tokens of the {inp.shape.name} batch: routing of "
-                      f"the batch and the experts of the sampled tokens, {dt:.1f} s on "
-                      f"{os.cpu_count()} host cores (BLAS threads {threads})"}
+            "sample": f"{what}: routing, every touched expert dequantised and applied, combine; "
+                      f"median of {len(times)} run(s) ({', '.join(f'{t:.1f}' for t in times)} s) "
+                      f"on {os.cpu_count()} host cores, BLAS threads {threads}",
+            "experts_touched": len(need)}
 
 
 def main():
@@ -325,27 +377,32 @@ def main():
         line["roofline"].update({"bound": "mfma", "achieved": res["gu_tflops"],
                                  "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                                  "frac": res["gu_tflops"] / FP8_PEAK_TFLOPS})
+    line["layer"] = {"bytes": res["layer_bytes"], "gbs": res["layer_gbs"],
+                     "frac_hbm": res["layer_gbs"] / HBM_PEAK_GBS,
+                     "note": "compulsory bytes of the whole forward (touched experts' FP8 "
+                             "codes and scales, router, bias, gamma, x read and out written "
+                             "once) over ms_per_step"}
     if args.workload == "decode" and not args.no_secondary:
+        sub = max(3, args.steps // 2)
         pre = synth.with_workload(base, synth.K2_PREFILL, seed=0)
-        rp = run_workload(layer, pre, max(3, args.steps // 2), 2)
-        pre_sclk = None if args.no_clock else sclk_during(layer, pre.x)
-        line["prefill"] = {
-            "tokens": rp["T"], "value": rp["T"] / (rp["ms"] * 1e-3), "unit": "tokens/s",
-            "ms_per_step": rp["ms"],
-            "fp8_tflops_layer": rp["total_flops"] / (rp["ms"] * 1e-3) / 1e12,
-            "frac_fp8_peak_layer": rp["total_flops"] / (rp["ms"] * 1e-3) / 1e12 / FP8_PEAK_TFLOPS,
-            "gateup_tflops": rp["gu_tflops"], "gateup_frac_fp8_peak":
-                rp["gu_tflops"] / FP8_PEAK_TFLOPS,
-            "gateup_gbs": rp["gu_gbs"], "gateup_frac_hbm_peak": rp["gu_gbs"] / HBM_PEAK_GBS,
-            "gateup_arithmetic_intensity": rp["gu_flops"] / rp["gu_bytes"],
-            "gateup_traffic": measured_traffic(pre.shape.name),
-            "gateup_mfma_counters": measured_mfma(pre.shape.name),
-            "sclk_mhz": pre_sclk,
-            # the published FP8 peak assumes 2400 MHz; at the measured clock:
-            "gateup_frac_fp8_peak_at_sclk":
-                rp["gu_tflops"] / (FP8_PEAK_TFLOPS * pre_sclk / 2400.0) if pre_sclk else None,
-            "stage_ms": rp["stage"]}
+        rp = run_workload(layer, pre, sub, 2)
+        sclk = None if args.no_clock else sclk_during(layer, pre.x)
+        line["prefill"] = secondary_line(rp, pre.shape.name, sclk)
+        print(f"# prefill {rp['ms']:.3f} ms", file=sys.stderr, flush=True)
         del pre
+        skw = synth.with_workload(base, synth.K2_SKEWED, seed=0)
+        rs = run_workload(layer, skw, sub, 2)
+        line["skewed"] = secondary_line(rs, skw.shape.name)
+        line["skewed"]["max_rows_per_expert"] = int(rs["counts"].max())
+        line["skewed"]["experts_under_10_rows"] = int((rs["counts"] < 10).sum())
+        print(f"# skewed {rs['ms']:.3f} ms", file=sys.stderr, flush=True)
+        del skw
+        dense = synth.generate(synth.K2_DENSE, seed=0, device="cuda")
+        dlayer = K2MoE(dense)
+        rd = run_workload(dlayer, dense, sub, 2)
+        line["dense"] = secondary_line(rd, dense.shape.name)
+        print(f"# dense {rd['ms']:.3f} ms", file=sys.stderr, flush=True)
+        del dlayer, dense
     if not args.no_clock:
         layer.use_router(inp)
         line["sclk_mhz"] = sclk_during(layer, inp.x)
@@ -359,7 +416,8 @@ def main():
         line["copy_probe_bytes"] = n * 4
         del src, dst
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(inp, args.cpu_tokens)
+        print("# timing the CPU oracle", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(inp, args.cpu_tokens, args.cpu_runs)
     print(json.dumps(line), flush=True)
 
 

@@ -154,6 +154,11 @@ moe_status moe_router(const moe_config* cfg, int64_t T, const void* x, const voi
                       size_t ws_bytes, void* stream);
 
 /* Group the T*k (token, slot) pairs by expert, stable in token order.
+ * The gate scores every token of the batch as one flat list of bsz*seq_len
+ * rows ("Kimi-K2-Base", Mixture of experts, Load balancing: the scores are
+ * viewed as bsz*seq_len rows before the bias is added), and each chosen
+ * expert is then applied to the tokens that chose it; this call builds that
+ * token-to-expert grouping for the grouped GEMMs.
  *  expert_offsets [E+1]: exclusive prefix sum of the per-expert counts
  *  (expert_offsets[E] = T*k); row_pair [T*k]: pair index t*k+slot of each
  *  permuted row; pair_row [T*k]: its inverse.  Bit-exact, no atomics order.
@@ -192,7 +197,11 @@ moe_status moe_combine(const moe_config* cfg, int64_t T, const float* rows,
                        const int32_t* pair_row, const float* topk_w, const float* shared_out,
                        const void* residual, void* out, int32_t out_f32, void* stream);
 
-/* The whole layer in one call: out [T, d] (layer dtype) = x + MoE(RMSNorm(x)).
+/* The whole layer in one call: out [T, d] (layer dtype) = x + MoE(RMSNorm(x)),
+ * the FFN half of a decoder block ("Kimi K2 · Dense transformer block",
+ * Code: post-attention RMSNorm, the MLP, then the residual add; the MLP of
+ * every block after the first is the MoE, "Kimi K2 · Architecture", Fact
+ * sheet: 384 routed + 1 shared experts, 8 chosen per token).
  * Same kernels as the four calls above, with the routing weights applied in
  * the down-projection epilogue; bitwise equal to the unfused chain. */
 moe_status moe_forward(const moe_config* cfg, int64_t T, const void* x, const void* norm_w,
