@@ -37,3 +37,30 @@ def run_oracle(inputs, tokens=None) -> dict:
     wr = None if inputs.w_router is None else to_f32(inputs.w_router)
     bias = None if inputs.bias is None else to_f32(inputs.bias)
     return moe_layer(p, x, norm_w, wr, bias, ExpertFetcher(inputs), tokens=tokens)
+
+
+def run_mla_oracle(inputs, tokens=None) -> dict:
+    """MLA oracle forward on generated inputs (any device), on a host copy of
+    the cache (the oracle writes the new positions into it; returned as
+    "cache")."""
+    import numpy as np
+    from .mla_ref import MLAParams, mla_layer
+    sh = inputs.shape
+    p = MLAParams(d_model=sh.d_model, n_heads=sh.n_heads, q_lora=sh.q_lora, kv_lora=sh.kv_lora,
+                  qk_nope=sh.qk_nope, qk_rope=sh.qk_rope, v_head=sh.v_head,
+                  rope_theta=sh.rope_theta, rope_factor=sh.rope_factor,
+                  rope_orig_len=sh.rope_orig_len, beta_fast=sh.beta_fast,
+                  beta_slow=sh.beta_slow, mscale_all_dim=sh.mscale_all_dim, rms_eps=sh.rms_eps)
+    w = {k: v.detach().cpu().numpy() for k, v in inputs.w.items()}
+    w["g_in"] = to_f32(inputs.norm_w)
+    w["g_qa"] = to_f32(inputs.g_qa)
+    w["g_kva"] = to_f32(inputs.g_kva)
+    cache = dict(codes=inputs.cache_codes.cpu().numpy().copy(),
+                 scales=inputs.cache_scales.cpu().numpy().copy(),
+                 rope=to_f32(inputs.cache_rope).copy())
+    T = sh.tokens
+    seq_of = np.arange(T) // sh.n_new
+    pos_of = np.asarray(sh.cached, dtype=np.int64)[seq_of] + np.arange(T) % sh.n_new
+    res = mla_layer(p, to_f32(inputs.x), w, seq_of, pos_of, cache, tokens=tokens)
+    res.update(cache=cache, seq_of=seq_of, pos_of=pos_of, params=p)
+    return res

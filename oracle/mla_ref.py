@@ -182,18 +182,17 @@ def attend(p: MLAParams, q: np.ndarray, qpos: int, keys_codes: np.ndarray,
     n = qpos + 1
     H, dn, dr, dv = p.n_heads, p.qk_nope, p.qk_rope, p.v_head
     c = dequantize_1x128(keys_codes[:n], keys_scales[:n])                 # [n, 512] float64
-    wkvb = dequantize_weight_rows(w["w_kvb"], w["s_kvb"]).reshape(H, dn + dv, p.kv_lora)
-    kv = f32(np.einsum("hok,nk->hno", wkvb, c))                           # [H, n, 256]
-    k_nope, v = kv[:, :, :dn], kv[:, :, dn:]
+    wkvb = dequantize_weight_rows(w["w_kvb"], w["s_kvb"])                 # [H*(dn+dv), 512]
+    kv = f32(wkvb @ c.T).reshape(H, dn + dv, n).astype(np.float64)       # up-projection
+    k_nope, v = kv[:, :dn, :], kv[:, dn:, :]                              # [H, 128, n] each
     q_nope = q[:, :dn].astype(np.float64)
     q_rot = apply_rope(q[:, dn:][None], np.array([qpos]), p)[0]          # [H, 64]
-    s = (np.einsum("hd,hnd->hn", q_nope, k_nope.astype(np.float64)) +
-         q_rot @ keys_rope[:n].astype(np.float64).T)
+    s = np.einsum("hd,hdn->hn", q_nope, k_nope) + q_rot @ keys_rope[:n].astype(np.float64).T
     s = f32(s * softmax_scale(p))
     s64 = s.astype(np.float64)
     e = np.exp(s64 - s64.max(axis=1, keepdims=True))
     pr = f32(e / e.sum(axis=1, keepdims=True))
-    o = f32(np.einsum("hn,hnd->hd", pr.astype(np.float64), v.astype(np.float64)))
+    o = f32(np.einsum("hn,hdn->hd", pr.astype(np.float64), v))
     return o.reshape(H * dv)
 
 

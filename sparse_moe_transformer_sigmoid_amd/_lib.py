@@ -1,4 +1,5 @@
-"""ctypes binding of libk2moe.so: the C ABI in include/k2moe.h, same names.
+"""ctypes binding of libk2moe.so: the C ABI in include/k2moe.h and include/k2mla.h,
+same names.
 
 Argument marshalling only -- every step of the layer runs in the HIP
 library.  Loading fails loudly if the library has not been built.
@@ -36,9 +37,26 @@ class MoEError(RuntimeError):
 STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED",
                 3: "MOE_ERR_WORKSPACE", 4: "MOE_ERR_HIP"}
 
+class mla_config(C.Structure):
+    _fields_ = [("d_model", C.c_int32), ("n_heads", C.c_int32), ("q_lora", C.c_int32),
+                ("kv_lora", C.c_int32), ("qk_nope", C.c_int32), ("qk_rope", C.c_int32),
+                ("v_head", C.c_int32), ("rope_orig_len", C.c_int32), ("rope_theta", C.c_float),
+                ("rope_factor", C.c_float), ("beta_fast", C.c_float), ("beta_slow", C.c_float),
+                ("mscale_all_dim", C.c_float), ("rms_eps", C.c_float)]
+
+
+class mla_weights(C.Structure):
+    _fields_ = [("w_qa", C.c_void_p), ("s_qa", C.c_void_p), ("w_qb", C.c_void_p),
+                ("s_qb", C.c_void_p), ("w_kva", C.c_void_p), ("s_kva", C.c_void_p),
+                ("w_kvb", C.c_void_p), ("s_kvb", C.c_void_p), ("w_o", C.c_void_p),
+                ("s_o", C.c_void_p), ("g_qa", C.c_void_p), ("g_kva", C.c_void_p)]
+
+
 EXPORTS = ["moe_status_str", "moe_last_error", "moe_packed_weights_bytes", "moe_pack_weights",
            "moe_workspace_bytes", "moe_router", "moe_permute", "moe_grouped_swiglu",
-           "moe_combine", "moe_forward", "moe_profile_enable", "moe_profile_read"]
+           "moe_combine", "moe_forward", "moe_profile_enable", "moe_profile_read",
+           "mla_packed_weights_bytes", "mla_pack_weights", "mla_workspace_bytes", "mla_forward",
+           "mla_attention"]
 STAGES = ["norm_quant", "router_gemm", "topk", "permute", "tiles", "gateup", "down", "combine"]
 
 _LIB = None
@@ -69,6 +87,13 @@ def load(path: str | None = None) -> C.CDLL:
         "moe_forward": (i32, [cfgp, i64, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "moe_profile_enable": (i32, [i32]),
         "moe_profile_read": (i32, [C.POINTER(C.c_double), C.POINTER(C.c_int64), i32]),
+        "mla_packed_weights_bytes": (sz, [C.POINTER(mla_config)]),
+        "mla_pack_weights": (i32, [C.POINTER(mla_config), C.POINTER(mla_weights), vp, vp]),
+        "mla_workspace_bytes": (i32, [C.POINTER(mla_config), i32, i32, i32, C.POINTER(sz)]),
+        "mla_forward": (i32, [C.POINTER(mla_config), i32, i32, i32, vp, vp, vp, vp, vp, vp, vp,
+                              vp, i32, vp, sz, vp]),
+        "mla_attention": (i32, [C.POINTER(mla_config), i32, i32, i32, vp, vp, vp, vp, vp, vp,
+                                vp, vp, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)

@@ -13,6 +13,14 @@ namespace {
 
 thread_local std::string g_err;
 
+}  // namespace
+
+// detail of the last non-OK status on this host thread, shared by every entry
+// point of the library (moe_last_error)
+std::string& k2::error_text() { return g_err; }
+
+namespace {
+
 moe_status fail(moe_status s, const std::string& msg) {
   g_err = msg;
   return s;

@@ -50,4 +50,26 @@ hipError_t launch_gemm_fp8(bool gateup, int tt, const GemmArgs& a, int grid, hip
   return gateup ? launch_tt<true>(tt, a, grid, s) : launch_tt<false>(tt, a, grid, s);
 }
 
+// One weight matrix (a single group of T rows) in the down form, its K blocks
+// cut into nsplit slices (grid.y); every block product summed exactly.
+hipError_t launch_gemm_dense(int tt, int nsplit, const GemmArgs& a, int grid, hipStream_t s) {
+  if (grid <= 0) return hipSuccess;
+  switch (tt) {
+    case 1:
+      gemm_fp8_kernel<false, 1, 2, false, 2, 1, 1, 0, 0, true, true>
+          <<<dim3(split_grid(grid), nsplit), 256, 0, s>>>(a);
+      break;
+    case 2:
+      gemm_fp8_kernel<false, 2, 2, false, 2, 1, 1, 0, 0, true, true>
+          <<<dim3(grid, nsplit), 256, 0, s>>>(a);
+      break;
+    case 4:
+      gemm_fp8_kernel<false, 4, 2, false, 2, 1, 1, 0, 0, true, true>
+          <<<dim3(grid, nsplit), 256, 0, s>>>(a);
+      break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace k2

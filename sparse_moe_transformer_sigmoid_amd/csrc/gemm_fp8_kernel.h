@@ -196,7 +196,7 @@ __device__ __forceinline__ int act_row_of(const GemmArgs& g, const WorkItem& w, 
 // each weight chunk once; at larger tiles ordinary stores measure faster).
 template <bool GATEUP, int TT, bool NTS>
 __device__ __forceinline__ void epilogue(const GemmArgs& g, v4f (&acc)[4][TT], float* lds_red,
-                                         const WorkItem& wi, int wave, int lane) {
+                                         const WorkItem& wi, int wave, int lane, int kslice) {
   const int nc = wi.nc, row0 = wi.row0, mcount = wi.mcount, ntt = wi.ntt;
   const bool shared_grp = wi.shared_grp;
   if constexpr (GATEUP) {
@@ -254,8 +254,9 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, v4f (&acc)[4][TT], f
           float wt = 1.f;
           const bool mul = g.weighted && !shared_grp;
           if (mul) wt = g.topk_w[min(max(g.row_pair[row], 0), g.P - 1)];
+          // split-K launches write one [P, d] slice of partial sums per K slice
           float* dst = shared_grp ? g.shared_out + (size_t)(row - g.P) * g.d
-                                  : g.rows + (size_t)row * g.d;
+                                  : g.rows + ((size_t)kslice * g.P + row) * g.d;
           dst += nc * 256 + 64 * wave + 4 * (lane >> 4);
 #pragma unroll
           for (int rt = 0; rt < 4; ++rt) {
@@ -287,8 +288,11 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, v4f (&acc)[4][TT], f
 // EXACT (BMODE 0): each 128-wide block product is summed by mfma_fp8_exact
 // (twice the MFMA cycles), so the gate/up values the requantisation decides
 // on are correct to fp32 rounding; for launches that wait on HBM, not MFMA.
+// SPLITK (down form): the K blocks are cut into gridDim.y equal slices, slice
+// blockIdx.y writing its partial sums to its own [P, d] slice of `rows`
+// (for small batches, whose few work items would not fill the chip).
 template <bool GATEUP, int TT, int NBUF, bool NT, int BSETS = 2, int MINW = 1, int GRPX = 0,
-          int BMODE = 0, int ILV = 0, bool EXACT = false>
+          int BMODE = 0, int ILV = 0, bool EXACT = false, bool SPLITK = false>
 __global__ __launch_bounds__(256, MINW) void gemm_fp8_kernel(const GemmArgs g) {
   static_assert(NBUF >= 2 && NBUF <= 4, "NBUF must be 2, 3 or 4");
   static_assert(BSETS == 1 || BSETS == 2, "BSETS must be 1 or 2");
@@ -296,6 +300,7 @@ __global__ __launch_bounds__(256, MINW) void gemm_fp8_kernel(const GemmArgs g) {
   // ring slot issued after the step's direct loads (one slot per step)
   static_assert(BMODE == 0 || (BMODE == 1 && NBUF == 2), "BMODE 1 needs NBUF 2");
   static_assert(!EXACT || (BMODE == 0 && ILV == 0), "EXACT is implemented for BMODE 0 only");
+  static_assert(!SPLITK || !GATEUP, "SPLITK is implemented for the down form only");
   constexpr int BM = 16 * TT;
   constexpr int CPT = (TT * 128 + 255) / 256;   // 16-byte staging chunks per thread
   // LDS rows past the tile (TT < 2) are write-only padding: every thread
@@ -320,6 +325,11 @@ __global__ __launch_bounds__(256, MINW) void gemm_fp8_kernel(const GemmArgs g) {
                               : decode_work(g, BM);
   if (!wi.valid) return;
   const int grp = wi.grp, nc = wi.nc, row0 = wi.row0, mcount = wi.mcount, ntt = wi.ntt;
+  // K slice of this workgroup: blocks kbs .. kbs + nkb_s - 1
+  const int kslice = SPLITK ? (int)blockIdx.y : 0;
+  const int nkb_s = SPLITK ? g.nkb / (int)gridDim.y : g.nkb;
+  const int kbs = kslice * nkb_s;
+  const uint8_t* const actp = g.act + (size_t)kbs * 128;
   const bool shared_grp = wi.shared_grp;
 
   auto act_row = [&](int m) { return act_row_of<GATEUP>(g, wi, m); };
@@ -347,13 +357,13 @@ __global__ __launch_bounds__(256, MINW) void gemm_fp8_kernel(const GemmArgs g) {
   const uint32_t brd0 = 128u * bj + 16u * ((2 * (lane >> 4)) ^ bsw);
   const uint32_t brd1 = 128u * bj + 16u * ((2 * (lane >> 4) + 1) ^ bsw);
   // thread tid stages the activation scale of tile row tid (clamped past the tile)
-  const uint32_t saoff = (uint32_t)act_row(tid) * g.nkb;
+  const uint32_t saoff = (uint32_t)act_row(tid) * g.nkb + kbs;
 
   // wave-uniform base of this wave's weight rows; per-lane 32-bit offsets
   // (the wave's rows span nkb * 8 KiB <= 4 MiB), so loads take the
   // scalar-base + vector-offset form and no 64-bit address registers
   const uint8_t* wp = g.wpk + (size_t)grp * g.expert_stride +
-                      (size_t)(nc * 4 + wave) * (size_t)g.nkb * 8192;
+                      (size_t)(nc * 4 + wave) * (size_t)g.nkb * 8192 + (size_t)kbs * 8192;
   const uint32_t wlane = lane * 16;
   const float* swp_base = g.wscale + (size_t)grp * g.wscale_stride + (size_t)nc * g.nkb * 2;
 
@@ -389,7 +399,7 @@ __global__ __launch_bounds__(256, MINW) void gemm_fp8_kernel(const GemmArgs g) {
   auto load_b = [&](int set, int kb) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i)
-      breg[set][i] = *reinterpret_cast<const v4i*>(g.act + (uint32_t)(boff[i] + kb * 128));
+      breg[set][i] = *reinterpret_cast<const v4i*>(actp + (uint32_t)(boff[i] + kb * 128));
     sareg[set] = *reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(g.act_s) +
                                                  (uint32_t)((saoff + kb) * 4));
   };
@@ -402,7 +412,7 @@ __global__ __launch_bounds__(256, MINW) void gemm_fp8_kernel(const GemmArgs g) {
   auto dma_b = [&](int buf, int kb) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i)
-      lds_load16(g.act, boff[i] + kb * 128, lds_addr(&lds_b(buf)[(256 * i + 64 * wave) * 16]));
+      lds_load16(actp, boff[i] + kb * 128, lds_addr(&lds_b(buf)[(256 * i + 64 * wave) * 16]));
     lds_load4(g.act_s, (saoff + kb) * 4, lds_addr(&lds_sa(buf)[64 * wave]));
   };
   auto store_b = [&](int set, int buf) {
@@ -413,10 +423,10 @@ __global__ __launch_bounds__(256, MINW) void gemm_fp8_kernel(const GemmArgs g) {
   };
   auto weight_scales = [&](int kb, float& s_gate_or_down, float& s_up) {
     if constexpr (GATEUP) {
-      s_gate_or_down = lds_sw[2 * kb];
-      s_up = lds_sw[2 * kb + 1];
+      s_gate_or_down = lds_sw[2 * (kb + kbs)];
+      s_up = lds_sw[2 * (kb + kbs) + 1];
     } else {
-      s_gate_or_down = lds_sw[(wave >> 1) * g.nkb + kb];
+      s_gate_or_down = lds_sw[(wave >> 1) * g.nkb + kb + kbs];
       s_up = s_gate_or_down;
     }
   };
@@ -520,7 +530,7 @@ __global__ __launch_bounds__(256, MINW) void gemm_fp8_kernel(const GemmArgs g) {
   // kb+NBUF-1, and ends by waiting only for the activations (BMODE 0: those
   // of block kb+1, issued one step earlier).
   auto kloop = [&](auto ntc) {
-  const int nkb = g.nkb;
+  const int nkb = nkb_s;
   if constexpr (BMODE == 1) {
     dma_b(0, 0);
     asm volatile("s_waitcnt vmcnt(0)" : : : "memory");   // block 0, before the barrier below
@@ -598,7 +608,7 @@ __global__ __launch_bounds__(256, MINW) void gemm_fp8_kernel(const GemmArgs g) {
     kloop(std::false_type{});
   }
 
-  epilogue<GATEUP, TT, NT>(g, acc, lds_red, wi, wave, lane);
+  epilogue<GATEUP, TT, NT>(g, acc, lds_red, wi, wave, lane, kslice);
 }
 
 }  // namespace

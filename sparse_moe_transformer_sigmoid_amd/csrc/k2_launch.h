@@ -5,7 +5,12 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <string>
+
 namespace k2 {
+
+// the thread-local text moe_last_error() returns
+std::string& error_text();
 
 // ---- norm + quant + router (norm_router.hip)
 hipError_t launch_norm_quant(bool fp8, int T, int d, float eps, const void* x, const void* gamma,

@@ -1,0 +1,735 @@
+// Kimi K2 multi-head latent attention (MLA) on gfx950: the kernels between the
+// FP8 projections.
+//
+// Shape ("Kimi K2 · Architecture", Fact sheet and config.json; "Kimi-K2-Base",
+// Attention): 64 heads; a 1,536-wide query latent and a 512-wide key-value
+// latent, each RMS-normalised before its up-projection; per head 128
+// query/key features without position, 64 rotary ones (one rotary key shared
+// by the heads) and 128 value features; softmax scale (0.1 ln 32 + 1)^2 /
+// sqrt(192); causal; positions numbered from the cached length.
+//
+// The attention runs in the absorbed form over a latent cache.  With W_uk,
+// W_uv the key and value rows of head h's key-value up-projection and c_j the
+// cached latent of position j:
+//   q_nope . (W_uk c_j) = (W_uk^T q_nope) . c_j,
+//   sum_j p_j (W_uv c_j) = W_uv (sum_j p_j c_j),
+// so a query becomes q_lat = [W_uk^T q_nope, rope(q_pe)] (576 wide), every
+// head scores against the same cache rows [c_j, k_rope_j], and the value
+// up-projection is applied once to the weighted latent sum.  The cache holds
+// c_j as the e4m3 codes and 1x128 scales the FP8 key-value up-projection
+// reads (656 bytes per position with the bf16 rotary key).
+#include <math.h>
+
+#include "k2_common.h"
+#include "mla_launch.h"
+
+namespace k2 {
+
+namespace {
+
+constexpr int DL = 512;           // latent width (kv_lora)
+constexpr int DR = 64;            // rotary width
+constexpr int DQ = DL + DR;       // absorbed query / cache row width
+constexpr int DN = 128;           // query/key features without position (qk_nope)
+constexpr int DV = 128;           // value features (v_head)
+constexpr int PT = 32;            // cache positions per attention step
+constexpr int CT_LD = DQ + 8;     // bf16 stride of a row-major cache row in LDS
+constexpr int TR_LD = PT + 8;     // bf16 stride of a transposed latent row in LDS
+
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint16_t bf16_bits(float f) { return (uint16_t)f32_to_bf16_rne(f); }
+
+__device__ __forceinline__ __bf16 to_bf16(float f) {
+  return __builtin_bit_cast(__bf16, bf16_bits(f));
+}
+
+// e4m3 code -> float (exact)
+__device__ __forceinline__ float e4m3_val(uint32_t code) {
+  const v2f p = __builtin_amdgcn_cvt_pk_f32_fp8((int)code, false);
+  return p[0];
+}
+
+// ------------------------------------------------------------------ packing
+// [n0 rows of src0; n1 rows of src1; zero rows] x K codes -> the grouped GEMM's
+// down-form fragment order (256-row chunks, four 64-row waves, K blocks, 16-row
+// tiles, lane halves), as the expert down projections are packed.
+__global__ __launch_bounds__(256) void pack_rows_kernel(int n_pad, int K, const uint8_t* src0,
+                                                        int n0, const uint8_t* src1, int n1,
+                                                        uint8_t* __restrict__ dst) {
+  const long q = (long)blockIdx.x * 256 + threadIdx.x;
+  if (q >= (long)n_pad * K / 16) return;
+  const int lane = q & 63, p = (q >> 6) & 1, rt = (q >> 7) & 3;
+  long rest = q >> 9;
+  const int nkb = K / QBLK;
+  const int kb = (int)(rest % nkb);
+  rest /= nkb;
+  const int w = (int)(rest & 3), j = (int)(rest >> 2);
+  const int row = j * 256 + 64 * w + 16 * rt + (lane & 15);
+  const int col = kb * 128 + (lane >> 4) * 32 + p * 16;
+  uint4 v = make_uint4(0, 0, 0, 0);
+  if (row < n0)
+    v = *reinterpret_cast<const uint4*>(src0 + (size_t)row * K + col);
+  else if (row < n0 + n1)
+    v = *reinterpret_cast<const uint4*>(src1 + (size_t)(row - n0) * K + col);
+  reinterpret_cast<uint4*>(dst)[q] = v;
+}
+
+// block scales [ceil(n0/128) of s0; ceil(n1/128) of s1; 1.0 padding] x K/128
+__global__ void pack_row_scales_kernel(int nb_pad, int kb, const float* s0, int nb0,
+                                       const float* s1, int nb1, float* __restrict__ dst) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= nb_pad * kb) return;
+  const int rb = i / kb, c = i % kb;
+  float v = 1.f;
+  if (rb < nb0) v = s0[rb * kb + c];
+  else if (rb < nb0 + nb1) v = s1[(rb - nb0) * kb + c];
+  dst[i] = v;
+}
+
+// the grouped GEMM's tables for one group of T rows (offsets, m-tile prefix,
+// m-tile -> group)
+__global__ void dense_tiles_kernel(int T, int bm, int32_t* offsets, int32_t* mt_start,
+                                   int32_t* tile_group) {
+  const int n = (T + bm - 1) / bm;
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i == 0) {
+    offsets[0] = 0;
+    offsets[1] = T;
+    mt_start[0] = 0;
+    mt_start[1] = n;
+  }
+  if (i < n) tile_group[i] = 0;
+}
+
+// out[t, c] = sum over s of part[s, t, c] (ascending s), c < ncol of rows of
+// width ld; then + residual and one rounding to bf16 (res != null), or fp32.
+__global__ __launch_bounds__(256) void slice_sum_kernel(int T, int ncol, int ld, int nsplit,
+                                                        const float* __restrict__ part,
+                                                        const uint16_t* __restrict__ res,
+                                                        void* __restrict__ out, int out_ld) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (long)T * (ncol / 4)) return;
+  const int t = (int)(i / (ncol / 4)), c = 4 * (int)(i % (ncol / 4));
+  float4 a = *reinterpret_cast<const float4*>(part + (size_t)t * ld + c);
+  for (int s = 1; s < nsplit; ++s) {
+    const float4 b = *reinterpret_cast<const float4*>(part + ((size_t)s * T + t) * ld + c);
+    a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+  }
+  if (res) {
+    const uint2 xr = *reinterpret_cast<const uint2*>(res + (size_t)t * out_ld + c);
+    const uint32_t o0 = f32_to_bf16_rne(bf16_to_f32(xr.x & 0xFFFFu) + a.x) |
+                        (f32_to_bf16_rne(bf16_to_f32(xr.x >> 16) + a.y) << 16);
+    const uint32_t o1 = f32_to_bf16_rne(bf16_to_f32(xr.y & 0xFFFFu) + a.z) |
+                        (f32_to_bf16_rne(bf16_to_f32(xr.y >> 16) + a.w) << 16);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + (size_t)t * out_ld + c) =
+        make_uint2(o0, o1);
+  } else {
+    *reinterpret_cast<float4*>(static_cast<float*>(out) + (size_t)t * out_ld + c) = a;
+  }
+}
+
+// ------------------------------------------------------- latents and cache
+__device__ __forceinline__ int token_pos(const int32_t* cached_len, int t, int n_new,
+                                        int max_len, int* seq) {
+  *seq = t / n_new;
+  const int p = cached_len[*seq] + t % n_new;
+  return min(max(p, 0), max_len - 1);
+}
+
+// rotate (a, b) by pos * f in double, round to fp32
+__device__ __forceinline__ void rope_pair(float a, float b, int pos, double f, float* ra,
+                                          float* rb) {
+  double sn, cs;
+  sincos((double)pos * f, &sn, &cs);
+  *ra = (float)((double)a * cs - (double)b * sn);
+  *rb = (float)((double)a * sn + (double)b * cs);
+}
+
+// Per token: RMSNorm of the query latent -> bf16 -> 1x128 codes (the input of
+// the query up-projection); RMSNorm of the key-value latent -> bf16 -> 1x128
+// codes and scales into the cache; the positional key rotated and rounded to
+// bf16 into the cache.  qkv row: [q_a (q_lora), kv_a latent (512), k_pe (64)].
+// Norms as in the input RMSNorm: mean of squares formed in fp64, rounded to
+// fp32, r = 1/sqrt(ms + eps), h = bf16((v r) g).
+__global__ __launch_bounds__(256) void mla_latent_kernel(
+    int q_lora, int qkv_ld, float eps, const float* __restrict__ qkv,
+    const uint16_t* __restrict__ g_qa, const uint16_t* __restrict__ g_kva,
+    const double* __restrict__ inv_freq, const int32_t* __restrict__ cached_len, int n_new,
+    int max_len, uint8_t* __restrict__ qa_q, float* __restrict__ qa_s,
+    uint8_t* __restrict__ c_codes, float* __restrict__ c_scales, uint16_t* __restrict__ c_rope) {
+  const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int seq;
+  const int pos = token_pos(cached_len, t, n_new, max_len, &seq);
+  const float* row = qkv + (size_t)t * qkv_ld;
+  const size_t cidx = (size_t)seq * max_len + pos;
+  __shared__ double red[2][4];
+  // sums of squares: query latent (q_lora values) and key-value latent (512)
+  double sq = 0.0, sc = 0.0;
+  for (int i = tid; i < q_lora; i += 256) sq += (double)row[i] * (double)row[i];
+  for (int i = tid; i < DL; i += 256) sc += (double)row[q_lora + i] * (double)row[q_lora + i];
+  sq = wave_sum(sq);
+  sc = wave_sum(sc);
+  if (lane == 0) {
+    red[0][wave] = sq;
+    red[1][wave] = sc;
+  }
+  __syncthreads();
+  const float msq = (float)((red[0][0] + red[0][1] + red[0][2] + red[0][3]) / (double)q_lora);
+  const float msc = (float)((red[1][0] + red[1][1] + red[1][2] + red[1][3]) / (double)DL);
+  const float rq = 1.0f / sqrtf(msq + eps), rc = 1.0f / sqrtf(msc + eps);
+  // a wave normalises and quantises 128-value blocks, two values per lane
+  auto quant_block = [&](const float* src, const uint16_t* g, float r, uint8_t* codes,
+                         float* scale) {
+    const int i = 2 * lane;
+    const float h0 = bf16_to_f32(f32_to_bf16_rne((src[i] * r) * bf16_to_f32(g[i])));
+    const float h1 = bf16_to_f32(f32_to_bf16_rne((src[i + 1] * r) * bf16_to_f32(g[i + 1])));
+    float amax = fmaxf(fabsf(h0), fabsf(h1));
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
+    const float s = fp8_scale(amax);
+    const uint32_t q = cvt4_e4m3(clamp_fp8(h0 / s), clamp_fp8(h1 / s), 0.f, 0.f);
+    *reinterpret_cast<uint16_t*>(codes + i) = (uint16_t)(q & 0xFFFFu);
+    if (lane == 0) *scale = s;
+  };
+  const int nqb = q_lora / QBLK;
+  for (int b = wave; b < nqb; b += 4)
+    quant_block(row + b * QBLK, g_qa + b * QBLK, rq, qa_q + (size_t)t * q_lora + b * QBLK,
+                qa_s + (size_t)t * nqb + b);
+  quant_block(row + q_lora + wave * QBLK, g_kva + wave * QBLK, rc,
+              c_codes + cidx * DL + wave * QBLK, c_scales + cidx * (DL / QBLK) + wave);
+  if (tid < DR / 2) {
+    float ra, rb;
+    rope_pair(row[q_lora + DL + 2 * tid], row[q_lora + DL + 2 * tid + 1], pos, inv_freq[tid],
+              &ra, &rb);
+    c_rope[cidx * DR + 2 * tid] = bf16_bits(ra);
+    c_rope[cidx * DR + 2 * tid + 1] = bf16_bits(rb);
+  }
+}
+
+// --------------------------------------------------------- query absorption
+constexpr int QA_TB = 16;   // tokens per workgroup
+
+// qcat[t, h] = scale * [W_uk^T q_nope (512), rope(q_pe) (64)] in fp32.
+// W_uk of head h: key-value up-projection rows h*(DN+DV) .. + DN - 1 (one
+// 128-row scale block), dequantised as code * block scale; fp32 sums.
+__global__ __launch_bounds__(256) void mla_qabsorb_kernel(
+    int T, int H, float smscale, const float* __restrict__ q, const uint8_t* __restrict__ w_kvb,
+    const float* __restrict__ s_kvb, const double* __restrict__ inv_freq,
+    const int32_t* __restrict__ cached_len, int n_new, int max_len,
+    float* __restrict__ qcat) {
+  const int h = blockIdx.x, t0 = blockIdx.y * QA_TB, tid = threadIdx.x;
+  const int qld = H * (DN + DR);
+  __shared__ __attribute__((aligned(16))) uint8_t wk[DN * DL];   // 64 KiB of codes
+  __shared__ float qn[QA_TB][DN];
+  const uint8_t* wsrc = w_kvb + (size_t)h * (DN + DV) * DL;
+  for (int i = tid; i < DN * DL / 16; i += 256)
+    reinterpret_cast<uint4*>(wk)[i] = reinterpret_cast<const uint4*>(wsrc)[i];
+  for (int i = tid; i < QA_TB * DN; i += 256) {
+    const int tt = i / DN, d = i % DN;
+    qn[tt][d] = (t0 + tt < T) ? q[(size_t)(t0 + tt) * qld + h * (DN + DR) + d] : 0.f;
+  }
+  __syncthreads();
+  // thread tid: latent features r = 2 tid, 2 tid + 1 (scale block r / 128)
+  const int r = 2 * tid;
+  const float sk = s_kvb[(size_t)(2 * h) * (DL / QBLK) + r / QBLK];
+  float acc[QA_TB][2];
+#pragma unroll
+  for (int tt = 0; tt < QA_TB; ++tt) acc[tt][0] = acc[tt][1] = 0.f;
+  for (int d = 0; d < DN; ++d) {
+    const uint32_t c2 = *reinterpret_cast<const uint16_t*>(&wk[d * DL + r]);
+    const v2f w2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)c2, false);
+    const float w0 = w2[0] * sk, w1 = w2[1] * sk;
+#pragma unroll
+    for (int tt = 0; tt < QA_TB; ++tt) {
+      acc[tt][0] = fmaf(qn[tt][d], w0, acc[tt][0]);
+      acc[tt][1] = fmaf(qn[tt][d], w1, acc[tt][1]);
+    }
+  }
+  for (int tt = 0; tt < QA_TB && t0 + tt < T; ++tt) {
+    float* dst = qcat + ((size_t)(t0 + tt) * H + h) * DQ;
+    *reinterpret_cast<float2*>(dst + r) = make_float2(acc[tt][0] * smscale, acc[tt][1] * smscale);
+  }
+  // rotary part: thread (token tt, pair i)
+  for (int i = tid; i < QA_TB * (DR / 2); i += 256) {
+    const int tt = i / (DR / 2), pr = i % (DR / 2), t = t0 + tt;
+    if (t >= T) continue;
+    int seq;
+    const int pos = token_pos(cached_len, t, n_new, max_len, &seq);
+    const float* qp = q + (size_t)t * qld + h * (DN + DR) + DN;
+    float ra, rb;
+    rope_pair(qp[2 * pr], qp[2 * pr + 1], pos, inv_freq[pr], &ra, &rb);
+    float* dst = qcat + ((size_t)t * H + h) * DQ + DL;
+    dst[2 * pr] = ra * smscale;
+    dst[2 * pr + 1] = rb * smscale;
+  }
+}
+
+// ------------------------------------------------------- latent attention
+// Eight waves: waves 0-3 compute, wave w = (token, 8 heads); waves 4-7 fill
+// LDS.  mode 0 (one new token per sequence, heads % 32 == 0): the compute
+// waves are one token's four groups of 8 heads (a workgroup covers 32 heads);
+// mode 1: up to four consecutive tokens of one sequence with one group of 8.
+// The cache positions [lo, hi) of the work item's split are visited in steps
+// of 32.  While the compute waves use one LDS buffer the fill waves load the
+// next step's cache rows into the other: the latent codes as exact bf16
+// values (every e4m3 value is one), twice -- row-major [pos][576] with the
+// rotary key (the A operand of the scores) and transposed [latent][pos] (the
+// A operand of the value sum) -- and the latent's 1x128 scales [block][pos].
+//
+// Sums to fp32 precision: the 16 MFMA columns are 8 heads x {hi, lo}, the
+// bf16 high part of a value and the bf16 rounding of its remainder, so one
+// MFMA gives both halves of the product and the two columns of a head add to
+// it within about 2^-17 relative.  Per 128-latent block b:
+//   S_b^T = C_b Q^T              (codes, query halves; lane: 4 positions x 1 column)
+//   s = sum_b scale_b(pos) S_b + S_rope, the two columns of a head added
+//   online softmax per head
+//   O_b^T += C_b^T (p scale_b)^T  (p * scale as {hi, lo} columns; the lane's 8 K
+//                                  slots = positions 4q..4q+3 of the first 16 and
+//                                  of the second 16, where S^T left them)
+// and finally writes its running max m, sum l and O^T (head x 512) unscaled.
+struct AttnArgs {
+  const uint8_t* c_codes;
+  const float* c_scales;
+  const uint16_t* c_rope;
+  const float* qcat;         // [T, H, 576] fp32, softmax scale folded in
+  const int32_t* cached_len; // [S]
+  float* part_o;             // [nsplit, T, H, 512]
+  float* part_ml;            // [nsplit, T, H, 2]
+  int T, H, n_new, max_len, nsplit, chunk, mode, items_per_split;
+};
+
+__device__ __forceinline__ v4f mfma_bf16(v8bf a, v8bf b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// the bf16 high part of v (round to nearest even) or the bf16 rounding of
+// the remainder v - high
+__device__ __forceinline__ uint32_t bf16_half(float v, bool lo) {
+  const uint32_t hb = f32_to_bf16_rne(v);
+  return lo ? f32_to_bf16_rne(v - bf16_to_f32(hb)) : hb;
+}
+
+constexpr int CT_ELEMS = PT * CT_LD, TR_ELEMS = DL * TR_LD;
+constexpr int HPW = 8;   // heads per compute wave
+
+__global__ __launch_bounds__(512, 1) void mla_attn_kernel(const AttnArgs g) {
+  __shared__ __attribute__((aligned(16))) uint16_t ct[2][CT_ELEMS];   // row-major cache rows
+  __shared__ __attribute__((aligned(16))) uint16_t tr[2][TR_ELEMS];   // transposed latents
+  __shared__ __attribute__((aligned(16))) float sc_l[2][DL / QBLK][PT];  // latent scales
+  __shared__ int kv_sh[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool compute = wave < 4;
+  const int q4 = lane >> 4, l16 = lane & 15;
+  const bool lo_col = l16 >= HPW;           // this lane's column holds the low halves
+  const int item = blockIdx.x % g.items_per_split, split = blockIdx.x / g.items_per_split;
+  const int hg_n = g.H / HPW;
+  const int cw = wave & 3;   // compute-wave index this wave stands for
+  // the compute wave's token and head group (fill waves compute the same
+  // values for the sequence, which is common to the workgroup)
+  int t, hg, seq;
+  bool active;
+  if (g.mode == 0) {
+    t = item / (hg_n / 4);
+    hg = (item % (hg_n / 4)) * 4 + cw;
+    active = true;
+  } else {
+    const int tb_n = (g.n_new + 3) / 4;
+    const int per_seq = tb_n * hg_n;
+    const int s_ = item / per_seq, rem = item % per_seq;
+    const int tb = rem / hg_n;
+    hg = rem % hg_n;
+    const int ti = tb * 4 + cw;
+    active = ti < g.n_new;
+    t = s_ * g.n_new + min(ti, g.n_new - 1);
+  }
+  const int qpos = token_pos(g.cached_len, t, g.n_new, g.max_len, &seq);
+  if (compute && lane == 0) kv_sh[cw] = active ? qpos + 1 : 0;
+  __syncthreads();
+  // the workgroup's positions: its split's range, up to its last query position
+  const int wg_end = max(max(kv_sh[0], kv_sh[1]), max(kv_sh[2], kv_sh[3]));
+  const int lo = split * g.chunk, hi = min(wg_end, lo + g.chunk);
+  const int my_end = (compute && active) ? qpos + 1 : 0;
+  const int h = hg * HPW + (l16 & (HPW - 1));   // this lane's head
+  const size_t cbase = (size_t)seq * g.max_len;
+
+  // fill waves: positions p0 .. p0 + 31 into buffer b (zeros past hi).  Item
+  // = (latent chunk of 16 features, pair of positions), two items per
+  // thread, then the rotary keys and the scales.
+  auto fill = [&](int b, int p0) {
+    const int ftid = tid - 256;
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int itm = ftid + 256 * it;
+      const int sub = itm >> 4, pr = itm & 15;
+      uint32_t pk[2][8];   // bf16 pairs: codes 2k, 2k+1 of position 2 pr + j
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int pl = 2 * pr + j, p = p0 + pl;
+        uint4 cv = make_uint4(0, 0, 0, 0);
+        if (p < hi)
+          cv = *reinterpret_cast<const uint4*>(g.c_codes + (cbase + p) * DL + 16 * sub);
+        const uint32_t w4[4] = {cv.x, cv.y, cv.z, cv.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          pk[j][2 * k] = __builtin_bit_cast(
+              uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w4[k], 1.f, false));
+          pk[j][2 * k + 1] = __builtin_bit_cast(
+              uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w4[k], 1.f, true));
+        }
+        uint4* dst = reinterpret_cast<uint4*>(&ct[b][pl * CT_LD + 16 * sub]);
+        dst[0] = make_uint4(pk[j][0], pk[j][1], pk[j][2], pk[j][3]);
+        dst[1] = make_uint4(pk[j][4], pk[j][5], pk[j][6], pk[j][7]);
+      }
+      // transposed: feature 16 sub + i, positions 2 pr and 2 pr + 1 (order of i
+      // staggered by chunk so a wave's writes spread over the LDS banks)
+#pragma unroll
+      for (int ii = 0; ii < 16; ++ii) {
+        const int i = (ii + sub) & 15, w = i >> 1;
+        const uint32_t v = (i & 1) ? ((pk[0][w] >> 16) | (pk[1][w] & 0xFFFF0000u))
+                                   : ((pk[0][w] & 0xFFFFu) | (pk[1][w] << 16));
+        *reinterpret_cast<uint32_t*>(&tr[b][(16 * sub + i) * TR_LD + 2 * pr]) = v;
+      }
+    }
+    // rotary keys: thread = (position, 8 features); scales: thread = (block, position)
+    {
+      const int pl = ftid >> 3, part = ftid & 7, p = p0 + pl;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (p < hi) v = *reinterpret_cast<const uint4*>(g.c_rope + (cbase + p) * DR + 8 * part);
+      *reinterpret_cast<uint4*>(&ct[b][pl * CT_LD + DL + 8 * part]) = v;
+      if (ftid < (DL / QBLK) * PT) {
+        const int blk = ftid / PT, pp = ftid % PT;
+        sc_l[b][blk][pp] = (p0 + pp < hi) ? g.c_scales[(cbase + p0 + pp) * (DL / QBLK) + blk]
+                                          : 0.f;
+      }
+    }
+  };
+
+  // compute waves: the query of head h as B fragments, high or low halves by
+  // column (dims 32 ks + 8 q4 .. + 7)
+  v8bf qb[DQ / 32];
+  v4f o[DL / 16];
+  float mrun = -INFINITY, lrun = 0.f;
+  if (compute) {
+    const float* qp = g.qcat + ((size_t)t * g.H + h) * DQ + 8 * q4;
+#pragma unroll
+    for (int ks = 0; ks < DQ / 32; ++ks) {
+      const float4 a = *reinterpret_cast<const float4*>(qp + 32 * ks);
+      const float4 c = *reinterpret_cast<const float4*>(qp + 32 * ks + 4);
+      const uint4 v = make_uint4(bf16_half(a.x, lo_col) | (bf16_half(a.y, lo_col) << 16),
+                                 bf16_half(a.z, lo_col) | (bf16_half(a.w, lo_col) << 16),
+                                 bf16_half(c.x, lo_col) | (bf16_half(c.y, lo_col) << 16),
+                                 bf16_half(c.z, lo_col) | (bf16_half(c.w, lo_col) << 16));
+      qb[ks] = __builtin_bit_cast(v8bf, v);
+    }
+#pragma unroll
+    for (int i = 0; i < DL / 16; ++i) o[i] = v4f{0.f, 0.f, 0.f, 0.f};
+  }
+  auto step = [&](int b, int p0) {
+    // ---- scores: S^T[pos, column] for positions p0 + 16 pt + 4 q4 + i
+    v4f s[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int blk = 0; blk <= DL / QBLK; ++blk) {   // four latent blocks, then the rotary key
+#pragma unroll
+      for (int pt = 0; pt < 2; ++pt) {
+        v4f acc = {0.f, 0.f, 0.f, 0.f};
+        const uint16_t* ap = &ct[b][(16 * pt + l16) * CT_LD + 8 * q4];
+        const int ks0 = blk * 4, ks1 = blk < DL / QBLK ? ks0 + 4 : DQ / 32;
+#pragma unroll
+        for (int ks = ks0; ks < ks1; ++ks) {
+          const uint4 av = *reinterpret_cast<const uint4*>(ap + 32 * ks);
+          acc = mfma_bf16(__builtin_bit_cast(v8bf, av), qb[ks], acc);
+        }
+        if (blk < DL / QBLK) {
+          const float4 sc = *reinterpret_cast<const float4*>(&sc_l[b][blk][16 * pt + 4 * q4]);
+          s[pt][0] = fmaf(sc.x, acc[0], s[pt][0]);
+          s[pt][1] = fmaf(sc.y, acc[1], s[pt][1]);
+          s[pt][2] = fmaf(sc.z, acc[2], s[pt][2]);
+          s[pt][3] = fmaf(sc.w, acc[3], s[pt][3]);
+        } else {
+          s[pt] += acc;
+        }
+        // operand reads stay with their block (hoisting all 18 at once would
+        // exceed the register budget)
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // the head's two columns (high and low query halves) add to its score
+#pragma unroll
+    for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[pt][i] += __shfl_xor(s[pt][i], HPW);
+    // causal mask and the step's maximum for head h (position p0 <= qpos is
+    // visible, so the maximum is finite)
+    float mx = -INFINITY;
+#pragma unroll
+    for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int p = p0 + 16 * pt + 4 * q4 + i;
+        if (p >= my_end || p >= hi) s[pt][i] = -INFINITY;
+        mx = fmaxf(mx, s[pt][i]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mnew = fmaxf(mrun, mx);
+    const float alpha = __expf(mrun - mnew);
+    float ps[2][4], lsum = 0.f;
+#pragma unroll
+    for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ps[pt][i] = __expf(s[pt][i] - mnew);
+        lsum += ps[pt][i];
+      }
+    lsum += __shfl_xor(lsum, 16);
+    lsum += __shfl_xor(lsum, 32);
+    lrun = lrun * alpha + lsum;
+    mrun = mnew;
+    // ---- O^T[latent, column] = alpha O^T + C_b^T (p scale_b)^T, block by block
+#pragma unroll
+    for (int blk = 0; blk < DL / QBLK; ++blk) {
+      const float4 s0 = *reinterpret_cast<const float4*>(&sc_l[b][blk][4 * q4]);
+      const float4 s1 = *reinterpret_cast<const float4*>(&sc_l[b][blk][16 + 4 * q4]);
+      const uint4 pv = make_uint4(
+          bf16_half(ps[0][0] * s0.x, lo_col) | (bf16_half(ps[0][1] * s0.y, lo_col) << 16),
+          bf16_half(ps[0][2] * s0.z, lo_col) | (bf16_half(ps[0][3] * s0.w, lo_col) << 16),
+          bf16_half(ps[1][0] * s1.x, lo_col) | (bf16_half(ps[1][1] * s1.y, lo_col) << 16),
+          bf16_half(ps[1][2] * s1.z, lo_col) | (bf16_half(ps[1][3] * s1.w, lo_col) << 16));
+      const v8bf pb = __builtin_bit_cast(v8bf, pv);
+#pragma unroll
+      for (int nt = blk * 8; nt < blk * 8 + 8; ++nt) {
+        const uint16_t* tp = &tr[b][(16 * nt + l16) * TR_LD + 4 * q4];
+        const uint2 a0 = *reinterpret_cast<const uint2*>(tp);
+        const uint2 a1 = *reinterpret_cast<const uint2*>(tp + 16);
+        const v8bf av = __builtin_bit_cast(v8bf, make_uint4(a0.x, a0.y, a1.x, a1.y));
+        o[nt] = mfma_bf16(av, pb, o[nt] * alpha);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // The two roles run separate loops with the same barriers (one before the
+  // first step, one after each step), so the compute waves' query fragments
+  // and accumulators are not live across the fill code.
+  if (!compute) {
+    if (lo < hi) fill(0, lo);
+    __syncthreads();
+    int b = 0;
+    for (int p0 = lo; p0 < hi; p0 += PT, b ^= 1) {
+      if (p0 + PT < hi) fill(b ^ 1, p0 + PT);
+      __syncthreads();
+    }
+    return;
+  }
+  __syncthreads();
+  {
+    int b = 0;
+    for (int p0 = lo; p0 < hi; p0 += PT, b ^= 1) {
+      if (active && p0 < my_end) step(b, p0);
+      __syncthreads();
+    }
+  }
+  if (!active) return;
+  // a head's two columns (contributions of the high and low p halves) add
+  // to its output; the high-column lanes write O^T, latent features
+  // 16 nt + 4 q4 + i
+#pragma unroll
+  for (int nt = 0; nt < DL / 16; ++nt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[nt][i] += __shfl_xor(o[nt][i], HPW);
+  if (lo_col) return;
+  const size_t pidx = ((size_t)split * g.T + t) * g.H + h;
+  float* po = g.part_o + pidx * DL;
+#pragma unroll
+  for (int nt = 0; nt < DL / 16; ++nt)
+    *reinterpret_cast<float4*>(po + 16 * nt + 4 * q4) =
+        make_float4(o[nt][0], o[nt][1], o[nt][2], o[nt][3]);
+  if (q4 == 0) {
+    g.part_ml[pidx * 2] = mrun;
+    g.part_ml[pidx * 2 + 1] = lrun;
+  }
+}
+
+// ------------------------------------------- merge, value up-projection
+constexpr int VU_TB = 16;   // tokens per workgroup
+
+// For head h and 16 tokens: merge the position splits (m, l, O) into
+// o_lat = sum_j p_j c_j / sum_j p_j, apply W_uv (rows h*(DN+DV)+DN .. + DV - 1,
+// one 128-row scale block) in fp32, write the 128 outputs as one 1x128 block
+// of the output projection's input (codes + scale) and, if attn != null, as
+// fp32.
+__global__ __launch_bounds__(256) void mla_vup_kernel(
+    int T, int H, int nsplit, const float* __restrict__ part_o, const float* __restrict__ part_ml,
+    const uint8_t* __restrict__ w_kvb, const float* __restrict__ s_kvb,
+    uint8_t* __restrict__ o_q, float* __restrict__ o_s, float* __restrict__ attn) {
+  const int h = blockIdx.x, t0 = blockIdx.y * VU_TB, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  __shared__ __attribute__((aligned(16))) uint8_t wv[DV * DL];      // 64 KiB of codes
+  __shared__ __attribute__((aligned(16))) float ol[VU_TB][DL];      // 32 KiB
+  __shared__ float half_sum[VU_TB][DV];
+  const uint8_t* wsrc = w_kvb + ((size_t)h * (DN + DV) + DN) * DL;
+  for (int i = tid; i < DV * DL / 16; i += 256)
+    reinterpret_cast<uint4*>(wv)[i] = reinterpret_cast<const uint4*>(wsrc)[i];
+  // merge: thread handles latent features tid and tid + 256 of every token
+  for (int tt = 0; tt < VU_TB; ++tt) {
+    const int t = t0 + tt;
+    if (t >= T) {
+      ol[tt][tid] = ol[tt][tid + 256] = 0.f;
+      continue;
+    }
+    float M = -INFINITY;
+    for (int s = 0; s < nsplit; ++s)
+      M = fmaxf(M, part_ml[(((size_t)s * T + t) * H + h) * 2]);
+    float L = 0.f, a0 = 0.f, a1 = 0.f;
+    for (int s = 0; s < nsplit; ++s) {
+      const size_t pi = ((size_t)s * T + t) * H + h;
+      const float m = part_ml[pi * 2];
+      if (m == -INFINITY) continue;
+      const float wgt = __expf(m - M);
+      L += part_ml[pi * 2 + 1] * wgt;
+      a0 += part_o[pi * DL + tid] * wgt;
+      a1 += part_o[pi * DL + tid + 256] * wgt;
+    }
+    ol[tt][tid] = a0 / L;
+    ol[tt][tid + 256] = a1 / L;
+  }
+  __syncthreads();
+  // o[t, d] = sum_r W_uv[d, r] * s(r / 128) * o_lat[t, r]: thread (d, half of r)
+  const int d = tid & (DV - 1), half = tid >> 7;
+  const float* sv = s_kvb + (size_t)(2 * h + 1) * (DL / QBLK);
+  float acc[VU_TB];
+#pragma unroll
+  for (int tt = 0; tt < VU_TB; ++tt) acc[tt] = 0.f;
+  for (int r = 256 * half; r < 256 * half + 256; r += 4) {
+    const uint32_t c4 = *reinterpret_cast<const uint32_t*>(&wv[d * DL + r]);
+    const v2f wa = __builtin_amdgcn_cvt_pk_f32_fp8((int)c4, false);
+    const v2f wb = __builtin_amdgcn_cvt_pk_f32_fp8((int)c4, true);
+    const float sc = sv[r / QBLK];
+    const float w0 = wa[0] * sc, w1 = wa[1] * sc, w2 = wb[0] * sc, w3 = wb[1] * sc;
+#pragma unroll
+    for (int tt = 0; tt < VU_TB; ++tt) {
+      const float4 x = *reinterpret_cast<const float4*>(&ol[tt][r]);
+      acc[tt] = fmaf(w0, x.x, fmaf(w1, x.y, fmaf(w2, x.z, fmaf(w3, x.w, acc[tt]))));
+    }
+  }
+  if (half == 1)
+    for (int tt = 0; tt < VU_TB; ++tt) half_sum[tt][d] = acc[tt];
+  __syncthreads();
+  // waves 0 and 1 hold d = 0..127 of every token: block maxima, then codes
+  __shared__ float bmax[VU_TB][2];
+  if (half == 0)
+    for (int tt = 0; tt < VU_TB; ++tt) {
+      acc[tt] += half_sum[tt][d];
+      float amax = fabsf(acc[tt]);
+#pragma unroll
+      for (int m = 1; m < 64; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
+      if (lane == 0) bmax[tt][wave] = amax;
+    }
+  __syncthreads();
+  if (half == 1) return;
+  for (int tt = 0; tt < VU_TB; ++tt) {
+    const int t = t0 + tt;
+    const float v = acc[tt];
+    const float amax = fmaxf(bmax[tt][0], bmax[tt][1]);
+    if (t < T) {
+      const float s = fp8_scale(amax);
+      const uint32_t q = cvt4_e4m3(clamp_fp8(v / s), 0.f, 0.f, 0.f);
+      o_q[(size_t)t * H * DV + h * DV + d] = (uint8_t)(q & 0xFFu);
+      if (d == 0) o_s[(size_t)t * H + h] = s;
+      if (attn) attn[(size_t)t * H * DV + h * DV + d] = v;
+    }
+  }
+}
+
+}  // namespace
+
+// ------------------------------------------------------------- launchers
+hipError_t launch_pack_rows(int n_pad, int K, const uint8_t* src0, int n0, const uint8_t* src1,
+                            int n1, const float* s0, const float* s1, uint8_t* dst_codes,
+                            float* dst_scales, hipStream_t s) {
+  const long n = (long)n_pad * K / 16;
+  pack_rows_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(n_pad, K, src0, n0, src1, n1,
+                                                               dst_codes);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int kb = K / QBLK, nb = n_pad / QBLK;
+  pack_row_scales_kernel<<<(nb * kb + 255) / 256, 256, 0, s>>>(
+      nb, kb, s0, (n0 + QBLK - 1) / QBLK, s1, (n1 + QBLK - 1) / QBLK, dst_scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_dense_tiles(int T, int bm, int32_t* offsets, int32_t* mt_start,
+                              int32_t* tile_group, hipStream_t s) {
+  const int n = (T + bm - 1) / bm;
+  dense_tiles_kernel<<<(max(n, 1) + 255) / 256, 256, 0, s>>>(T, bm, offsets, mt_start,
+                                                              tile_group);
+  return hipGetLastError();
+}
+
+hipError_t launch_slice_sum(int T, int ncol, int ld, int nsplit, const float* part,
+                            const uint16_t* residual, void* out, int out_ld, hipStream_t s) {
+  const long n = (long)T * (ncol / 4);
+  slice_sum_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(T, ncol, ld, nsplit, part,
+                                                               residual, out, out_ld);
+  return hipGetLastError();
+}
+
+hipError_t launch_mla_latent(int T, int q_lora, int qkv_ld, float eps, const float* qkv,
+                             const uint16_t* g_qa, const uint16_t* g_kva, const double* inv_freq,
+                             const int32_t* cached_len, int n_new, int max_len, uint8_t* qa_q,
+                             float* qa_s, uint8_t* c_codes, float* c_scales, uint16_t* c_rope,
+                             hipStream_t s) {
+  mla_latent_kernel<<<T, 256, 0, s>>>(q_lora, qkv_ld, eps, qkv, g_qa, g_kva, inv_freq,
+                                      cached_len, n_new, max_len, qa_q, qa_s, c_codes, c_scales,
+                                      c_rope);
+  return hipGetLastError();
+}
+
+hipError_t launch_mla_qabsorb(int T, int H, float smscale, const float* q, const uint8_t* w_kvb,
+                              const float* s_kvb, const double* inv_freq,
+                              const int32_t* cached_len, int n_new, int max_len, float* qcat,
+                              hipStream_t s) {
+  dim3 grid(H, (T + QA_TB - 1) / QA_TB);
+  mla_qabsorb_kernel<<<grid, 256, 0, s>>>(T, H, smscale, q, w_kvb, s_kvb, inv_freq, cached_len,
+                                          n_new, max_len, qcat);
+  return hipGetLastError();
+}
+
+hipError_t launch_mla_attn(int T, int H, int n_seq, int n_new, int max_len, int nsplit,
+                           int chunk, const uint8_t* c_codes, const float* c_scales,
+                           const uint16_t* c_rope, const float* qcat,
+                           const int32_t* cached_len, float* part_o, float* part_ml,
+                           hipStream_t s) {
+  AttnArgs a{};
+  a.c_codes = c_codes;
+  a.c_scales = c_scales;
+  a.c_rope = c_rope;
+  a.qcat = qcat;
+  a.cached_len = cached_len;
+  a.part_o = part_o;
+  a.part_ml = part_ml;
+  a.T = T;
+  a.H = H;
+  a.n_new = n_new;
+  a.max_len = max_len;
+  a.nsplit = nsplit;
+  a.chunk = chunk;
+  a.mode = (n_new == 1 && H % 32 == 0) ? 0 : 1;
+  a.items_per_split = a.mode == 0 ? T * (H / 32) : n_seq * ((n_new + 3) / 4) * (H / 8);
+  mla_attn_kernel<<<a.items_per_split * nsplit, 512, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_mla_vup(int T, int H, int nsplit, const float* part_o, const float* part_ml,
+                          const uint8_t* w_kvb, const float* s_kvb, uint8_t* o_q, float* o_s,
+                          float* attn, hipStream_t s) {
+  dim3 grid(H, (T + VU_TB - 1) / VU_TB);
+  mla_vup_kernel<<<grid, 256, 0, s>>>(T, H, nsplit, part_o, part_ml, w_kvb, s_kvb, o_q, o_s,
+                                      attn);
+  return hipGetLastError();
+}
+
+}  // namespace k2

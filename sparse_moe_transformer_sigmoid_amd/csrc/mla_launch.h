@@ -1,0 +1,43 @@
+// Internal launchers of the MLA attention kernels (host side).  Every launcher
+// enqueues on `s` and returns hipGetLastError() of its launches.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "k2_launch.h"
+
+namespace k2 {
+
+// packing of one projection matrix (or two stacked) into the grouped GEMM's
+// down-form layout, zero rows up to n_pad; scales padded with 1.0
+hipError_t launch_pack_rows(int n_pad, int K, const uint8_t* src0, int n0, const uint8_t* src1,
+                            int n1, const float* s0, const float* s1, uint8_t* dst_codes,
+                            float* dst_scales, hipStream_t s);
+// tables of one group of T rows for the grouped GEMM
+hipError_t launch_dense_tiles(int T, int bm, int32_t* offsets, int32_t* mt_start,
+                              int32_t* tile_group, hipStream_t s);
+// the dense FP8 GEMM rows[k, T, d] = partial sums of slice k (a.rows, a.d = padded N);
+// tt = 1, 2 or 4 (16-, 32-, 64-row m-tiles)
+hipError_t launch_gemm_dense(int tt, int nsplit, const GemmArgs& a, int grid, hipStream_t s);
+// sum of K slices, optionally + bf16 residual and rounding to bf16
+hipError_t launch_slice_sum(int T, int ncol, int ld, int nsplit, const float* part,
+                            const uint16_t* residual, void* out, int out_ld, hipStream_t s);
+hipError_t launch_mla_latent(int T, int q_lora, int qkv_ld, float eps, const float* qkv,
+                             const uint16_t* g_qa, const uint16_t* g_kva, const double* inv_freq,
+                             const int32_t* cached_len, int n_new, int max_len, uint8_t* qa_q,
+                             float* qa_s, uint8_t* c_codes, float* c_scales, uint16_t* c_rope,
+                             hipStream_t s);
+hipError_t launch_mla_qabsorb(int T, int H, float smscale, const float* q, const uint8_t* w_kvb,
+                              const float* s_kvb, const double* inv_freq,
+                              const int32_t* cached_len, int n_new, int max_len, float* qcat,
+                              hipStream_t s);
+hipError_t launch_mla_attn(int T, int H, int n_seq, int n_new, int max_len, int nsplit,
+                           int chunk, const uint8_t* c_codes, const float* c_scales,
+                           const uint16_t* c_rope, const float* qcat,
+                           const int32_t* cached_len, float* part_o, float* part_ml,
+                           hipStream_t s);
+hipError_t launch_mla_vup(int T, int H, int nsplit, const float* part_o, const float* part_ml,
+                          const uint8_t* w_kvb, const float* s_kvb, uint8_t* o_q, float* o_s,
+                          float* attn, hipStream_t s);
+
+}  // namespace k2

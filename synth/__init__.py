@@ -1,6 +1,9 @@
-"""Seeded synthetic workloads for the K2 MoE layer (shapes and input recipe only)."""
+"""Seeded synthetic workloads for the K2 MoE layer and the MLA attention sub-layer
+(shapes and input recipe only)."""
 from .configs import (ALL, FMT_F32, FMT_FP8, K2_DECODE, K2_DENSE, K2_EP8_SHARD, K2_PREFILL,
                       K2_SKEWED, TINY, MoEShape, small_fp8)
+from .mla import (MLA_K2_DECODE, MLA_K2_PREFILL, MLAInputs, MLAShape, generate_mla,
+                  small_mla)
 from .gen import (MoEInputs, bias_vector, block_quantize_weight, generate,
                   generate_router_inputs, with_workload)
 
@@ -8,4 +11,5 @@ __all__ = ["ALL", "FMT_F32", "FMT_FP8", "K2_DECODE", "K2_DENSE", "K2_EP8_SHARD",
            "K2_SKEWED",
            "TINY", "MoEShape", "small_fp8", "MoEInputs", "block_quantize_weight", "generate",
            "generate_router_inputs", "bias_vector",
-           "with_workload"]
+           "with_workload", "MLAShape", "MLAInputs", "MLA_K2_DECODE", "MLA_K2_PREFILL",
+           "generate_mla", "small_mla"]
