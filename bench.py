@@ -14,9 +14,12 @@ decode step, its timed steps replayed from a HIP graph of moe_forward; --eager
 times plain launches), the dominant kernel's roofline fraction measured with
 HIP events inside an eager timed region, the whole layer's compulsory bytes
 over the step time, the same for the 8192-token prefill, the 16384-token
-skewed-routing step and the 4096-token dense FFN, the shader clock the driver
-reports while decode and prefill run (sampled from sysfs after the timed
-steps), and the CPU oracle timed on the whole decode batch.
+skewed-routing step and the 4096-token dense FFN, the MLA attention
+sub-layer at decode (64 sequences over 4,096 cached positions) and prefill
+(2 x 4,096 tokens) with its attention kernel against its roofline, the
+shader clock the driver reports while decode and prefill run (sampled from
+sysfs after the timed steps), and the CPU oracle timed on the whole decode
+batch.
 """
 from __future__ import annotations
 
@@ -33,6 +36,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer tokens/s at K2 shape (64-tok decode, 8K prefill); % of roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 # HBM bytes per launch of the gate/up GEMM, from rocprofv3 --pmc FETCH_SIZE (x2.000,
 # the factor a 1 GiB copy probe gives) + WRITE_SIZE (x1.000), see
 # profiles/gemm_gateup_k2_decode.md; valid only for the GEMM sources whose combined
@@ -79,6 +83,8 @@ def parse():
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the prefill, skewed-routing and dense-FFN lines")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-mla", action="store_true",
+                    help="skip the MLA attention decode and prefill lines")
     ap.add_argument("--eager", action="store_true",
                     help="time decode with eager launches instead of a HIP graph")
     ap.add_argument("--cpu-tokens", type=int, default=64,
@@ -108,8 +114,8 @@ def timed(layer, x, steps, warmup):
     for _ in range(warmup):
         layer.forward(x, out)
     torch.cuda.synchronize()
-    ms = (C.c_double * 8)()
-    n = (C.c_int64 * 8)()
+    ms = (C.c_double * len(L.STAGES))()
+    n = (C.c_int64 * len(L.STAGES))()
     L.check("moe_profile_read", lib.moe_profile_read(ms, n, 1))
     L.check("moe_profile_enable", lib.moe_profile_enable(1))
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -210,6 +216,81 @@ def secondary_line(r, workload, sclk=None):
         "gateup_frac_fp8_peak_at_sclk":
             r["gu_tflops"] / (FP8_PEAK_TFLOPS * sclk / 2400.0) if sclk else None,
         "stage_ms": r["stage"]}
+
+
+def mla_line(shape, steps, warmup):
+    """One MLA attention workload: whole sub-layer time (HIP events on the
+    launch stream), per-stage times, and the attention kernel against its
+    roofline.  Decode is bound by HBM: per step it must read every attended
+    cache position (656 B: 512 latent codes, 4 scales, 64 bf16 rotary
+    features) and the absorbed queries and write the latent outputs.  Prefill
+    is bound by the bf16 MFMA: 2 (576 + 512) flops per (query, head, visible
+    position)."""
+    import numpy as np
+    import torch
+
+    import synth
+    from sparse_moe_transformer_sigmoid_amd import _lib as L
+    from sparse_moe_transformer_sigmoid_amd.mla import K2MLA
+
+    lib = L.load()
+    inp = synth.generate_mla(shape, seed=0, device="cuda")
+    layer = K2MLA(inp)
+    cache = inp.fresh_cache()
+    out = torch.empty_like(inp.x)
+    S, n = shape.n_seq, shape.n_new
+    for _ in range(warmup):
+        layer.forward(inp.x, inp.cached_len, cache, S, n, out=out)
+    torch.cuda.synchronize()
+    nst = len(L.STAGES)
+    ms_a, n_a = (C.c_double * nst)(), (C.c_int64 * nst)()
+    L.check("moe_profile_read", lib.moe_profile_read(ms_a, n_a, 1))
+    L.check("moe_profile_enable", lib.moe_profile_enable(1))
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        layer.forward(inp.x, inp.cached_len, cache, S, n, out=out)
+    stop.record()
+    torch.cuda.synchronize()
+    L.check("moe_profile_enable", lib.moe_profile_enable(0))
+    L.check("moe_profile_read", lib.moe_profile_read(ms_a, n_a, 1))
+    step_ms = start.elapsed_time(stop) / steps
+    stage = {nm: ms_a[i] / steps for i, nm in enumerate(L.STAGES) if nm.startswith("mla_")}
+    T, H = shape.tokens, shape.n_heads
+    cached = np.asarray(shape.cached, dtype=np.int64)
+    visible = int(sum(int(c) * n + n * (n + 1) // 2 for c in cached))   # (query, position) pairs
+    attended = int(np.sum(cached + n))                                  # cache rows per sequence
+    row_bytes = shape.kv_lora + 4 * (shape.kv_lora // 128) + 2 * shape.qk_rope
+    attn_bytes = attended * row_bytes + T * H * (shape.kv_lora + shape.qk_rope) * 4 + \
+        T * H * shape.kv_lora * 4
+    attn_flops = 2.0 * visible * H * ((shape.kv_lora + shape.qk_rope) + shape.kv_lora)
+    a_ms = stage["mla_attn"]
+    w_bytes = sum(v.numel() * v.element_size() for v in inp.w.values())
+    layer_bytes = w_bytes + attended * row_bytes + 2 * T * shape.d_model * 2
+    line = {"workload": shape.name, "sequences": S, "new_tokens_per_sequence": n,
+            "cached_per_sequence": sorted(set(int(c) for c in cached)), "tokens": T,
+            "ms_per_step": step_ms, "value": T / (step_ms * 1e-3), "unit": "tokens/s",
+            "stage_ms": stage, "layer_bytes": layer_bytes,
+            "layer_frac_hbm": layer_bytes / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    ai = attn_flops / attn_bytes
+    if ai < BF16_PEAK_TFLOPS * 1e3 / HBM_PEAK_GBS:
+        gbs = attn_bytes / (a_ms * 1e-3) / 1e9
+        line["roofline"] = {"kernel": "mla_attn_kernel", "bound": "hbm", "achieved": gbs,
+                            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                            "kernel_ms": a_ms, "algorithmic_bytes": attn_bytes,
+                            "algorithmic_flops": attn_flops, "arithmetic_intensity": ai}
+    else:
+        tf = attn_flops / (a_ms * 1e-3) / 1e12
+        line["roofline"] = {"kernel": "mla_attn_kernel", "bound": "mfma", "achieved": tf,
+                            "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                            "frac": tf / BF16_PEAK_TFLOPS, "kernel_ms": a_ms,
+                            "algorithmic_bytes": attn_bytes, "algorithmic_flops": attn_flops,
+                            "arithmetic_intensity": ai,
+                            "note": "bf16 MFMA peak; every product is formed as high and low "
+                                    "bf16 halves, so the executed MFMA work is twice the "
+                                    "algorithmic flops"}
+    del layer, inp, cache
+    return line
 
 
 def sclk_file():
@@ -403,6 +484,12 @@ def main():
         line["dense"] = secondary_line(rd, dense.shape.name)
         print(f"# dense {rd['ms']:.3f} ms", file=sys.stderr, flush=True)
         del dlayer, dense
+    if args.workload == "decode" and not args.no_mla:
+        line["mla"] = {}
+        for nm, shp_m in (("decode", synth.MLA_K2_DECODE), ("prefill", synth.MLA_K2_PREFILL)):
+            line["mla"][nm] = mla_line(shp_m, max(3, args.steps // 2), 2)
+            print(f"# mla {nm} {line['mla'][nm]['ms_per_step']:.3f} ms", file=sys.stderr,
+                  flush=True)
     if not args.no_clock:
         layer.use_router(inp)
         line["sclk_mhz"] = sclk_during(layer, inp.x)

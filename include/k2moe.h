@@ -208,6 +208,22 @@ moe_status moe_forward(const moe_config* cfg, int64_t T, const void* x, const vo
                        const void* w_router, const float* bias, const void* packed_w,
                        void* out, void* ws, size_t ws_bytes, void* stream);
 
+/* moe_forward without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  The workspace is a static device array of 48 MiB
+ * in the library, one copy per GPU, allocated with the code object and held
+ * until the process ends; its device address is looked up once per device
+ * (hipGetSymbolAddress) on the first call there.  A batch whose
+ * moe_workspace_bytes(MOE_WS_FORWARD) exceeds 48 MiB is rejected with
+ * MOE_ERR_WORKSPACE (Kimi K2 shape: up to 130 tokens).  No part of the array
+ * needs to start zeroed (every workspace word is written before it is read).
+ * All calls on one GPU share the array: calls that overlap in time on one GPU
+ * (other streams, other host threads) race and must be serialised by the
+ * caller.  Results are bitwise those of moe_forward. */
+moe_status moe_forward_noalloc(const moe_config* cfg, int64_t T, const void* x,
+                               const void* norm_w, const void* w_router, const float* bias,
+                               const void* packed_w, void* out, void* stream);
+
 /* ---- diagnostics: per-stage timing with HIP events ---------------------
  * While profiling is on, every entry point records a HIP event before and
  * after each of its kernel stages, on the caller's stream.  This is the only
@@ -224,7 +240,12 @@ typedef enum {
   MOE_STAGE_GATEUP = 5,      /* grouped gate/up GEMM + SwiGLU + requantisation */
   MOE_STAGE_DOWN = 6,        /* grouped down GEMM */
   MOE_STAGE_COMBINE = 7,     /* weighted combine + residual */
-  MOE_STAGE_COUNT = 8
+  /* the MLA attention entry points of k2mla.h */
+  MOE_STAGE_MLA_PROJ = 8,    /* input RMSNorm and quantisation, the four FP8 projections */
+  MOE_STAGE_MLA_LATENT = 9,  /* latent norms, cache entries, query absorption */
+  MOE_STAGE_MLA_ATTN = 10,   /* attention over the latent cache */
+  MOE_STAGE_MLA_VUP = 11,    /* split merge, value up-projection, 1x128 quantisation */
+  MOE_STAGE_COUNT = 12
 } moe_stage;
 
 moe_status moe_profile_enable(int32_t on);

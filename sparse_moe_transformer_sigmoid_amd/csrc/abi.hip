@@ -108,6 +108,17 @@ class Stage {
   bool active_ = false;
 };
 
+}  // namespace
+
+// stage timing for the other translation units of the library (the MLA calls)
+void* k2::profile_begin(int stage, hipStream_t s) {
+  Stage* st = new Stage(stage, s);
+  return st;
+}
+void k2::profile_end(void* handle) { delete static_cast<Stage*>(handle); }
+
+namespace {
+
 constexpr size_t ALIGN = 256;
 size_t align_up(size_t x) { return (x + ALIGN - 1) & ~(ALIGN - 1); }
 
@@ -437,6 +448,32 @@ moe_status run_experts(const Dims& D, const Layout& L, void* ws, const void* xq,
   return MOE_OK;
 }
 
+// ---- the allocation-free forward (moe_forward_noalloc): its workspace is a
+// static device array, one copy per GPU, held until the process ends.
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)48 << 20;   // K2 shape: up to 130 tokens
+static __device__ __align__(256) uint8_t scratch[NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[MAX_DEVICES] = {};
+
+// The device address of `scratch` on the current device, looked up once per
+// device (each GPU holds its own copy; the host-side name is only a handle).
+moe_status scratch_of_current_device(void** ptr) {
+  int dev = -1;
+  K2_HIP(hipGetDevice(&dev));
+  K2_REQUIRE(dev >= 0 && dev < MAX_DEVICES, MOE_ERR_UNSUPPORTED, "device index beyond 63");
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void* p = nullptr;
+    K2_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    K2_REQUIRE(p != nullptr, MOE_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_dev[dev] = p;
+  }
+  *ptr = g_scratch_dev[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -701,6 +738,24 @@ moe_status moe_forward(const moe_config* cfg, int64_t T, const void* x, const vo
   K2_HIP(k2::launch_combine(D.fp8, !D.fp8, (int)T, D.d, D.k, rows, pair_row, w, 0, shared, x, out,
                             s));
   return MOE_OK;
+}
+
+moe_status moe_forward_noalloc(const moe_config* cfg, int64_t T, const void* x,
+                               const void* norm_w, const void* w_router, const float* bias,
+                               const void* packed_w, void* out, void* stream) {
+  Dims D;
+  moe_status st = check_cfg(cfg, &D);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(T, &D)) != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  const size_t need = layout(D, MOE_WS_FORWARD).total;
+  K2_REQUIRE(need <= NOALLOC_SCRATCH_BYTES, MOE_ERR_WORKSPACE,
+             "moe_forward_noalloc: " + std::to_string(T) + " tokens need " +
+                 std::to_string(need) + " bytes of workspace; the static scratch array holds " +
+                 std::to_string(NOALLOC_SCRATCH_BYTES) + " (Kimi K2 shape: up to 130 tokens)");
+  void* ws = nullptr;
+  if ((st = scratch_of_current_device(&ws)) != MOE_OK) return st;
+  return moe_forward(cfg, T, x, norm_w, w_router, bias, packed_w, out, ws, need, stream);
 }
 
 }  // extern "C"

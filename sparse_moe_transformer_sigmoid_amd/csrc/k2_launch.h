@@ -11,6 +11,15 @@ namespace k2 {
 
 // the thread-local text moe_last_error() returns
 std::string& error_text();
+// per-stage HIP-event timing (moe_profile_enable): a stage's launches are
+// bracketed by profile_begin / profile_end on their stream
+void* profile_begin(int stage, hipStream_t s);
+void profile_end(void* handle);
+struct ProfileScope {
+  void* h;
+  ProfileScope(int stage, hipStream_t s) : h(profile_begin(stage, s)) {}
+  ~ProfileScope() { profile_end(h); }
+};
 
 // ---- norm + quant + router (norm_router.hip)
 hipError_t launch_norm_quant(bool fp8, int T, int d, float eps, const void* x, const void* gamma,

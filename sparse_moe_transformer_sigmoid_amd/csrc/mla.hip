@@ -34,7 +34,10 @@ constexpr int DN = 128;           // query/key features without position (qk_nop
 constexpr int DV = 128;           // value features (v_head)
 constexpr int PT = 32;            // cache positions per attention step
 constexpr int CT_LD = DQ + 8;     // bf16 stride of a row-major cache row in LDS
-constexpr int TR_LD = PT + 8;     // bf16 stride of a transposed latent row in LDS
+// bf16 stride of a transposed latent row in LDS: 18 dwords, so the four
+// 16-row chunks a fill wave writes in one instruction fall on two bank halves
+// and the 16 rows a compute wave reads on 16 distinct even banks
+constexpr int TR_LD = PT + 4;
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
@@ -301,6 +304,12 @@ struct AttnArgs {
   int T, H, n_new, max_len, nsplit, chunk, mode, items_per_split;
 };
 
+// the value of the lane 8 apart in the same 16-lane row (a row rotated by 8)
+__device__ __forceinline__ float xor8(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+      0, __builtin_bit_cast(int, v), 0x128 /* row_ror:8 */, 0xF, 0xF, false));
+}
+
 __device__ __forceinline__ v4f mfma_bf16(v8bf a, v8bf b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -355,23 +364,47 @@ __global__ __launch_bounds__(512, 1) void mla_attn_kernel(const AttnArgs g) {
   const int h = hg * HPW + (l16 & (HPW - 1));   // this lane's head
   const size_t cbase = (size_t)seq * g.max_len;
 
-  // fill waves: positions p0 .. p0 + 31 into buffer b (zeros past hi).  Item
-  // = (latent chunk of 16 features, pair of positions), two items per
-  // thread, then the rotary keys and the scales.
-  auto fill = [&](int b, int p0) {
-    const int ftid = tid - 256;
+  // fill waves: positions p0 .. p0 + 31, loaded into registers (zeros past hi)
+  // two steps before they are written into an LDS buffer, so the loads of a
+  // step have two steps of compute to arrive.  Item = (latent chunk of 16
+  // features, pair of positions), two items per thread; then the rotary keys
+  // (thread = position, 8 features) and the scales (thread = block, position).
+  const int ftid = tid - 256;
+  struct Raw {
+    uint4 cv[2][2];   // [item][position of the pair]: 16 codes each
+    uint4 rope;
+    float sc;
+  };
+  auto load_raw = [&](Raw& r, int p0) {
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
-      const int itm = ftid + 256 * it;
-      const int sub = itm >> 4, pr = itm & 15;
+      const int itm = ftid + 256 * it, sub = itm >> 4, pr = itm & 15;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int p = p0 + 2 * pr + j;
+        r.cv[it][j] = p < hi ? *reinterpret_cast<const uint4*>(g.c_codes + (cbase + p) * DL +
+                                                                16 * sub)
+                             : make_uint4(0, 0, 0, 0);
+      }
+    }
+    const int pr_ = p0 + (ftid >> 3);
+    r.rope = pr_ < hi ? *reinterpret_cast<const uint4*>(g.c_rope + (cbase + pr_) * DR +
+                                                        8 * (ftid & 7))
+                      : make_uint4(0, 0, 0, 0);
+    r.sc = 0.f;
+    if (ftid < (DL / QBLK) * PT) {
+      const int pp = p0 + ftid % PT;
+      if (pp < hi) r.sc = g.c_scales[(cbase + pp) * (DL / QBLK) + ftid / PT];
+    }
+  };
+  auto store_raw = [&](int b, const Raw& r) {
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int itm = ftid + 256 * it, sub = itm >> 4, pr = itm & 15;
       uint32_t pk[2][8];   // bf16 pairs: codes 2k, 2k+1 of position 2 pr + j
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const int pl = 2 * pr + j, p = p0 + pl;
-        uint4 cv = make_uint4(0, 0, 0, 0);
-        if (p < hi)
-          cv = *reinterpret_cast<const uint4*>(g.c_codes + (cbase + p) * DL + 16 * sub);
-        const uint32_t w4[4] = {cv.x, cv.y, cv.z, cv.w};
+        const uint32_t w4[4] = {r.cv[it][j].x, r.cv[it][j].y, r.cv[it][j].z, r.cv[it][j].w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           pk[j][2 * k] = __builtin_bit_cast(
@@ -379,32 +412,23 @@ __global__ __launch_bounds__(512, 1) void mla_attn_kernel(const AttnArgs g) {
           pk[j][2 * k + 1] = __builtin_bit_cast(
               uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w4[k], 1.f, true));
         }
-        uint4* dst = reinterpret_cast<uint4*>(&ct[b][pl * CT_LD + 16 * sub]);
+        uint4* dst = reinterpret_cast<uint4*>(&ct[b][(2 * pr + j) * CT_LD + 16 * sub]);
         dst[0] = make_uint4(pk[j][0], pk[j][1], pk[j][2], pk[j][3]);
         dst[1] = make_uint4(pk[j][4], pk[j][5], pk[j][6], pk[j][7]);
       }
-      // transposed: feature 16 sub + i, positions 2 pr and 2 pr + 1 (order of i
-      // staggered by chunk so a wave's writes spread over the LDS banks)
+      // transposed: feature 16 sub + i, positions 2 pr and 2 pr + 1 (i is a
+      // compile-time index: a per-thread index into pk would become select
+      // chains over all its registers)
 #pragma unroll
-      for (int ii = 0; ii < 16; ++ii) {
-        const int i = (ii + sub) & 15, w = i >> 1;
+      for (int i = 0; i < 16; ++i) {
+        const int w = i >> 1;
         const uint32_t v = (i & 1) ? ((pk[0][w] >> 16) | (pk[1][w] & 0xFFFF0000u))
                                    : ((pk[0][w] & 0xFFFFu) | (pk[1][w] << 16));
         *reinterpret_cast<uint32_t*>(&tr[b][(16 * sub + i) * TR_LD + 2 * pr]) = v;
       }
     }
-    // rotary keys: thread = (position, 8 features); scales: thread = (block, position)
-    {
-      const int pl = ftid >> 3, part = ftid & 7, p = p0 + pl;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (p < hi) v = *reinterpret_cast<const uint4*>(g.c_rope + (cbase + p) * DR + 8 * part);
-      *reinterpret_cast<uint4*>(&ct[b][pl * CT_LD + DL + 8 * part]) = v;
-      if (ftid < (DL / QBLK) * PT) {
-        const int blk = ftid / PT, pp = ftid % PT;
-        sc_l[b][blk][pp] = (p0 + pp < hi) ? g.c_scales[(cbase + p0 + pp) * (DL / QBLK) + blk]
-                                          : 0.f;
-      }
-    }
+    *reinterpret_cast<uint4*>(&ct[b][(ftid >> 3) * CT_LD + DL + 8 * (ftid & 7)]) = r.rope;
+    if (ftid < (DL / QBLK) * PT) sc_l[b][ftid / PT][ftid % PT] = r.sc;
   };
 
   // compute waves: the query of head h as B fragments, high or low halves by
@@ -460,7 +484,7 @@ __global__ __launch_bounds__(512, 1) void mla_attn_kernel(const AttnArgs g) {
 #pragma unroll
     for (int pt = 0; pt < 2; ++pt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s[pt][i] += __shfl_xor(s[pt][i], HPW);
+      for (int i = 0; i < 4; ++i) s[pt][i] += xor8(s[pt][i]);
     // causal mask and the step's maximum for head h (position p0 <= qpos is
     // visible, so the maximum is finite)
     float mx = -INFINITY;
@@ -515,11 +539,30 @@ __global__ __launch_bounds__(512, 1) void mla_attn_kernel(const AttnArgs g) {
   // first step, one after each step), so the compute waves' query fragments
   // and accumulators are not live across the fill code.
   if (!compute) {
-    if (lo < hi) fill(0, lo);
+    // register ring of two steps: step k + 1 is written while step k + 3's
+    // loads are issued (positions past hi load nothing)
+    Raw ra, rb;
+    if (lo < hi) {
+      load_raw(ra, lo);
+      load_raw(rb, lo + PT);
+      store_raw(0, ra);
+      load_raw(ra, lo + 2 * PT);
+    }
     __syncthreads();
     int b = 0;
-    for (int p0 = lo; p0 < hi; p0 += PT, b ^= 1) {
-      if (p0 + PT < hi) fill(b ^ 1, p0 + PT);
+    for (int p0 = lo; p0 < hi; p0 += 2 * PT) {
+      // step p0 (buffer b) is being computed; write step p0 + PT from rb
+      if (p0 + PT < hi) {
+        store_raw(b ^ 1, rb);
+        load_raw(rb, p0 + 3 * PT);
+      }
+      __syncthreads();
+      if (p0 + PT >= hi) break;
+      // step p0 + PT (buffer b ^ 1) is being computed; write step p0 + 2 PT from ra
+      if (p0 + 2 * PT < hi) {
+        store_raw(b, ra);
+        load_raw(ra, p0 + 4 * PT);
+      }
       __syncthreads();
     }
     return;
@@ -539,7 +582,7 @@ __global__ __launch_bounds__(512, 1) void mla_attn_kernel(const AttnArgs g) {
 #pragma unroll
   for (int nt = 0; nt < DL / 16; ++nt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[nt][i] += __shfl_xor(o[nt][i], HPW);
+    for (int i = 0; i < 4; ++i) o[nt][i] += xor8(o[nt][i]);
   if (lo_col) return;
   const size_t pidx = ((size_t)split * g.T + t) * g.H + h;
   float* po = g.part_o + pidx * DL;

@@ -308,36 +308,56 @@ moe_status run_mla(const mla_config* cfg, int32_t S, int32_t n, int32_t L, const
   const uint8_t* kvb = pk + P.kvb_codes;
   const float* kvbs = reinterpret_cast<const float*>(pk + P.kvb_scales);
 
-  // input RMSNorm + 1x128 quantisation
-  M_HIP(k2::launch_norm_quant(true, T, D.d, D.eps, x, norm_w, at<void>(ws, W.hbuf), xq, xs, s));
-  // [q_a; kv_a] = h [W_qa; W_kva]^T
-  if ((st = run_gemm(D, T, D.n_qkv_pad, D.d, W.ns_qkv, xq, xs, pk + P.qkv_codes,
-                     reinterpret_cast<const float*>(pk + P.qkv_scales), offsets, mt_start,
-                     tile_group, part, s)) != MOE_OK)
-    return st;
-  M_HIP(k2::launch_slice_sum(T, D.n_qkv_pad, D.n_qkv_pad, W.ns_qkv, part, nullptr, qkv,
-                             D.n_qkv_pad, s));
-  // latent norms, query-latent codes, cache entries
-  M_HIP(k2::launch_mla_latent(T, D.ql, D.n_qkv_pad, D.eps, qkv,
-                              reinterpret_cast<const uint16_t*>(pk + P.g_qa),
-                              reinterpret_cast<const uint16_t*>(pk + P.g_kva), freq, cached_len,
-                              n, L, qa_q, qa_s, static_cast<uint8_t*>(cache_codes), cache_scales,
-                              static_cast<uint16_t*>(cache_rope), s));
-  // q = qa W_qb^T
-  if ((st = run_gemm(D, T, D.n_qb, D.ql, W.ns_qb, qa_q, qa_s, pk + P.qb_codes,
-                     reinterpret_cast<const float*>(pk + P.qb_scales), offsets, mt_start,
-                     tile_group, part, s)) != MOE_OK)
-    return st;
-  M_HIP(k2::launch_slice_sum(T, D.n_qb, D.n_qb, W.ns_qb, part, nullptr, q, D.n_qb, s));
-  // absorbed queries, attention over the cache, value up-projection
-  M_HIP(k2::launch_mla_qabsorb(T, D.H, D.smscale, q, kvb, kvbs, freq, cached_len, n, L, qcat,
-                               s));
-  M_HIP(k2::launch_mla_attn(T, D.H, S, n, L, W.ns_attn, W.chunk,
-                            static_cast<const uint8_t*>(cache_codes), cache_scales,
-                            static_cast<const uint16_t*>(cache_rope), qcat, cached_len, part_o,
-                            part_ml, s));
-  M_HIP(k2::launch_mla_vup(T, D.H, W.ns_attn, part_o, part_ml, kvb, kvbs, o_q, o_s, attn, s));
+  {
+    k2::ProfileScope ps(MOE_STAGE_MLA_PROJ, s);
+    // input RMSNorm + 1x128 quantisation
+    M_HIP(k2::launch_norm_quant(true, T, D.d, D.eps, x, norm_w, at<void>(ws, W.hbuf), xq, xs,
+                                s));
+    // [q_a; kv_a] = h [W_qa; W_kva]^T
+    if ((st = run_gemm(D, T, D.n_qkv_pad, D.d, W.ns_qkv, xq, xs, pk + P.qkv_codes,
+                       reinterpret_cast<const float*>(pk + P.qkv_scales), offsets, mt_start,
+                       tile_group, part, s)) != MOE_OK)
+      return st;
+    M_HIP(k2::launch_slice_sum(T, D.n_qkv_pad, D.n_qkv_pad, W.ns_qkv, part, nullptr, qkv,
+                               D.n_qkv_pad, s));
+  }
+  {
+    k2::ProfileScope ps(MOE_STAGE_MLA_LATENT, s);
+    // latent norms, query-latent codes, cache entries
+    M_HIP(k2::launch_mla_latent(T, D.ql, D.n_qkv_pad, D.eps, qkv,
+                                reinterpret_cast<const uint16_t*>(pk + P.g_qa),
+                                reinterpret_cast<const uint16_t*>(pk + P.g_kva), freq,
+                                cached_len, n, L, qa_q, qa_s, static_cast<uint8_t*>(cache_codes),
+                                cache_scales, static_cast<uint16_t*>(cache_rope), s));
+  }
+  {
+    k2::ProfileScope ps(MOE_STAGE_MLA_PROJ, s);
+    // q = qa W_qb^T
+    if ((st = run_gemm(D, T, D.n_qb, D.ql, W.ns_qb, qa_q, qa_s, pk + P.qb_codes,
+                       reinterpret_cast<const float*>(pk + P.qb_scales), offsets, mt_start,
+                       tile_group, part, s)) != MOE_OK)
+      return st;
+    M_HIP(k2::launch_slice_sum(T, D.n_qb, D.n_qb, W.ns_qb, part, nullptr, q, D.n_qb, s));
+  }
+  {
+    k2::ProfileScope ps(MOE_STAGE_MLA_LATENT, s);
+    // absorbed queries
+    M_HIP(k2::launch_mla_qabsorb(T, D.H, D.smscale, q, kvb, kvbs, freq, cached_len, n, L, qcat,
+                                 s));
+  }
+  {
+    k2::ProfileScope ps(MOE_STAGE_MLA_ATTN, s);
+    M_HIP(k2::launch_mla_attn(T, D.H, S, n, L, W.ns_attn, W.chunk,
+                              static_cast<const uint8_t*>(cache_codes), cache_scales,
+                              static_cast<const uint16_t*>(cache_rope), qcat, cached_len, part_o,
+                              part_ml, s));
+  }
+  {
+    k2::ProfileScope ps(MOE_STAGE_MLA_VUP, s);
+    M_HIP(k2::launch_mla_vup(T, D.H, W.ns_attn, part_o, part_ml, kvb, kvbs, o_q, o_s, attn, s));
+  }
   if (!out) return MOE_OK;
+  k2::ProfileScope ps(MOE_STAGE_MLA_PROJ, s);
   // out = x + o W_o^T
   if ((st = run_gemm(D, T, D.n_o, D.H * D.v, W.ns_o, o_q, o_s, pk + P.o_codes,
                      reinterpret_cast<const float*>(pk + P.o_scales), offsets, mt_start,

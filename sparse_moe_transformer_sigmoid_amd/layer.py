@@ -180,6 +180,15 @@ class K2MoE:
                _p(self.bias), _p(self.packed), _p(out), _p(ws), ws.numel(), _stream())
         return out
 
+    def forward_noalloc(self, x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+        """moe_forward_noalloc: the library's static scratch array as workspace."""
+        T = x.shape[0]
+        if out is None:
+            out = torch.empty((T, self.shape.d_model), dtype=self._act_dtype(), device=self.device)
+        L.call("moe_forward_noalloc", C.byref(self.cfg), T, _p(x), _p(self.norm_w),
+               _p(self.w_router), _p(self.bias), _p(self.packed), _p(out), _stream())
+        return out
+
     def capture_forward(self, x: torch.Tensor, out: torch.Tensor) -> torch.cuda.CUDAGraph:
         """Record moe_forward(x) -> out into a HIP graph (replay with .replay()).
 
