@@ -225,3 +225,18 @@ def test_mla_forward_argument_checks():
     assert st == L.MOE_ERR_INVALID_ARG and b"attn is NULL" in lib.moe_last_error()
     st = lib.mla_pack_weights(C.byref(cfg), None, FAKE, None)
     assert st == L.MOE_ERR_INVALID_ARG
+
+
+def test_noalloc_rejects_a_batch_beyond_its_scratch():
+    """The static scratch array holds 48 MiB: 130 tokens at the K2 shape fit,
+    131 do not (checked on the host, before any HIP call)."""
+    lib = L.load()
+    cfg = _cfg()
+    n = C.c_size_t(0)
+    assert lib.moe_workspace_bytes(C.byref(cfg), 130, L.MOE_WS_FORWARD, C.byref(n)) == L.MOE_OK
+    assert n.value <= 48 << 20
+    assert lib.moe_workspace_bytes(C.byref(cfg), 131, L.MOE_WS_FORWARD, C.byref(n)) == L.MOE_OK
+    assert n.value > 48 << 20
+    st = lib.moe_forward_noalloc(C.byref(cfg), 131, *[FAKE] * 7, None)
+    assert st == L.MOE_ERR_WORKSPACE and b"50331648" in lib.moe_last_error()
+    assert lib.moe_forward_noalloc(C.byref(cfg), 0, *[None] * 7, None) == L.MOE_OK
