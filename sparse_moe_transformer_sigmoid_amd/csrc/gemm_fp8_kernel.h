@@ -122,7 +122,12 @@ struct WorkItem {
 // even XCDs XCD_EVEN_SHARE items for every XCD_ODD_SHARE of an odd one, and
 // all XCDs finish together; the grid must then hold 8 * ceil(quota_even)
 // workgroups (see split_grid).
-template <int RE = 1, int RO = 1>
+//
+// FULL_FIRST: a group's m-tiles are full BM-row tiles and one last tile of
+// the remainder (launches that skip the 16-row token tiles past a tile's
+// rows, so a group executes 16 * ceil(m / 16) rows); otherwise its rows are
+// split into near-equal tiles.
+template <int RE = 1, int RO = 1, bool FULL_FIRST = false>
 __device__ __forceinline__ WorkItem decode_work(const GemmArgs& g, int BM) {
   WorkItem w{};
   const int Wtot = g.mt_start[g.G] * g.NC;
@@ -155,8 +160,9 @@ __device__ __forceinline__ WorkItem decode_work(const GemmArgs& g, int BM) {
     row0_g = min(max(g.offsets[lo], 0), g.P);
     m_g = min(max(g.offsets[lo + 1] - row0_g, 0), g.P - row0_g);
   }
-  // the group's rows are split into ceil(m / BM) m-tiles of near-equal size
-  // (at most BM rows each), so the last tile of a group is not mostly padding
+  // the group's rows are split into ceil(m / BM) m-tiles of at most BM rows:
+  // near-equal ones, so the last tile of a group is not mostly padding, or
+  // (FULL_FIRST) full tiles and the remainder
   const int mtiles = (m_g + BM - 1) / BM;
   const int rr = L - g.mt_start[lo] * g.NC;
   // order inside a group: blocks of up to SUPER m-tiles; within a block,
@@ -168,8 +174,8 @@ __device__ __forceinline__ WorkItem decode_work(const GemmArgs& g, int BM) {
   const int r2 = rr - blk * g.NC * SUPER;
   w.nc = r2 / sm;
   const int mt = blk * SUPER + (r2 - w.nc * sm);
-  const int r_lo = (int)(((int64_t)mt * m_g) / mtiles);
-  const int r_hi = (int)(((int64_t)(mt + 1) * m_g) / mtiles);
+  const int r_lo = FULL_FIRST ? mt * BM : (int)(((int64_t)mt * m_g) / mtiles);
+  const int r_hi = FULL_FIRST ? min(r_lo + BM, m_g) : (int)(((int64_t)(mt + 1) * m_g) / mtiles);
   w.row0 = row0_g + r_lo;
   w.mcount = r_hi - r_lo;
   w.ntt = (w.mcount + 15) >> 4;
@@ -302,6 +308,11 @@ __global__ __launch_bounds__(256, MINW) void gemm_fp8_kernel(const GemmArgs g) {
   static_assert(!EXACT || (BMODE == 0 && ILV == 0), "EXACT is implemented for BMODE 0 only");
   static_assert(!SPLITK || !GATEUP, "SPLITK is implemented for the down form only");
   constexpr int BM = 16 * TT;
+  // 128-row tiles compute only their token tiles that hold rows: the K loop
+  // is instantiated for 1 .. 8 active tiles and chosen once per workgroup
+  // (a branch inside the loop costs the register allocation dearly); the
+  // group's rows are cut full-tiles-first
+  constexpr bool SKIP = TT == 8;
   constexpr int CPT = (TT * 128 + 255) / 256;   // 16-byte staging chunks per thread
   // LDS rows past the tile (TT < 2) are write-only padding: every thread
   // stages its chunk unconditionally, keeping the K loop free of branches
@@ -322,9 +333,10 @@ __global__ __launch_bounds__(256, MINW) void gemm_fp8_kernel(const GemmArgs g) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   const WorkItem wi = TT == 1 ? decode_work<XCD_EVEN_SHARE, XCD_ODD_SHARE>(g, BM)
-                              : decode_work(g, BM);
+                              : decode_work<1, 1, SKIP>(g, BM);
   if (!wi.valid) return;
-  const int grp = wi.grp, nc = wi.nc, row0 = wi.row0, mcount = wi.mcount, ntt = wi.ntt;
+  const int grp = wi.grp, nc = wi.nc, row0 = wi.row0, mcount = wi.mcount;
+  const int ntt = __builtin_amdgcn_readfirstlane(wi.ntt);
   // K slice of this workgroup: blocks kbs .. kbs + nkb_s - 1
   const int kslice = SPLITK ? (int)blockIdx.y : 0;
   const int nkb_s = SPLITK ? g.nkb / (int)gridDim.y : g.nkb;
@@ -370,11 +382,9 @@ __global__ __launch_bounds__(256, MINW) void gemm_fp8_kernel(const GemmArgs g) {
   // gate/up: [kb][gate, up] of chunk nc; down: [row block 2nc + h][kb], h = 0, 1
   for (int i = tid; i < 2 * g.nkb; i += 256) lds_sw[i] = swp_base[i];
 
+  // accumulators: zeroed, accumulated and written out inside each K-loop
+  // instance, so no value of them is live where the instances meet
   v4f acc[4][TT];
-#pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt) acc[rt][tt] = v4f{0.f, 0.f, 0.f, 0.f};
 
   // weight fragments: a ring of NBUF register buffers, loaded NBUF-1 K blocks ahead;
   // activations: two register sets, loaded two K blocks ahead, stored to LDS one
@@ -440,7 +450,8 @@ __global__ __launch_bounds__(256, MINW) void gemm_fp8_kernel(const GemmArgs g) {
   // BMODE 1: one token tile at a time, the next tile's B fragment and scale
   // read from LDS before the current tile's MFMAs (its latency hides behind
   // them), promotion FMAs one MFMA behind
-  auto compute_la = [&](const v8i (&w)[4], int buf, int kb) {
+  auto compute_la = [&](const v8i (&w)[4], int buf, int kb, auto na) {
+    constexpr int NA = decltype(na)::value;
     float swg, swu;
     weight_scales(kb, swg, swu);
     auto read_b = [&](int t, v8i& b, float& sa) {
@@ -452,10 +463,10 @@ __global__ __launch_bounds__(256, MINW) void gemm_fp8_kernel(const GemmArgs g) {
     float sac;
     read_b(0, bc, sac);
 #pragma unroll
-    for (int t = 0; t < TT; ++t) {
+    for (int t = 0; t < NA; ++t) {
       v8i bn = bc;
       float san = sac;
-      if (t + 1 < TT) read_b(t + 1, bn, san);
+      if (t + 1 < NA) read_b(t + 1, bn, san);
       const float s0 = sac * swg, s1 = sac * swu;
       v4f prev = mfma_fp8(w[0], bc);
 #pragma unroll
@@ -467,18 +478,20 @@ __global__ __launch_bounds__(256, MINW) void gemm_fp8_kernel(const GemmArgs g) {
       acc[3][t] += prev * s1;
       bc = bn;
       sac = san;
-      if (t + 1 < TT) __builtin_amdgcn_sched_barrier(0);
+      if (t + 1 < NA) __builtin_amdgcn_sched_barrier(0);
     }
   };
-  auto compute = [&](const v8i (&w)[4], int buf, int kb) {
+  auto compute = [&](const v8i (&w)[4], int buf, int kb, auto na) {
+    constexpr int NA = decltype(na)::value;
+    static_assert(NA == TT || GRP == 1, "partial tiles need one token tile per group");
     if constexpr (BMODE == 1) {
-      compute_la(w, buf, kb);
+      compute_la(w, buf, kb, na);
       return;
     }
     float swg, swu;
     weight_scales(kb, swg, swu);
 #pragma unroll
-    for (int t0 = 0; t0 < TT; t0 += GRP) {
+    for (int t0 = 0; t0 < NA; t0 += GRP) {
       v8i bf[GRP];
       float s0[GRP], s1[GRP];
 #pragma unroll
@@ -518,7 +531,7 @@ __global__ __launch_bounds__(256, MINW) void gemm_fp8_kernel(const GemmArgs g) {
         }
         __builtin_amdgcn_sched_group_barrier(0x002, 8 + 2 * GRP, 0);
       }
-      if (t0 + GRP < TT) __builtin_amdgcn_sched_barrier(0);
+      if (t0 + GRP < NA) __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -529,14 +542,24 @@ __global__ __launch_bounds__(256, MINW) void gemm_fp8_kernel(const GemmArgs g) {
   // each step issues the activations before the weights of block
   // kb+NBUF-1, and ends by waiting only for the activations (BMODE 0: those
   // of block kb+1, issued one step earlier).
-  auto kloop = [&](auto ntc) {
+  auto kloop = [&](auto ntc, auto na) {
   const int nkb = nkb_s;
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) acc[rt][tt] = v4f{0.f, 0.f, 0.f, 0.f};
   if constexpr (BMODE == 1) {
     dma_b(0, 0);
     asm volatile("s_waitcnt vmcnt(0)" : : : "memory");   // block 0, before the barrier below
   } else {
-    load_b(0, 0);
-    if (BSETS == 2 && nkb > 1) load_b(BSETS - 1, 1);
+    // kb0 = 0, through an asm the compiler cannot see into and whose text
+    // differs per instance: the instances' first loads are then not merged
+    // ahead of the branch that picks one (their registers would stay live
+    // through the other instances)
+    int kb0;
+    asm volatile("s_mov_b32 %0, 0 ; active tiles %1" : "=s"(kb0) : "i"(decltype(na)::value));
+    load_b(0, kb0);
+    if (BSETS == 2 && nkb > 1) load_b(BSETS - 1, kb0 + 1);
   }
 #pragma unroll
   for (int i = 0; i < NBUF - 1; ++i)
@@ -565,7 +588,7 @@ __global__ __launch_bounds__(256, MINW) void gemm_fp8_kernel(const GemmArgs g) {
     // keep the prefetches issued here: the scheduler would otherwise sink
     // them next to their use to save registers, undoing the ring
     __builtin_amdgcn_sched_barrier(0);
-    compute(wbuf[j % NBUF], cur, kb);
+    compute(wbuf[j % NBUF], cur, kb, na);
     if constexpr (BMODE == 1) {
       // This wave's direct loads of block kb+1 are older than the 8 weight
       // loads issued after them, so vmcnt(8) completes them without waiting
@@ -596,19 +619,29 @@ __global__ __launch_bounds__(256, MINW) void gemm_fp8_kernel(const GemmArgs g) {
     for (int j = 0; j < STEP; ++j)
       if (kb0 + j < nkb) step(j, kb0 + j);
   }
-
+  epilogue<GATEUP, TT, NT>(g, acc, lds_red, wi, wave, lane, kslice);
   };
   // The shared expert's group has several m-tiles in the launches whose
   // routed groups have one: its weight chunks are read once per m-tile, so
   // that group loads them through L2 while routed chunks stream past it.
+  using all_tiles = std::integral_constant<int, TT>;
   if constexpr (NT) {
-    if (wi.shared_grp) kloop(std::false_type{});
-    else kloop(std::true_type{});
+    if (wi.shared_grp) kloop(std::false_type{}, all_tiles{});
+    else kloop(std::true_type{}, all_tiles{});
+  } else if constexpr (SKIP) {
+    switch (ntt) {
+      case 1: kloop(std::false_type{}, std::integral_constant<int, 1>{}); break;
+      case 2: kloop(std::false_type{}, std::integral_constant<int, 2>{}); break;
+      case 3: kloop(std::false_type{}, std::integral_constant<int, 3>{}); break;
+      case 4: kloop(std::false_type{}, std::integral_constant<int, 4>{}); break;
+      case 5: kloop(std::false_type{}, std::integral_constant<int, 5>{}); break;
+      case 6: kloop(std::false_type{}, std::integral_constant<int, 6>{}); break;
+      case 7: kloop(std::false_type{}, std::integral_constant<int, 7>{}); break;
+      default: kloop(std::false_type{}, all_tiles{}); break;
+    }
   } else {
-    kloop(std::false_type{});
+    kloop(std::false_type{}, all_tiles{});
   }
-
-  epilogue<GATEUP, TT, NT>(g, acc, lds_red, wi, wave, lane, kslice);
 }
 
 }  // namespace
