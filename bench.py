@@ -83,6 +83,8 @@ def parse():
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the prefill, skewed-routing and dense-FFN lines")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-balance", action="store_true",
+                    help="skip the routing bias update line")
     ap.add_argument("--no-mla", action="store_true",
                     help="skip the MLA attention decode and prefill lines")
     ap.add_argument("--eager", action="store_true",
@@ -293,6 +295,54 @@ def mla_line(shape, steps, warmup):
     return line
 
 
+def balance_line(steps, warmup):
+    """One training step's routing bias update at the K2 prefill batch: zero
+    the loads, count the 8,192 x 8 top-k choices over 384 experts
+    (moe_expert_load), update the bias (moe_bias_update).  Algorithmic bytes:
+    the choices read once, the loads written and read back, the bias read and
+    written.  The step is a handful of small launches, so its time is launch
+    latency rather than bandwidth; it runs once per training step."""
+    import torch
+
+    import synth
+    from sparse_moe_transformer_sigmoid_amd import _lib as L
+    from sparse_moe_transformer_sigmoid_amd.layer import config_from_shape
+
+    shape = synth.K2_PREFILL
+    E, k, T = shape.n_experts, shape.top_k, shape.tokens
+    cfg = config_from_shape(shape)
+    ids = synth.topk_choices(T, k, E, seed=0, skew=0.5, device="cuda")
+    counts = torch.zeros(E, dtype=torch.int32, device="cuda")
+    bias = synth.bias_values(E, seed=0, device="cuda")
+    s = torch.cuda.current_stream()
+    sp = C.c_void_p(s.cuda_stream)
+
+    def one():
+        counts.zero_()
+        L.call("moe_expert_load", C.byref(cfg), T, ids.data_ptr(), counts.data_ptr(), sp)
+        L.call("moe_bias_update", C.byref(cfg), counts.data_ptr(), C.c_float(1e-3),
+               bias.data_ptr(), sp)
+
+    for _ in range(warmup):
+        one()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(s)
+    for _ in range(steps):
+        one()
+    stop.record(s)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    nbytes = T * k * 4 + 2 * E * 4 + 2 * E * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": "bias_update_k2_prefill", "choices": T * k, "experts": E,
+            "ms_per_step": ms, "algorithmic_bytes": nbytes,
+            "roofline": {"kernel": "expert_load_kernel + bias_update_kernel", "bound": "hbm",
+                         "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS,
+                         "note": "three small launches (zero, count, update): latency-bound"}}
+
+
 def sclk_file():
     """The amdgpu driver's shader-clock table of the GPU torch uses (sysfs
     pp_dpm_sclk, found by the device's PCI address), or None."""
@@ -490,6 +540,10 @@ def main():
             line["mla"][nm] = mla_line(shp_m, max(3, args.steps // 2), 2)
             print(f"# mla {nm} {line['mla'][nm]['ms_per_step']:.3f} ms", file=sys.stderr,
                   flush=True)
+    if args.workload == "decode" and not args.no_balance:
+        line["bias_update"] = balance_line(max(10, args.steps), 3)
+        print(f"# bias update {line['bias_update']['ms_per_step'] * 1e3:.1f} us", file=sys.stderr,
+              flush=True)
     if not args.no_clock:
         layer.use_router(inp)
         line["sclk_mhz"] = sclk_during(layer, inp.x)

@@ -224,6 +224,39 @@ moe_status moe_forward_noalloc(const moe_config* cfg, int64_t T, const void* x,
                                const void* norm_w, const void* w_router, const float* bias,
                                const void* packed_w, void* out, void* stream);
 
+/* ---- Routing bias update (training): aux-loss-free load balancing.
+ *
+ * The router adds e_score_correction_bias to the sigmoid scores for the top-k
+ * choice only ("Kimi-K2-Base", Mixture of experts, Load balancing; "Kimi K2 ·
+ * Architecture", config.json topk_method noaux_tc); the pages state that the
+ * rule adjusting that bias is not described.  The rule implemented is the
+ * published aux-loss-free balancing rule (Wang et al. 2024): with c_e the
+ * number of top-k choices of routed expert e over a training step and cbar
+ * = sum_e c_e / E their mean, after the step
+ *     bias[e] <- bias[e] + speed * sign(cbar - c_e)      (sign 0 at the mean)
+ * with the sign decided exactly on integers and one fp32 addition per expert.
+ * A step over several micro-batches accumulates their loads with
+ * moe_expert_load into one counts array, then calls moe_bias_update once
+ * (with data parallelism the counts are summed over the ranks in between). */
+
+/* counts[e] += number of entries of topk_ids [T, top_k] (int32, from
+ * moe_router) equal to e, for 0 <= e < n_experts; other values are not routed
+ * experts of this layer and are not counted.  counts: int32 [n_experts],
+ * caller-owned device memory, 4-byte aligned, zeroed by the caller at the
+ * start of a step; the total over a step must stay below 2^31.  The counts
+ * are exact integers, the same whatever order the workgroups add in.  T = 0
+ * enqueues nothing; a dense config has no routed experts
+ * (MOE_ERR_INVALID_ARG). */
+moe_status moe_expert_load(const moe_config* cfg, int64_t T, const int32_t* topk_ids,
+                           int32_t* counts, void* stream);
+
+/* bias [n_experts] fp32 (device, in place) <- bias + speed * sign(cbar - c_e)
+ * from the step's counts [n_experts] int32 (device); speed must be finite and
+ * >= 0 (MOE_ERR_INVALID_ARG otherwise).  Reads counts, writes bias: the
+ * counts may be zeroed for the next step once this call has run. */
+moe_status moe_bias_update(const moe_config* cfg, const int32_t* counts, float speed,
+                           float* bias, void* stream);
+
 /* ---- diagnostics: per-stage timing with HIP events ---------------------
  * While profiling is on, every entry point records a HIP event before and
  * after each of its kernel stages, on the caller's stream.  This is the only
@@ -245,7 +278,8 @@ typedef enum {
   MOE_STAGE_MLA_LATENT = 9,  /* latent norms, cache entries, query absorption */
   MOE_STAGE_MLA_ATTN = 10,   /* attention over the latent cache */
   MOE_STAGE_MLA_VUP = 11,    /* split merge, value up-projection, 1x128 quantisation */
-  MOE_STAGE_COUNT = 12
+  MOE_STAGE_BALANCE = 12,    /* expert loads and the routing bias update */
+  MOE_STAGE_COUNT = 13
 } moe_stage;
 
 moe_status moe_profile_enable(int32_t on);

@@ -1,6 +1,7 @@
 // C ABI of the K2 MoE layer: argument validation, workspace layout and the
 // launch sequence of each entry point.  See include/k2moe.h for the contract.
 #include <algorithm>
+#include <cmath>
 #include <cstdio>
 #include <mutex>
 #include <string>
@@ -756,6 +757,36 @@ moe_status moe_forward_noalloc(const moe_config* cfg, int64_t T, const void* x,
   void* ws = nullptr;
   if ((st = scratch_of_current_device(&ws)) != MOE_OK) return st;
   return moe_forward(cfg, T, x, norm_w, w_router, bias, packed_w, out, ws, need, stream);
+}
+
+moe_status moe_expert_load(const moe_config* cfg, int64_t T, const int32_t* topk_ids,
+                           int32_t* counts, void* stream) {
+  Dims D;
+  moe_status st = check_cfg(cfg, &D);
+  if (st != MOE_OK) return st;
+  K2_REQUIRE(!D.dense, MOE_ERR_INVALID_ARG, "a dense layer has no routed experts to balance");
+  if ((st = check_tokens(T, &D)) != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  K2_PTR4(topk_ids, "topk_ids");
+  K2_PTR4(counts, "counts");
+  Stage stg(MOE_STAGE_BALANCE, static_cast<hipStream_t>(stream));
+  K2_HIP(k2::launch_expert_load(D.P, D.E, topk_ids, counts, static_cast<hipStream_t>(stream)));
+  return MOE_OK;
+}
+
+moe_status moe_bias_update(const moe_config* cfg, const int32_t* counts, float speed,
+                           float* bias, void* stream) {
+  Dims D;
+  moe_status st = check_cfg(cfg, &D);
+  if (st != MOE_OK) return st;
+  K2_REQUIRE(!D.dense, MOE_ERR_INVALID_ARG, "a dense layer has no routing bias");
+  K2_REQUIRE(std::isfinite(speed) && speed >= 0.f, MOE_ERR_INVALID_ARG,
+             "speed must be finite and >= 0");
+  K2_PTR4(counts, "counts");
+  K2_PTR4(bias, "bias");
+  Stage stg(MOE_STAGE_BALANCE, static_cast<hipStream_t>(stream));
+  K2_HIP(k2::launch_bias_update(D.E, counts, speed, bias, static_cast<hipStream_t>(stream)));
+  return MOE_OK;
 }
 
 }  // extern "C"

@@ -97,4 +97,10 @@ hipError_t launch_pack_fp8(int d, int I, const uint8_t* wg, const uint8_t* wu,
                            const float* sd, uint8_t* dst_codes, float* dst_gu_scales,
                            float* dst_d_scales, hipStream_t s);
 
+// ---- routing bias update (balance.hip)
+hipError_t launch_expert_load(int64_t n, int E, const int32_t* ids, int32_t* counts,
+                              hipStream_t s);
+hipError_t launch_bias_update(int E, const int32_t* counts, float speed, float* bias,
+                              hipStream_t s);
+
 }  // namespace k2

@@ -189,6 +189,24 @@ class K2MoE:
                _p(self.w_router), _p(self.bias), _p(self.packed), _p(out), _stream())
         return out
 
+    def expert_load(self, topk_ids: torch.Tensor,
+                    counts: torch.Tensor | None = None) -> torch.Tensor:
+        """moe_expert_load: add the expert loads of topk_ids [T, k] int32 into
+        counts (int32 [n_experts]; a zeroed one when None)."""
+        if counts is None:
+            counts = torch.zeros(self.shape.n_experts, dtype=torch.int32, device=self.device)
+        L.call("moe_expert_load", C.byref(self.cfg), topk_ids.shape[0], _p(topk_ids),
+               _p(counts), _stream())
+        return counts
+
+    def bias_update(self, counts: torch.Tensor, speed: float,
+                    bias: torch.Tensor | None = None) -> torch.Tensor:
+        """moe_bias_update, in place on bias (default: this layer's routing bias)."""
+        b = self.bias if bias is None else bias
+        L.call("moe_bias_update", C.byref(self.cfg), _p(counts), C.c_float(speed), _p(b),
+               _stream())
+        return b
+
     def capture_forward(self, x: torch.Tensor, out: torch.Tensor) -> torch.cuda.CUDAGraph:
         """Record moe_forward(x) -> out into a HIP graph (replay with .replay()).
 

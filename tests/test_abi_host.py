@@ -240,3 +240,29 @@ def test_noalloc_rejects_a_batch_beyond_its_scratch():
     st = lib.moe_forward_noalloc(C.byref(cfg), 131, *[FAKE] * 7, None)
     assert st == L.MOE_ERR_WORKSPACE and b"50331648" in lib.moe_last_error()
     assert lib.moe_forward_noalloc(C.byref(cfg), 0, *[None] * 7, None) == L.MOE_OK
+
+
+def test_balance_argument_checks():
+    cfg = _cfg()
+    nan, inf = float("nan"), float("inf")
+    # loads: T < 0, NULL or misaligned arrays; T = 0 is a no-op
+    assert L.status_of("moe_expert_load", C.byref(cfg), -1, FAKE, FAKE, None) == L.MOE_ERR_INVALID_ARG
+    assert L.status_of("moe_expert_load", C.byref(cfg), 4, None, FAKE, None) == L.MOE_ERR_INVALID_ARG
+    assert L.status_of("moe_expert_load", C.byref(cfg), 4, FAKE, FAKE + 2, None) == \
+        L.MOE_ERR_INVALID_ARG
+    assert L.status_of("moe_expert_load", C.byref(cfg), 0, None, None, None) == L.MOE_OK
+    # update: speed finite and >= 0, both arrays present and aligned
+    for bad in (nan, inf, -1e-3):
+        assert L.status_of("moe_bias_update", C.byref(cfg), FAKE, C.c_float(bad), FAKE, None) == \
+            L.MOE_ERR_INVALID_ARG, bad
+    assert L.status_of("moe_bias_update", C.byref(cfg), None, C.c_float(1e-3), FAKE, None) == \
+        L.MOE_ERR_INVALID_ARG
+    assert L.status_of("moe_bias_update", C.byref(cfg), FAKE, C.c_float(1e-3), FAKE + 1, None) == \
+        L.MOE_ERR_INVALID_ARG
+    # a dense layer has no routed experts and no bias
+    dense = _cfg(synth.K2_DENSE)
+    assert L.status_of("moe_expert_load", C.byref(dense), 4, FAKE, FAKE, None) == \
+        L.MOE_ERR_INVALID_ARG
+    assert L.status_of("moe_bias_update", C.byref(dense), FAKE, C.c_float(1e-3), FAKE, None) == \
+        L.MOE_ERR_INVALID_ARG
+    assert "dense" in L.load().moe_last_error().decode()
