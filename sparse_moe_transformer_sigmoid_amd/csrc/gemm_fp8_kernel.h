@@ -123,11 +123,13 @@ struct WorkItem {
 // all XCDs finish together; the grid must then hold 8 * ceil(quota_even)
 // workgroups (see split_grid).
 //
-// FULL_FIRST: a group's m-tiles are full BM-row tiles and one last tile of
-// the remainder (launches that skip the 16-row token tiles past a tile's
-// rows, so a group executes 16 * ceil(m / 16) rows); otherwise its rows are
-// split into near-equal tiles.
-template <int RE = 1, int RO = 1, bool FULL_FIRST = false>
+// BY16: the group's ceil(m / 16) token tiles are dealt out as evenly as
+// possible over its m-tiles, the first ones taking one more (launches that
+// skip the token tiles past a tile's rows: a group then executes
+// 16 * ceil(m / 16) rows, and its m-tiles, which read the same weight
+// chunks, take near-equal time and stay close together in L2); otherwise its
+// rows are split into near-equal tiles.
+template <int RE = 1, int RO = 1, bool BY16 = false>
 __device__ __forceinline__ WorkItem decode_work(const GemmArgs& g, int BM) {
   WorkItem w{};
   const int Wtot = g.mt_start[g.G] * g.NC;
@@ -160,9 +162,9 @@ __device__ __forceinline__ WorkItem decode_work(const GemmArgs& g, int BM) {
     row0_g = min(max(g.offsets[lo], 0), g.P);
     m_g = min(max(g.offsets[lo + 1] - row0_g, 0), g.P - row0_g);
   }
-  // the group's rows are split into ceil(m / BM) m-tiles of at most BM rows:
-  // near-equal ones, so the last tile of a group is not mostly padding, or
-  // (FULL_FIRST) full tiles and the remainder
+  // the group's rows are split into ceil(m / BM) m-tiles of at most BM rows,
+  // near-equal ones, so the last tile of a group is not mostly padding
+  // (BY16: near-equal numbers of 16-row token tiles)
   const int mtiles = (m_g + BM - 1) / BM;
   const int rr = L - g.mt_start[lo] * g.NC;
   // order inside a group: blocks of up to SUPER m-tiles; within a block,
@@ -174,8 +176,15 @@ __device__ __forceinline__ WorkItem decode_work(const GemmArgs& g, int BM) {
   const int r2 = rr - blk * g.NC * SUPER;
   w.nc = r2 / sm;
   const int mt = blk * SUPER + (r2 - w.nc * sm);
-  const int r_lo = FULL_FIRST ? mt * BM : (int)(((int64_t)mt * m_g) / mtiles);
-  const int r_hi = FULL_FIRST ? min(r_lo + BM, m_g) : (int)(((int64_t)(mt + 1) * m_g) / mtiles);
+  int r_lo, r_hi;
+  if constexpr (BY16) {
+    const int n16 = (m_g + 15) >> 4, q16 = n16 / mtiles, x16 = n16 % mtiles;
+    r_lo = 16 * (mt * q16 + min(mt, x16));
+    r_hi = min(r_lo + 16 * (q16 + (mt < x16 ? 1 : 0)), m_g);
+  } else {
+    r_lo = (int)(((int64_t)mt * m_g) / mtiles);
+    r_hi = (int)(((int64_t)(mt + 1) * m_g) / mtiles);
+  }
   w.row0 = row0_g + r_lo;
   w.mcount = r_hi - r_lo;
   w.ntt = (w.mcount + 15) >> 4;
@@ -311,7 +320,7 @@ __global__ __launch_bounds__(256, MINW) void gemm_fp8_kernel(const GemmArgs g) {
   // 128-row tiles compute only their token tiles that hold rows: the K loop
   // is instantiated for 1 .. 8 active tiles and chosen once per workgroup
   // (a branch inside the loop costs the register allocation dearly); the
-  // group's rows are cut full-tiles-first
+  // group's token tiles are dealt out evenly over its m-tiles
   constexpr bool SKIP = TT == 8;
   constexpr int CPT = (TT * 128 + 255) / 256;   // 16-byte staging chunks per thread
   // LDS rows past the tile (TT < 2) are write-only padding: every thread
