@@ -279,7 +279,12 @@ typedef enum {
   MOE_STAGE_MLA_ATTN = 10,   /* attention over the latent cache */
   MOE_STAGE_MLA_VUP = 11,    /* split merge, value up-projection, 1x128 quantisation */
   MOE_STAGE_BALANCE = 12,    /* expert loads and the routing bias update */
-  MOE_STAGE_COUNT = 13
+  /* the training step of k2train.h */
+  MOE_STAGE_TRAIN_FWD = 13,   /* bf16 gate/up (+ FP8 copies) and down GEMMs */
+  MOE_STAGE_TRAIN_DGRAD = 14, /* dgrad GEMMs of down and gate/up */
+  MOE_STAGE_TRAIN_WGRAD = 15, /* operand transposes and the weight-gradient GEMMs */
+  MOE_STAGE_TRAIN_OTHER = 16, /* sums per token, router and RMSNorm backward */
+  MOE_STAGE_COUNT = 17
 } moe_stage;
 
 moe_status moe_profile_enable(int32_t on);

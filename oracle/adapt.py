@@ -64,3 +64,30 @@ def run_mla_oracle(inputs, tokens=None) -> dict:
     res = mla_layer(p, to_f32(inputs.x), w, seq_of, pos_of, cache, tokens=tokens)
     res.update(cache=cache, seq_of=seq_of, pos_of=pos_of, params=p)
     return res
+
+
+class LazyExperts:
+    """Expert weights of a training workload fetched from the device one
+    expert at a time (float32 arrays of the bf16 values)."""
+
+    def __init__(self, inputs, which):
+        self.inputs, self.which = inputs, which
+        self.cache = {}
+
+    def __getitem__(self, e):
+        e = int(e)
+        if e not in self.cache:
+            g, u, d = self.inputs.expert(e)
+            self.cache[e] = to_f32({"gate": g, "up": u, "down": d}[self.which])
+        return self.cache[e]
+
+
+def train_oracle_inputs(inputs):
+    """(params, x, norm_w, bias, TrainWeights, dout) of a training workload,
+    the expert weights fetched lazily."""
+    from .train_ref import TrainWeights
+    p = params_from_shape(inputs.shape)
+    W = TrainWeights(gate=LazyExperts(inputs, "gate"), up=LazyExperts(inputs, "up"),
+                     down=LazyExperts(inputs, "down"), w_router=to_f32(inputs.w_router))
+    return (p, to_f32(inputs.x), to_f32(inputs.norm_w), inputs.bias.detach().cpu().numpy(), W,
+            to_f32(inputs.dout))

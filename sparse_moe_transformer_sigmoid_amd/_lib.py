@@ -56,9 +56,13 @@ EXPORTS = ["moe_status_str", "moe_last_error", "moe_packed_weights_bytes", "moe_
            "moe_workspace_bytes", "moe_router", "moe_permute", "moe_grouped_swiglu",
            "moe_combine", "moe_forward", "moe_profile_enable", "moe_profile_read",
            "mla_packed_weights_bytes", "mla_pack_weights", "mla_workspace_bytes", "mla_forward",
-           "mla_attention", "moe_forward_noalloc", "moe_expert_load", "moe_bias_update"]
+           "mla_attention", "moe_forward_noalloc", "moe_expert_load", "moe_bias_update",
+           "moe_train_weights_bytes", "moe_train_transposed_bytes", "moe_train_transpose_weights",
+           "moe_train_saved_bytes", "moe_train_workspace_bytes", "moe_train_forward",
+           "moe_train_backward"]
 STAGES = ["norm_quant", "router_gemm", "topk", "permute", "tiles", "gateup", "down", "combine",
-          "mla_proj", "mla_latent", "mla_attn", "mla_vup", "balance"]
+          "mla_proj", "mla_latent", "mla_attn", "mla_vup", "balance", "train_fwd", "train_dgrad",
+          "train_wgrad", "train_other"]
 
 _LIB = None
 
@@ -91,6 +95,14 @@ def load(path: str | None = None) -> C.CDLL:
         "moe_forward_noalloc": (i32, [cfgp, i64, vp, vp, vp, vp, vp, vp, vp]),
         "moe_expert_load": (i32, [cfgp, i64, vp, vp, vp]),
         "moe_bias_update": (i32, [cfgp, vp, C.c_float, vp, vp]),
+        "moe_train_weights_bytes": (sz, [cfgp]),
+        "moe_train_transposed_bytes": (sz, [cfgp]),
+        "moe_train_transpose_weights": (i32, [cfgp, vp, vp, vp]),
+        "moe_train_saved_bytes": (i32, [cfgp, i64, C.POINTER(sz)]),
+        "moe_train_workspace_bytes": (i32, [cfgp, i64, C.POINTER(sz)]),
+        "moe_train_forward": (i32, [cfgp, i64, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "moe_train_backward": (i32, [cfgp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                     vp, sz, vp]),
         "mla_packed_weights_bytes": (sz, [C.POINTER(mla_config)]),
         "mla_pack_weights": (i32, [C.POINTER(mla_config), C.POINTER(mla_weights), vp, vp]),
         "mla_workspace_bytes": (i32, [C.POINTER(mla_config), i32, i32, i32, C.POINTER(sz)]),

@@ -9,6 +9,8 @@
 
 #include "k2_launch.h"
 #include "k2moe.h"
+#include "k2train.h"
+#include "train_launch.h"
 
 namespace {
 
@@ -449,6 +451,118 @@ moe_status run_experts(const Dims& D, const Layout& L, void* ws, const void* xq,
   return MOE_OK;
 }
 
+// ---- the training step (k2train.h)
+
+moe_status check_train_cfg(const moe_config* cfg, Dims* D) {
+  moe_status st = check_cfg(cfg, D);
+  if (st != MOE_OK) return st;
+  K2_REQUIRE(D->fp8 && !D->dense, MOE_ERR_UNSUPPORTED,
+             "the training step needs fmt = MOE_FMT_BF16_FP8B128 and a routed layer");
+  K2_REQUIRE(D->d % 256 == 0 && D->I % 256 == 0, MOE_ERR_UNSUPPORTED,
+             "the training step needs d_model % 256 == 0 and d_ff % 256 == 0");
+  return MOE_OK;
+}
+
+struct TrainSaved {
+  size_t hq, hs, ids, w, s, offsets, row_pair, pair_row, guq, gus, total;
+};
+
+TrainSaved train_saved(const Dims& D) {
+  TrainSaved v{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align_up(bytes);
+    return o;
+  };
+  const size_t T = (size_t)D.T, P = (size_t)D.P, d = (size_t)D.d, I = (size_t)D.I;
+  const size_t R = P + (D.S ? T : 0);
+  v.hq = take(T * d);
+  v.hs = take(T * (d / 128) * 4);
+  v.ids = take(P * 4);
+  v.w = take(P * 4);
+  v.s = take(P * 4);
+  v.offsets = take(((size_t)D.E + 1) * 4);
+  v.row_pair = take(P * 4);
+  v.pair_row = take(P * 4);
+  v.guq = take(R * 2 * I);
+  v.gus = take(R * (2 * I / 128) * 4);
+  v.total = D.T == 0 ? 0 : off;
+  return v;
+}
+
+// Columns of the transposed, group-padded operands of the weight gradients:
+// every group pads to a multiple of 32 rows; the grid of the transposes
+// covers whole 64-column blocks.
+int64_t train_ldt(const Dims& D) {
+  const int64_t R = D.P + (D.S ? D.T : 0);
+  return (R + 32 * (int64_t)D.G + 63) / 64 * 64;
+}
+
+struct TrainLayout {
+  Layout fl;   // router / permutation sub-buffers of the forward layout
+  size_t gap, mt_start, tile_group, abf, rows, shared, dgu, dwp, dh, dz, dht, pad_off, dywT,
+      aT, dguT, hT, total;
+};
+
+TrainLayout train_layout(const Dims& D) {
+  TrainLayout L{};
+  L.fl = layout(D, MOE_WS_ROUTER);
+  const Layout pl = layout(D, MOE_WS_PERMUTE);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align_up(bytes);
+    return o;
+  };
+  // the router and permutation buffers first, at the offsets those layouts use
+  L.fl.ccount = L.fl.total + pl.ccount;
+  L.fl.cbase = L.fl.total + pl.cbase;
+  off = L.fl.total + pl.total;
+  const size_t T = (size_t)D.T, P = (size_t)D.P, d = (size_t)D.d, I = (size_t)D.I;
+  const size_t R = P + (D.S ? T : 0);
+  const size_t ldt = (size_t)train_ldt(D);
+  L.gap = take(T * 4);
+  L.mt_start = take(((size_t)D.G + 1) * 4);
+  L.tile_group = take((size_t)mtile_bound(D, 128) * 4);
+  L.abf = take(R * I * 2);
+  L.rows = take(P * d * 4);
+  L.shared = take((D.S ? T : 1) * d * 4);
+  L.dgu = take(R * 2 * I * 2);
+  L.dwp = take(R * (I / 256) * 4);
+  L.dh = take(T * d * 4);
+  L.dz = take(P * 4);
+  L.dht = take(T * d * 4);
+  L.pad_off = take(((size_t)D.G + 1) * 4);
+  L.dywT = take(d * ldt * 2);
+  L.aT = take(I * ldt * 2);
+  L.dguT = take(2 * I * ldt * 2);
+  L.hT = take(d * ldt * 2);
+  L.total = D.T == 0 ? 0 : off;
+  return L;
+}
+
+int train_grid(const Dims& D, int nc) {
+  const int64_t g = (mtile_bound(D, 128) * nc + 7) / 8 * 8;
+  return (int)std::min<int64_t>(g, (int64_t)1 << 30);
+}
+
+k2::TrainGemmArgs train_rows_args(const Dims& D, const TrainLayout& L, void* ws,
+                                  const int32_t* offsets, const int32_t* row_pair) {
+  k2::TrainGemmArgs a{};
+  a.offsets = offsets;
+  a.row_pair = row_pair;
+  a.mt_start = at<int32_t>(ws, L.mt_start);
+  a.tile_group = at<int32_t>(ws, L.tile_group);
+  a.E = D.E;
+  a.G = D.G;
+  a.T = (int)D.T;
+  a.P = (int)D.P;
+  a.k = D.k;
+  a.I = D.I;
+  return a;
+}
+
 // ---- the allocation-free forward (moe_forward_noalloc): its workspace is a
 // static device array, one copy per GPU, held until the process ends.
 constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)48 << 20;   // K2 shape: up to 130 tokens
@@ -786,6 +900,308 @@ moe_status moe_bias_update(const moe_config* cfg, const int32_t* counts, float s
   K2_PTR4(bias, "bias");
   Stage stg(MOE_STAGE_BALANCE, static_cast<hipStream_t>(stream));
   K2_HIP(k2::launch_bias_update(D.E, counts, speed, bias, static_cast<hipStream_t>(stream)));
+  return MOE_OK;
+}
+
+size_t moe_train_weights_bytes(const moe_config* cfg) {
+  Dims D;
+  if (check_train_cfg(cfg, &D) != MOE_OK) return 0;
+  return (size_t)D.G * 3 * (size_t)D.I * D.d * 2;
+}
+
+size_t moe_train_transposed_bytes(const moe_config* cfg) {
+  return moe_train_weights_bytes(cfg);
+}
+
+moe_status moe_train_transpose_weights(const moe_config* cfg, const void* w, void* wt,
+                                       void* stream) {
+  Dims D;
+  moe_status st = check_train_cfg(cfg, &D);
+  if (st != MOE_OK) return st;
+  K2_PTR(w, "w");
+  K2_PTR(wt, "wt");
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t d = (size_t)D.d, I = (size_t)D.I, es = 3 * I * d;
+  const uint16_t* src = static_cast<const uint16_t*>(w);
+  uint16_t* dst = static_cast<uint16_t*>(wt);
+  // expert g: down^T [I, d] at g * 3Id, [gate; up]^T [d, 2I] at g * 3Id + Id
+  K2_HIP(k2::launch_transpose_w(D.G, (int)d, (int)I, src + 2 * I * d, es, (int)I, dst, es,
+                                (int)d, 0, s));
+  K2_HIP(k2::launch_transpose_w(D.G, (int)I, (int)d, src, es, (int)d, dst + I * d, es,
+                                (int)(2 * I), 0, s));
+  K2_HIP(k2::launch_transpose_w(D.G, (int)I, (int)d, src + I * d, es, (int)d, dst + I * d, es,
+                                (int)(2 * I), (int)I, s));
+  return MOE_OK;
+}
+
+moe_status moe_train_saved_bytes(const moe_config* cfg, int64_t T, size_t* bytes) {
+  Dims D;
+  moe_status st = check_train_cfg(cfg, &D);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(T, &D)) != MOE_OK) return st;
+  K2_REQUIRE(bytes != nullptr, MOE_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = train_saved(D).total;
+  return MOE_OK;
+}
+
+moe_status moe_train_workspace_bytes(const moe_config* cfg, int64_t T, size_t* bytes) {
+  Dims D;
+  moe_status st = check_train_cfg(cfg, &D);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(T, &D)) != MOE_OK) return st;
+  K2_REQUIRE(bytes != nullptr, MOE_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = train_layout(D).total;
+  return MOE_OK;
+}
+
+moe_status moe_train_forward(const moe_config* cfg, int64_t T, const void* x, const void* norm_w,
+                             const void* w_router, const float* bias, const void* w, void* out,
+                             void* saved, void* ws, size_t ws_bytes, void* stream) {
+  Dims D;
+  moe_status st = check_train_cfg(cfg, &D);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(T, &D)) != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  K2_PTR(x, "x");
+  K2_PTR(norm_w, "norm_w");
+  K2_PTR(w_router, "w_router");
+  K2_PTR4(bias, "bias");
+  K2_PTR(w, "w");
+  K2_PTR(out, "out");
+  K2_PTR(saved, "saved");
+  K2_PTR(ws, "ws");
+  const TrainLayout L = train_layout(D);
+  K2_REQUIRE(ws_bytes >= L.total, MOE_ERR_WORKSPACE,
+             "workspace too small: need " + std::to_string(L.total));
+  const TrainSaved v = train_saved(D);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t* ids = at<int32_t>(saved, v.ids);
+  float* wts = at<float>(saved, v.w);
+  int32_t* offsets = at<int32_t>(saved, v.offsets);
+  int32_t* row_pair = at<int32_t>(saved, v.row_pair);
+  // norm + FP8 copy of h (hq, hs: the kept up-projection input), router, top-k
+  if ((st = run_router(D, L.fl, ws, x, norm_w, w_router, bias, ids, wts,
+                       at<float>(ws, L.gap), at<void>(saved, v.hq),
+                       at<float>(saved, v.hs), s)) != MOE_OK)
+    return st;
+  {
+    Stage stg(MOE_STAGE_TOPK, s);
+    K2_HIP(k2::launch_chosen_scores((int)T, D.E, D.k, at<float>(ws, L.fl.zpart), ids,
+                                    at<float>(saved, v.s), s));
+  }
+  if ((st = run_permute(D, L.fl, ws, ids, offsets, row_pair, at<int32_t>(saved, v.pair_row), s)) !=
+      MOE_OK)
+    return st;
+  {
+    Stage stg(MOE_STAGE_TILES, s);
+    K2_HIP(k2::launch_build_tiles(D.E, D.S, (int)T, D.k, 128, (int)mtile_bound(D, 128), offsets,
+                                  at<int32_t>(ws, L.mt_start), at<int32_t>(ws, L.tile_group), s));
+  }
+  const size_t d = (size_t)D.d, I = (size_t)D.I;
+  const uint16_t* W = static_cast<const uint16_t*>(w);
+  k2::TrainGemmArgs a = train_rows_args(D, L, ws, offsets, row_pair);
+  a.topk_w = wts;
+  a.guq = at<uint8_t>(saved, v.guq);
+  a.gus = at<float>(saved, v.gus);
+  a.abf = at<uint16_t>(ws, L.abf);
+  a.rows = at<float>(ws, L.rows);
+  a.shared_out = at<float>(ws, L.shared);
+  a.ldo = D.d;
+  {
+    Stage stg(MOE_STAGE_TRAIN_FWD, s);
+    // gate/up: A = gate (A2 = up) of each expert, B = h rows by token
+    a.A = W;
+    a.A2 = W + I * d;
+    a.a_stride = 3 * I * d;
+    a.lda = D.d;
+    a.B = at<uint16_t>(ws, L.fl.hbuf);
+    a.ldb = D.d;
+    a.K = D.d;
+    a.NC = D.I / 128;
+    K2_HIP(k2::launch_train_gemm(k2::TM_FWD_GU, a, train_grid(D, a.NC), s));
+    // down: A = down [d, I], B = a rows
+    a.A = W + 2 * I * d;
+    a.A2 = nullptr;
+    a.lda = D.I;
+    a.B = a.abf;
+    a.ldb = D.I;
+    a.K = D.I;
+    a.NC = D.d / 256;
+    K2_HIP(k2::launch_train_gemm(k2::TM_FWD_DOWN, a, train_grid(D, a.NC), s));
+  }
+  Stage stg(MOE_STAGE_COMBINE, s);
+  K2_HIP(k2::launch_combine(true, false, (int)T, D.d, D.k, a.rows, at<int32_t>(saved, v.pair_row),
+                            wts, 0, D.S ? a.shared_out : nullptr, x, out, s));
+  return MOE_OK;
+}
+
+moe_status moe_train_backward(const moe_config* cfg, int64_t T, const void* dout, const void* x,
+                              const void* norm_w, const void* w_router, const void* w,
+                              const void* wt, const void* saved, float* dx, float* d_norm_w,
+                              float* d_w_router, float* d_w, float* dh_rows, float* dw, void* ws,
+                              size_t ws_bytes, void* stream) {
+  Dims D;
+  moe_status st = check_train_cfg(cfg, &D);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(T, &D)) != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  K2_PTR(dout, "dout");
+  K2_PTR(x, "x");
+  K2_PTR(norm_w, "norm_w");
+  K2_PTR(w_router, "w_router");
+  K2_PTR(w, "w");
+  K2_PTR(wt, "wt");
+  K2_PTR(saved, "saved");
+  K2_PTR(dx, "dx");
+  K2_PTR(d_norm_w, "d_norm_w");
+  K2_PTR(d_w_router, "d_w_router");
+  K2_PTR(d_w, "d_w");
+  K2_OPT_PTR(dh_rows, "dh_rows");
+  K2_OPT_PTR4(dw, "dw");
+  K2_PTR(ws, "ws");
+  const TrainLayout L = train_layout(D);
+  K2_REQUIRE(ws_bytes >= L.total, MOE_ERR_WORKSPACE,
+             "workspace too small: need " + std::to_string(L.total));
+  const TrainSaved v = train_saved(D);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int32_t* offsets = at<const int32_t>(const_cast<void*>(saved), v.offsets);
+  const int32_t* row_pair = at<const int32_t>(const_cast<void*>(saved), v.row_pair);
+  const int32_t* pair_row = at<const int32_t>(const_cast<void*>(saved), v.pair_row);
+  const float* wts = at<const float>(const_cast<void*>(saved), v.w);
+  void* sv = const_cast<void*>(saved);
+  const size_t d = (size_t)D.d, I = (size_t)D.I, P = (size_t)D.P;
+  const int64_t ldt = train_ldt(D);
+  const uint16_t* WT = static_cast<const uint16_t*>(wt);
+  float* rows = dh_rows ? dh_rows : at<float>(ws, L.rows);
+  float* shared = dh_rows ? dh_rows + P * d : at<float>(ws, L.shared);
+  {
+    Stage stg(MOE_STAGE_TILES, s);
+    K2_HIP(k2::launch_build_tiles(D.E, D.S, (int)T, D.k, 128, (int)mtile_bound(D, 128), offsets,
+                                  at<int32_t>(ws, L.mt_start), at<int32_t>(ws, L.tile_group), s));
+  }
+  k2::TrainGemmArgs a = train_rows_args(D, L, ws, offsets, row_pair);
+  a.topk_w = wts;
+  a.guq = at<uint8_t>(sv, v.guq);
+  a.gus = at<float>(sv, v.gus);
+  a.abf = at<uint16_t>(ws, L.abf);
+  a.dgu = at<uint16_t>(ws, L.dgu);
+  a.dwp = at<float>(ws, L.dwp);
+  a.rows = rows;
+  a.shared_out = shared;
+  a.ldo = D.d;
+  {
+    Stage stg(MOE_STAGE_TRAIN_DGRAD, s);
+    // down: da_raw = W_down^T dy (A = down^T [I, d]), epilogue: a~, dw, dg, du
+    a.A = WT;
+    a.a_stride = 3 * I * d;
+    a.lda = D.d;
+    a.B = static_cast<const uint16_t*>(dout);
+    a.ldb = D.d;
+    a.K = D.d;
+    a.NC = D.I / 256;
+    K2_HIP(k2::launch_train_gemm(k2::TM_BWD_DOWN, a, train_grid(D, a.NC), s));
+    // gate/up: dh_row = [W_gate; W_up]^T [dg; du] (A = [gate; up]^T [d, 2I])
+    a.A = WT + I * d;
+    a.lda = 2 * D.I;
+    a.B = a.dgu;
+    a.ldb = 2 * D.I;
+    a.K = 2 * D.I;
+    a.NC = D.d / 256;
+    K2_HIP(k2::launch_train_gemm(k2::TM_BWD_GU, a, train_grid(D, a.NC), s));
+  }
+  float* dh = at<float>(ws, L.dh);
+  float* dz = at<float>(ws, L.dz);
+  float* dht = at<float>(ws, L.dht);
+  {
+    Stage stg(MOE_STAGE_TRAIN_OTHER, s);
+    K2_HIP(k2::launch_combine(false, true, (int)T, D.d, D.k, rows, pair_row, wts, 0,
+                              D.S ? shared : nullptr, nullptr, dh, s));
+    k2::RouterBwdArgs r{};
+    r.T = (int)T;
+    r.d = D.d;
+    r.k = D.k;
+    r.E = D.E;
+    r.P = (int)D.P;
+    r.nchunk = D.I / 256;
+    r.renorm = D.renorm;
+    r.scaling = D.scaling;
+    r.eps = D.eps;
+    r.dwp = a.dwp;
+    r.pair_row = pair_row;
+    r.ids = at<const int32_t>(sv, v.ids);
+    r.s = at<const float>(sv, v.s);
+    r.dh = dh;
+    r.w_router = static_cast<const uint16_t*>(w_router);
+    r.x = static_cast<const uint16_t*>(x);
+    r.norm_w = static_cast<const uint16_t*>(norm_w);
+    r.dout = static_cast<const uint16_t*>(dout);
+    r.dz = dz;
+    r.dw_out = dw;
+    r.dh_total = dht;
+    r.dx = dx;
+    K2_HIP(k2::launch_router_norm_bwd(r, s));
+    K2_HIP(k2::launch_col_sum((int)T, D.d, dht, d_norm_w, s));
+    K2_HIP(k2::launch_router_wgrad(D.E, D.d, D.k, (int)D.P, offsets, row_pair, dz,
+                                   at<const uint8_t>(sv, v.hq), at<const float>(sv, v.hs),
+                                   d_w_router, s));
+  }
+  Stage stg(MOE_STAGE_TRAIN_WGRAD, s);
+  int32_t* pad_off = at<int32_t>(ws, L.pad_off);
+  K2_HIP(k2::launch_pad_offsets(D.E, D.G, (int)T, (int)D.P, offsets, pad_off, s));
+  k2::TransposeArgs ta{};
+  ta.offsets = offsets;
+  ta.row_pair = row_pair;
+  ta.topk_w = wts;
+  ta.pad_off = pad_off;
+  ta.E = D.E;
+  ta.G = D.G;
+  ta.T = (int)T;
+  ta.P = (int)D.P;
+  ta.k = D.k;
+  ta.ldt = (int)ldt;
+  uint16_t* dywT = at<uint16_t>(ws, L.dywT);
+  uint16_t* aT = at<uint16_t>(ws, L.aT);
+  uint16_t* dguT = at<uint16_t>(ws, L.dguT);
+  uint16_t* hT = at<uint16_t>(ws, L.hT);
+  ta.src = static_cast<const uint16_t*>(dout);
+  ta.C = D.d;
+  ta.dst = dywT;
+  K2_HIP(k2::launch_transpose_pad(1, ta, (int)ldt, s));
+  ta.src = a.abf;
+  ta.C = D.I;
+  ta.dst = aT;
+  K2_HIP(k2::launch_transpose_pad(0, ta, (int)ldt, s));
+  ta.src = a.dgu;
+  ta.C = 2 * D.I;
+  ta.dst = dguT;
+  K2_HIP(k2::launch_transpose_pad(0, ta, (int)ldt, s));
+  ta.src = nullptr;
+  ta.codes = at<const uint8_t>(sv, v.hq);
+  ta.scales = at<const float>(sv, v.hs);
+  ta.C = D.d;
+  ta.dst = hT;
+  K2_HIP(k2::launch_transpose_pad(2, ta, (int)ldt, s));
+  // dW_down [d, I] = sum (w dy)^T a~ ; dW_gate, dW_up [2I, d] = sum [dg; du]^T h~
+  k2::TrainGemmArgs g{};
+  g.G = D.G;
+  g.pad_off = pad_off;
+  g.out_stride = 3 * I * d;
+  g.A = dywT;
+  g.lda = (int)ldt;
+  g.B = aT;
+  g.ldb = (int)ldt;
+  g.MT = D.d / 256;
+  g.NT = D.I / 128;
+  g.out = d_w + 2 * I * d;
+  g.ldo = D.I;
+  K2_HIP(k2::launch_train_gemm(k2::TM_WGRAD, g, (D.G * g.MT * g.NT + 7) / 8 * 8, s));
+  g.A = dguT;
+  g.B = hT;
+  g.MT = 2 * D.I / 256;
+  g.NT = D.d / 128;
+  g.out = d_w;
+  g.ldo = D.d;
+  K2_HIP(k2::launch_train_gemm(k2::TM_WGRAD, g, (D.G * g.MT * g.NT + 7) / 8 * 8, s));
   return MOE_OK;
 }
 

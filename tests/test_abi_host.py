@@ -16,7 +16,7 @@ from sparse_moe_transformer_sigmoid_amd.build import lib_path
 from sparse_moe_transformer_sigmoid_amd.layer import config_from_shape
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADERS = [os.path.join(ROOT, "include", h) for h in ("k2moe.h", "k2mla.h")]
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("k2moe.h", "k2mla.h", "k2train.h")]
 
 pytestmark = pytest.mark.skipif(not os.path.exists(lib_path()),
                                 reason="libk2moe.so not built")

@@ -204,8 +204,8 @@ MUTATIONS = {
 def _wrap_router(mp, post):
     orig = TR.router_norm_backward
 
-    def f(p, fwd, x, norm_w, W, dout, dh, dw, exact=False, tokens=None):
-        return post(orig(p, fwd, x, norm_w, W, dout, dh, dw, exact, tokens))
+    def f(p, fwd, x, norm_w, W, dout, dh, dw, exact=False, tokens=None, bounds=None):
+        return post(orig(p, fwd, x, norm_w, W, dout, dh, dw, exact, tokens, bounds))
     mp.setattr(TR, "router_norm_backward", f)
 
 
@@ -232,16 +232,16 @@ def _no_routed_weight(mp):
 def _renorm_sign(mp):
     orig = TR.router_norm_backward
 
-    def f(p, fwd, x, norm_w, W, dout, dh, dw, exact=False, tokens=None):
-        return orig(p, fwd, x, norm_w, W, dout, dh, -dw, exact, tokens)
+    def f(p, fwd, x, norm_w, W, dout, dh, dw, exact=False, tokens=None, bounds=None):
+        return orig(p, fwd, x, norm_w, W, dout, dh, -dw, exact, tokens, bounds)
     mp.setattr(TR, "router_norm_backward", f)
 
 
 def _no_residual_grad(mp):
     orig = TR.router_norm_backward
 
-    def f(p, fwd, x, norm_w, W, dout, dh, dw, exact=False, tokens=None):
-        r = orig(p, fwd, x, norm_w, W, dout, dh, dw, exact, tokens)
+    def f(p, fwd, x, norm_w, W, dout, dh, dw, exact=False, tokens=None, bounds=None):
+        r = orig(p, fwd, x, norm_w, W, dout, dh, dw, exact, tokens, bounds)
         r["dx"] = f32(r["dx"] - f32(dout))
         return r
     mp.setattr(TR, "router_norm_backward", f)
@@ -260,8 +260,8 @@ def _down_grad_transposed(mp):
 def _no_norm_weight(mp):
     orig = TR.router_norm_backward
 
-    def f(p, fwd, x, norm_w, W, dout, dh, dw, exact=False, tokens=None):
-        return orig(p, fwd, x, np.ones_like(norm_w), W, dout, dh, dw, exact, tokens)
+    def f(p, fwd, x, norm_w, W, dout, dh, dw, exact=False, tokens=None, bounds=None):
+        return orig(p, fwd, x, np.ones_like(norm_w), W, dout, dh, dw, exact, tokens, bounds)
     mp.setattr(TR, "router_norm_backward", f)
 
 
@@ -293,3 +293,166 @@ def test_pins_catch_planted_mistake(name, monkeypatch):
         except AssertionError:
             failed += 1
     assert failed > 0, f"no pin caught: {name}"
+
+
+def test_error_model_covers_an_fp32_level_change():
+    """Another evaluation of the same step whose fp32 sums differ at the
+    level of their rounding (here: the gate and down weights scaled by
+    1 + 1e-7 noise, which moves g, da_raw, dg, du, a~ and w dy by about 1e-7
+    relative) rounds some fragile bf16 operands and fragile kept e4m3 codes
+    the other way; every output then stays within the bound the oracle
+    states for it (one bf16 step of each fragile operand, one e4m3 step of
+    each fragile code, carried through the backward)."""
+    p, x, norm_w, bias, W, dout = _problem(11, T=200, d=256, E=16, k=4, I=256)
+    fwd = TR.train_forward(p, x, norm_w, bias, W)
+    ref = TR.train_backward(p, fwd, x, norm_w, W, dout)
+    rng = np.random.default_rng(12)
+    jig = lambda a: a.astype(np.float64) * (1.0 + 1e-7 * rng.standard_normal(a.shape))
+    W2 = TR.TrainWeights(gate=jig(W.gate), up=W.up, w_router=W.w_router, down=jig(W.down))
+    fwd2 = TR.train_forward(p, x, norm_w, bias, W2)
+    assert np.array_equal(fwd2["ids"], fwd["ids"])
+    flipped = (fwd2["gq"] != fwd["gq"]) | (fwd2["uq"] != fwd["uq"])
+    assert flipped.any() and np.all(fwd["gfrag"][fwd2["gq"] != fwd["gq"]])
+    alt = TR.train_backward(p, fwd2, x, norm_w, W2, dout)
+    pairs = [(alt["dW"][n], ref["dW"][n], ref["dW_bound"][n]) for n in ("gate", "up", "down")]
+    pairs += [(alt["dh_rows"], ref["dh_rows"], ref["bound_dh_rows"]),
+              (alt["dw"], ref["dw"], ref["bound_dw"]), (alt["dx"], ref["dx"], ref["bound_dx"]),
+              (alt["d_norm_w"], ref["d_norm_w"], ref["bound_d_norm_w"]),
+              (alt["d_w_router"], ref["d_w_router"], ref["bound_d_w_router"])]
+    worst = 0.0
+    for a, r, bnd in pairs:
+        diff = np.abs(a.astype(np.float64) - r)
+        rms = np.sqrt(np.mean(r.astype(np.float64) ** 2))
+        assert np.all(diff <= bnd + 1e-5 * rms)
+        worst = max(worst, diff.max() / rms)
+    assert worst > 1e-3      # the change is visible: fragile operands and codes did flip
+
+# ------------------------------------------------------------ mutation pass
+def _plant(mp, name, fn):
+    mp.setattr(TR, name, fn)
+
+
+MUTATIONS = {
+    "silu derivative without its second term": ("_dsilu", lambda g: 1.0 / (1.0 + np.exp(-g))),
+    "silu derivative of a sigmoid gate": ("_dsilu",
+                                          lambda g: np.exp(-g) / (1.0 + np.exp(-g)) ** 2),
+}
+
+
+def _wrap_router(mp, post):
+    orig = TR.router_norm_backward
+
+    def f(p, fwd, x, norm_w, W, dout, dh, dw, exact=False, tokens=None, bounds=None):
+        return post(orig(p, fwd, x, norm_w, W, dout, dh, dw, exact, tokens, bounds))
+    mp.setattr(TR, "router_norm_backward", f)
+
+
+def _wrap_expert(mp, pre=None, post=None):
+    orig = TR.expert_backward
+
+    def f(p, fwd, dout, W, e, rows, exact=False):
+        if pre:
+            fwd = pre(fwd)
+        return post(orig(p, fwd, dout, W, e, rows, exact)) if post else orig(p, fwd, dout, W, e, rows, exact)
+    mp.setattr(TR, "expert_backward", f)
+
+
+def _no_routed_weight(mp):
+    orig = TR.expert_backward
+
+    def f(p, fwd, dout, W, e, rows, exact=False):
+        f2 = dict(fwd)
+        f2["w"] = np.ones_like(fwd["w"])
+        return orig(p, f2, dout, W, e, rows, exact)
+    mp.setattr(TR, "expert_backward", f)
+
+
+def _renorm_sign(mp):
+    orig = TR.router_norm_backward
+
+    def f(p, fwd, x, norm_w, W, dout, dh, dw, exact=False, tokens=None, bounds=None):
+        return orig(p, fwd, x, norm_w, W, dout, dh, -dw, exact, tokens, bounds)
+    mp.setattr(TR, "router_norm_backward", f)
+
+
+def _no_residual_grad(mp):
+    orig = TR.router_norm_backward
+
+    def f(p, fwd, x, norm_w, W, dout, dh, dw, exact=False, tokens=None, bounds=None):
+        r = orig(p, fwd, x, norm_w, W, dout, dh, dw, exact, tokens, bounds)
+        r["dx"] = f32(r["dx"] - f32(dout))
+        return r
+    mp.setattr(TR, "router_norm_backward", f)
+
+
+def _stored_not_used(mp):
+    orig = TR.stored_inputs
+    mp.setattr(TR, "stored_inputs", lambda fwd, rows, exact=False: orig(fwd, rows, True))
+
+
+def _down_grad_transposed(mp):
+    _wrap_expert(mp, post=lambda b: {**b, "dW_down": (b["dW_down"].reshape(-1)[::-1]
+                                                      .reshape(b["dW_down"].shape))})
+
+
+def _no_norm_weight(mp):
+    orig = TR.router_norm_backward
+
+    def f(p, fwd, x, norm_w, W, dout, dh, dw, exact=False, tokens=None, bounds=None):
+        return orig(p, fwd, x, np.ones_like(norm_w), W, dout, dh, dw, exact, tokens, bounds)
+    mp.setattr(TR, "router_norm_backward", f)
+
+
+FN_MUTATIONS = {
+    "routed weight left out of da": _no_routed_weight,
+    "renormalisation gradient with the wrong sign": _renorm_sign,
+    "residual gradient dropped": _no_residual_grad,
+    "fp32 g, u, h read instead of the stored copies": _stored_not_used,
+    "dW_down laid out wrongly": _down_grad_transposed,
+    "norm weight left out of the RMSNorm backward": _no_norm_weight,
+}
+
+PINS = [lambda: test_exact_gradient_matches_torch_autograd(0, True),
+        lambda: test_exact_gradient_matches_torch_autograd(2, False),
+        test_fp8_storage_matches_torch_with_the_same_storage]
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS) + sorted(FN_MUTATIONS))
+def test_pins_catch_planted_mistake(name, monkeypatch):
+    if name in MUTATIONS:
+        attr, fn = MUTATIONS[name]
+        _plant(monkeypatch, attr, fn)
+    else:
+        FN_MUTATIONS[name](monkeypatch)
+    failed = 0
+    for pin in PINS:
+        try:
+            pin()
+        except AssertionError:
+            failed += 1
+    assert failed > 0, f"no pin caught: {name}"
+
+
+def test_error_model_covers_an_fp32_level_change():
+    """Another evaluation of the same step whose fp32 sums differ at the
+    level of their rounding (here: the down weights scaled by 1 + 1e-7 noise,
+    which moves da_raw, dg, du, a~ and w dy by about 1e-7 relative) rounds
+    some fragile bf16 operands the other way; every weight-gradient element
+    then stays within the bound the oracle states for it (one bf16 step of
+    each fragile operand in its sum).  At the Kimi K2 width one such step of
+    a large operand moves an element by a few percent of the tensor's RMS."""
+    p, x, norm_w, bias, W, dout = _problem(11, T=200, d=256, E=16, k=4, I=256)
+    fwd = TR.train_forward(p, x, norm_w, bias, W)
+    ref = TR.train_backward(p, fwd, x, norm_w, W, dout)
+    rng = np.random.default_rng(12)
+    W2 = TR.TrainWeights(gate=W.gate, up=W.up, w_router=W.w_router,
+                         down=(W.down.astype(np.float64) *
+                               (1.0 + 1e-7 * rng.standard_normal(W.down.shape))))
+    alt = TR.train_backward(p, fwd, x, norm_w, W2, dout)
+    worst_plain = 0.0
+    for n in ("gate", "up", "down"):
+        d = np.abs(alt["dW"][n].astype(np.float64) - ref["dW"][n])
+        rms = np.sqrt(np.mean(ref["dW"][n].astype(np.float64) ** 2))
+        assert np.all(d <= ref["dW_bound"][n] + 1e-5 * rms), n
+        worst_plain = max(worst_plain, d.max() / rms)
+    assert worst_plain > 1e-4      # the change is visible: fragile operands did flip
