@@ -83,6 +83,8 @@ def parse():
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the prefill, skewed-routing and dense-FFN lines")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-train", action="store_true",
+                    help="skip the training-step line")
     ap.add_argument("--no-balance", action="store_true",
                     help="skip the routing bias update line")
     ap.add_argument("--no-mla", action="store_true",
@@ -343,6 +345,67 @@ def balance_line(steps, warmup):
                          "note": "three small launches (zero, count, update): latency-bound"}}
 
 
+def train_line(steps, warmup):
+    """One training step of the MoE layer at the K2 prefill batch (8,192
+    tokens, 384 + 1 experts, bf16 weights): moe_train_forward (keeping FP8
+    copies) then moe_train_backward (all gradients), HIP events on the launch
+    stream, per-stage times from the library's profiler.  Algorithmic work:
+    18 R I d bf16 flops (R = T k + T rows; forward 6 R I d, dgrad 6 R I d,
+    wgrad 6 R I d) and, as bytes, the weights read (bf16, twice: forward and
+    transposed copies for dgrad) plus the fp32 weight gradients written."""
+    import torch
+
+    import synth
+    from sparse_moe_transformer_sigmoid_amd import _lib as L
+    from sparse_moe_transformer_sigmoid_amd.train import K2Train
+
+    lib = L.load()
+    sh = synth.K2_PREFILL
+    inp = synth.generate_train(sh, seed=0, device="cuda")
+    layer = K2Train(inp)
+    T, d, I = sh.tokens, sh.d_model, sh.d_ff
+    G = sh.n_experts + sh.n_shared
+    out = torch.empty_like(inp.x)
+    saved = layer.saved_buffer(T)
+    grads = None
+
+    def one():
+        nonlocal grads
+        layer.forward(inp.x, saved, out)
+        grads = layer.backward(inp.dout, inp.x, saved, grads)
+
+    for _ in range(warmup):
+        one()
+    torch.cuda.synchronize()
+    nst = len(L.STAGES)
+    ms_a, n_a = (C.c_double * nst)(), (C.c_int64 * nst)()
+    L.check("moe_profile_read", lib.moe_profile_read(ms_a, n_a, 1))
+    L.check("moe_profile_enable", lib.moe_profile_enable(1))
+    s = torch.cuda.current_stream()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(s)
+    for _ in range(steps):
+        one()
+    stop.record(s)
+    torch.cuda.synchronize()
+    L.check("moe_profile_enable", lib.moe_profile_enable(0))
+    L.check("moe_profile_read", lib.moe_profile_read(ms_a, n_a, 1))
+    ms = start.elapsed_time(stop) / steps
+    stage = {nm: ms_a[i] / steps for i, nm in enumerate(L.STAGES) if ms_a[i] > 0}
+    R = T * sh.top_k + T * sh.n_shared
+    flops = 18.0 * R * I * d
+    nbytes = 2 * G * 3 * I * d * 2 + G * 3 * I * d * 4
+    tf = flops / (ms * 1e-3) / 1e12
+    line = {"workload": "k2_prefill_train_step", "tokens": T, "rows": R, "ms_per_step": ms,
+            "value": T / (ms * 1e-3), "unit": "tokens/s", "stage_ms": stage,
+            "algorithmic_tflop": flops / 1e12, "bf16_tflops": tf,
+            "frac_bf16_peak": tf / BF16_PEAK_TFLOPS, "weight_and_grad_bytes": nbytes,
+            "frac_hbm_of_weight_and_grad_bytes": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    del layer, inp, grads, saved, out
+    torch.cuda.empty_cache()
+    return line
+
+
 def sclk_file():
     """The amdgpu driver's shader-clock table of the GPU torch uses (sysfs
     pp_dpm_sclk, found by the device's PCI address), or None."""
@@ -540,6 +603,9 @@ def main():
             line["mla"][nm] = mla_line(shp_m, max(3, args.steps // 2), 2)
             print(f"# mla {nm} {line['mla'][nm]['ms_per_step']:.3f} ms", file=sys.stderr,
                   flush=True)
+    if args.workload == "decode" and not args.no_train:
+        line["train"] = train_line(max(3, args.steps // 4), 2)
+        print(f"# training step {line['train']['ms_per_step']:.2f} ms", file=sys.stderr, flush=True)
     if args.workload == "decode" and not args.no_balance:
         line["bias_update"] = balance_line(max(10, args.steps), 3)
         print(f"# bias update {line['bias_update']['ms_per_step'] * 1e3:.1f} us", file=sys.stderr,

@@ -501,8 +501,8 @@ int64_t train_ldt(const Dims& D) {
 
 struct TrainLayout {
   Layout fl;   // router / permutation sub-buffers of the forward layout
-  size_t gap, mt_start, tile_group, abf, rows, shared, dgu, dwp, dh, dz, dht, pad_off, dywT,
-      aT, dguT, hT, total;
+  size_t gap, mt_start, tile_group, abf, rows, shared, dgu, dwp, dh, dz, dht, colsum, pad_off,
+      dywT, aT, dguT, hT, total;
 };
 
 TrainLayout train_layout(const Dims& D) {
@@ -533,6 +533,7 @@ TrainLayout train_layout(const Dims& D) {
   L.dh = take(T * d * 4);
   L.dz = take(P * 4);
   L.dht = take(T * d * 4);
+  L.colsum = take(k2::col_sum_scratch_bytes((int)D.T, D.d));
   L.pad_off = take(((size_t)D.G + 1) * 4);
   L.dywT = take(d * ldt * 2);
   L.aT = take(I * ldt * 2);
@@ -1140,7 +1141,7 @@ moe_status moe_train_backward(const moe_config* cfg, int64_t T, const void* dout
     r.dh_total = dht;
     r.dx = dx;
     K2_HIP(k2::launch_router_norm_bwd(r, s));
-    K2_HIP(k2::launch_col_sum((int)T, D.d, dht, d_norm_w, s));
+    K2_HIP(k2::launch_col_sum((int)T, D.d, dht, at<double>(ws, L.colsum), d_norm_w, s));
     K2_HIP(k2::launch_router_wgrad(D.E, D.d, D.k, (int)D.P, offsets, row_pair, dz,
                                    at<const uint8_t>(sv, v.hq), at<const float>(sv, v.hs),
                                    d_w_router, s));

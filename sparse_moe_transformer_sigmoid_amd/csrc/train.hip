@@ -237,19 +237,31 @@ __global__ __launch_bounds__(256, 2) void train_gemm_kernel(const TrainGemmArgs 
 
   // ---------------------------------------------------------- epilogues
   if constexpr (MODE == TM_WGRAD) {
-    // C[m][n] -> out[grp][m][n] (fp32, nn.Linear layout of the gradient)
-    float* out = g.out + (size_t)grp * g.out_stride;
+    // C[m][n] -> out[grp][m][n] (fp32, nn.Linear layout of the gradient).
+    // Each wave turns 16 of its rows at a time around in LDS so that 32
+    // lanes store one row's 128 columns (512 contiguous bytes), non-temporal
+    // (the gradient is not read again here).
+    constexpr int OT_LD = TN + 4;
+    __shared__ __attribute__((aligned(16))) float ot[4][16 * OT_LD];
+    float* out = g.out + (size_t)grp * g.out_stride + (size_t)TN * wi.ni;
+    float* tw = ot[wave];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
-        const size_t n = (size_t)(TN * wi.ni + 16 * nt + l16);
+      for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const size_t m = (size_t)(256 * wi.mi + TMW * wave + 16 * mt + 4 * q4 + r);
-          out[m * g.ldo + n] = acc[mt][nt][r];
-        }
+        for (int r = 0; r < 4; ++r) tw[(4 * q4 + r) * OT_LD + 16 * nt + l16] = acc[mt][nt][r];
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int row = 2 * i + (lane >> 5), col = 4 * (lane & 31);
+        const v4f v = *reinterpret_cast<const v4f*>(&tw[row * OT_LD + col]);
+        const size_t m = (size_t)(256 * wi.mi + TMW * wave + 16 * mt + row);
+        __builtin_nontemporal_store(v, reinterpret_cast<v4f*>(out + m * g.ldo + col));
       }
+      __builtin_amdgcn_wave_barrier();
+    }
     return;
   }
   const int ntt = (wi.mcount + 15) >> 4;
@@ -642,12 +654,26 @@ __global__ __launch_bounds__(256) void router_norm_bwd_kernel(const RouterBwdArg
   }
 }
 
-// Column sums over tokens (fixed order): out[c] = sum_t in[t][c], in fp64
-__global__ __launch_bounds__(256) void col_sum_kernel(int T, int d, const float* in, float* out) {
+// Column sums over tokens in a fixed order, in fp64: partial sums over
+// chunks of COL_CHUNK tokens (one thread per column and chunk), then the
+// chunks in ascending order.
+constexpr int COL_CHUNK = 128;
+__global__ __launch_bounds__(256) void col_partial_kernel(int T, int d, const float* in,
+                                                          double* part) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= d) return;
+  const int t0 = blockIdx.y * COL_CHUNK, t1 = min(t0 + COL_CHUNK, T);
+  double s = 0.0;
+  for (int t = t0; t < t1; ++t) s += (double)in[(size_t)t * d + c];
+  part[(size_t)blockIdx.y * d + c] = s;
+}
+
+__global__ __launch_bounds__(256) void col_sum_kernel(int nchunk, int d, const double* part,
+                                                      float* out) {
   const int c = blockIdx.x * 256 + threadIdx.x;
   if (c >= d) return;
   double s = 0.0;
-  for (int t = 0; t < T; ++t) s += (double)in[(size_t)t * d + c];
+  for (int k = 0; k < nchunk; ++k) s += part[(size_t)k * d + c];
   out[c] = (float)s;
 }
 
@@ -732,8 +758,15 @@ hipError_t launch_router_norm_bwd(const RouterBwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_col_sum(int T, int d, const float* in, float* out, hipStream_t s) {
-  col_sum_kernel<<<(d + 255) / 256, 256, 0, s>>>(T, d, in, out);
+size_t col_sum_scratch_bytes(int T, int d) {
+  return (size_t)((T + COL_CHUNK - 1) / COL_CHUNK) * d * sizeof(double);
+}
+
+hipError_t launch_col_sum(int T, int d, const float* in, double* scratch, float* out,
+                          hipStream_t s) {
+  const int nchunk = (T + COL_CHUNK - 1) / COL_CHUNK;
+  col_partial_kernel<<<dim3((d + 255) / 256, nchunk), 256, 0, s>>>(T, d, in, scratch);
+  col_sum_kernel<<<(d + 255) / 256, 256, 0, s>>>(nchunk, d, scratch, out);
   return hipGetLastError();
 }
 

@@ -89,7 +89,9 @@ struct RouterBwdArgs {
   float* dx;                  // [T, d]
 };
 hipError_t launch_router_norm_bwd(const RouterBwdArgs& a, hipStream_t s);
-hipError_t launch_col_sum(int T, int d, const float* in, float* out, hipStream_t s);
+size_t col_sum_scratch_bytes(int T, int d);
+hipError_t launch_col_sum(int T, int d, const float* in, double* scratch, float* out,
+                          hipStream_t s);
 hipError_t launch_router_wgrad(int E, int d, int k, int P, const int32_t* offsets,
                                const int32_t* row_pair, const float* dz, const uint8_t* hq,
                                const float* hs, float* dwr, hipStream_t s);
