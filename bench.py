@@ -396,11 +396,18 @@ def train_line(steps, warmup):
     flops = 18.0 * R * I * d
     nbytes = 2 * G * 3 * I * d * 2 + G * 3 * I * d * 4
     tf = flops / (ms * 1e-3) / 1e12
+    gbs = nbytes / (ms * 1e-3) / 1e9
     line = {"workload": "k2_prefill_train_step", "tokens": T, "rows": R, "ms_per_step": ms,
             "value": T / (ms * 1e-3), "unit": "tokens/s", "stage_ms": stage,
             "algorithmic_tflop": flops / 1e12, "bf16_tflops": tf,
-            "frac_bf16_peak": tf / BF16_PEAK_TFLOPS, "weight_and_grad_bytes": nbytes,
-            "frac_hbm_of_weight_and_grad_bytes": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+            "frac_bf16_peak": tf / BF16_PEAK_TFLOPS,
+            # 18 R I d flops over the bytes below is ~144 flop/B, under the bf16
+            # ridge point (312 flop/B): the step's roofline is HBM
+            "roofline": {"kernel": "whole step", "bound": "hbm", "achieved": gbs,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                         "algorithmic_bytes": nbytes,
+                         "note": "bf16 expert weights read twice (forward; transposed copies "
+                                 "for dgrad) and fp32 weight gradients written once"}}
     del layer, inp, grads, saved, out
     torch.cuda.empty_cache()
     return line
