@@ -33,7 +33,7 @@ constexpr int DQ = DL + DR;       // absorbed query / cache row width
 constexpr int DN = 128;           // query/key features without position (qk_nope)
 constexpr int DV = 128;           // value features (v_head)
 constexpr int PT = 32;            // cache positions per attention step
-constexpr int CT_LD = DQ + 8;     // bf16 stride of a row-major cache row in LDS
+constexpr int CT_LD = DL + 8;     // bf16 stride of a row-major cache latent in LDS
 // bf16 stride of a transposed latent row in LDS: 18 dwords, so the four
 // 16-row chunks a fill wave writes in one instruction fall on two bank halves
 // and the 16 rows a compute wave reads on 16 distinct even banks
@@ -271,16 +271,19 @@ __global__ __launch_bounds__(256) void mla_qabsorb_kernel(
 }
 
 // ------------------------------------------------------- latent attention
-// Eight waves: waves 0-3 compute, wave w = (token, 8 heads); waves 4-7 fill
-// LDS.  mode 0 (one new token per sequence, heads % 32 == 0): the compute
-// waves are one token's four groups of 8 heads (a workgroup covers 32 heads);
-// mode 1: up to four consecutive tokens of one sequence with one group of 8.
-// The cache positions [lo, hi) of the work item's split are visited in steps
-// of 32.  While the compute waves use one LDS buffer the fill waves load the
-// next step's cache rows into the other: the latent codes as exact bf16
-// values (every e4m3 value is one), twice -- row-major [pos][576] with the
-// rotary key (the A operand of the scores) and transposed [latent][pos] (the
-// A operand of the value sum) -- and the latent's 1x128 scales [block][pos].
+// Eight waves, each a column block of 8 (token, head) pairs.  mode 0 (one new
+// token per sequence): the waves are one token's groups of 8 heads, so a
+// workgroup covers min(heads, 64) heads and reads each cache position once for
+// all of them; mode 1: up to eight consecutive tokens of one sequence with one
+// group of 8 heads.  The cache positions [lo, hi) of the work item's split are
+// visited in steps of 32.  The cache bytes of a step (latent codes, rotary
+// keys, scales) are copied straight from global memory into one of NS LDS
+// stages (global_load_lds, no staging registers), NS - 1 steps ahead of the
+// compute.  Per step every wave first converts its share of the step's codes
+// into exact bf16 values (every e4m3 value is one), twice -- row-major
+// [pos][512] (the A operand of the scores) and transposed [latent][pos] (the
+// A operand of the value sum) -- and then computes; the rotary keys and the
+// scales are read from their stage as they arrived.
 //
 // Sums to fp32 precision: the 16 MFMA columns are 8 heads x {hi, lo}, the
 // bf16 high part of a value and the bf16 rounding of its remainder, so one
@@ -302,6 +305,7 @@ struct AttnArgs {
   float* part_o;             // [nsplit, T, H, 512]
   float* part_ml;            // [nsplit, T, H, 2]
   int T, H, n_new, max_len, nsplit, chunk, mode, items_per_split;
+  int hw;                    // mode 0: heads per workgroup
 };
 
 // the value of the lane 8 apart in the same 16-lane row (a row rotated by 8)
@@ -314,144 +318,187 @@ __device__ __forceinline__ v4f mfma_bf16(v8bf a, v8bf b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// the bf16 high part of v (round to nearest even) or the bf16 rounding of
-// the remainder v - high
-__device__ __forceinline__ uint32_t bf16_half(float v, bool lo) {
-  const uint32_t hb = f32_to_bf16_rne(v);
-  return lo ? f32_to_bf16_rne(v - bf16_to_f32(hb)) : hb;
+// two fp32 values -> packed bf16 (a low), round to nearest even (gfx950's
+// converter)
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){a, b}, v2bf));
+}
+// the bf16 high parts of (a, b) (lo = 0) or the bf16 roundings of their
+// remainders a - high (lo = 1; exact in fp32), packed
+__device__ __forceinline__ uint32_t bf16_half2(float a, float b, float lo) {
+  const uint32_t hb = pack_bf16(a, b);
+  return pack_bf16(fmaf(-lo, __uint_as_float(hb << 16), a),
+                   fmaf(-lo, __uint_as_float(hb & 0xFFFF0000u), b));
 }
 
 constexpr int CT_ELEMS = PT * CT_LD, TR_ELEMS = DL * TR_LD;
-constexpr int HPW = 8;   // heads per compute wave
+constexpr int HPW = 8;   // heads per wave
+constexpr int AW = 8;    // waves per workgroup
+constexpr int NS = 3;    // LDS stages of raw cache bytes (copies run NS - 1 steps ahead)
+
+// Direct global -> LDS copies (global_load_lds_dword / _dwordx4): lane l's 4
+// or 16 bytes from global [base + voff] land at LDS byte address M0 + l *
+// size.  They complete in issue order with the other vector loads (vmcnt);
+// the compiler does not track them, so the kernel waits for them itself.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+__device__ __forceinline__ void lds_copy16(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               : : "v"(voff), "s"(base), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_copy4(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+               : : "v"(voff), "s"(base), "s"(lds) : "memory", "m0");
+}
+// wait until at most n (wave-uniform, 0..9) of this wave's vector loads are
+// outstanding
+__device__ __forceinline__ void vm_wait(int n) {
+  switch (n) {
+    case 0: asm volatile("s_waitcnt vmcnt(0)" : : : "memory"); break;
+    case 1: asm volatile("s_waitcnt vmcnt(1)" : : : "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(2)" : : : "memory"); break;
+    case 3: asm volatile("s_waitcnt vmcnt(3)" : : : "memory"); break;
+    case 4: asm volatile("s_waitcnt vmcnt(4)" : : : "memory"); break;
+    case 5: asm volatile("s_waitcnt vmcnt(5)" : : : "memory"); break;
+    case 6: asm volatile("s_waitcnt vmcnt(6)" : : : "memory"); break;
+    case 7: asm volatile("s_waitcnt vmcnt(7)" : : : "memory"); break;
+    case 8: asm volatile("s_waitcnt vmcnt(8)" : : : "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(9)" : : : "memory"); break;
+  }
+}
 
 __global__ __launch_bounds__(512, 1) void mla_attn_kernel(const AttnArgs g) {
-  __shared__ __attribute__((aligned(16))) uint16_t ct[2][CT_ELEMS];   // row-major cache rows
-  __shared__ __attribute__((aligned(16))) uint16_t tr[2][TR_ELEMS];   // transposed latents
-  __shared__ __attribute__((aligned(16))) float sc_l[2][DL / QBLK][PT];  // latent scales
-  __shared__ int kv_sh[4];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const bool compute = wave < 4;
+  // raw stages: codes [pos][512] with the 16-byte chunk c of position p at
+  // chunk slot c ^ ((p / 2) % 16); rotary keys [pos][64] bf16 with chunk c at
+  // slot c ^ ((p / 2) % 8) (both so that 16 consecutive positions read at one
+  // chunk fall on distinct banks); scales [block][pos]
+  __shared__ __attribute__((aligned(16))) uint8_t cr[NS][PT * DL];
+  __shared__ __attribute__((aligned(16))) uint16_t crope[NS][PT * DR];
+  __shared__ __attribute__((aligned(16))) float csc[NS][DL / QBLK][PT];
+  __shared__ __attribute__((aligned(16))) uint16_t ct[CT_ELEMS];   // row-major bf16 latents
+  __shared__ __attribute__((aligned(16))) uint16_t tr[TR_ELEMS];   // transposed bf16 latents
+  __shared__ int kv_sh[AW];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q4 = lane >> 4, l16 = lane & 15;
   const bool lo_col = l16 >= HPW;           // this lane's column holds the low halves
+  const float lo_f = lo_col ? 1.f : 0.f;
   const int item = blockIdx.x % g.items_per_split, split = blockIdx.x / g.items_per_split;
-  const int hg_n = g.H / HPW;
-  const int cw = wave & 3;   // compute-wave index this wave stands for
-  // the compute wave's token and head group (fill waves compute the same
-  // values for the sequence, which is common to the workgroup)
-  int t, hg, seq;
+  // the wave's token and first head (every wave of a workgroup is on one
+  // sequence; waves past the token count or the head count only convert)
+  int t, h0;
   bool active;
   if (g.mode == 0) {
-    t = item / (hg_n / 4);
-    hg = (item % (hg_n / 4)) * 4 + cw;
-    active = true;
+    const int ngrp = g.H / g.hw;
+    t = item / ngrp;
+    h0 = (item % ngrp) * g.hw + wave * HPW;
+    active = wave * HPW < g.hw;
   } else {
-    const int tb_n = (g.n_new + 3) / 4;
+    const int hg_n = g.H / HPW;
+    const int tb_n = (g.n_new + AW - 1) / AW;
     const int per_seq = tb_n * hg_n;
     const int s_ = item / per_seq, rem = item % per_seq;
     const int tb = rem / hg_n;
-    hg = rem % hg_n;
-    const int ti = tb * 4 + cw;
+    h0 = (rem % hg_n) * HPW;
+    const int ti = tb * AW + wave;
     active = ti < g.n_new;
     t = s_ * g.n_new + min(ti, g.n_new - 1);
   }
+  int seq;
   const int qpos = token_pos(g.cached_len, t, g.n_new, g.max_len, &seq);
-  if (compute && lane == 0) kv_sh[cw] = active ? qpos + 1 : 0;
+  if (lane == 0) kv_sh[wave] = active ? qpos + 1 : 0;
   __syncthreads();
   // the workgroup's positions: its split's range, up to its last query position
-  const int wg_end = max(max(kv_sh[0], kv_sh[1]), max(kv_sh[2], kv_sh[3]));
+  int wg_end = 0;
+#pragma unroll
+  for (int w = 0; w < AW; ++w) wg_end = max(wg_end, kv_sh[w]);
   const int lo = split * g.chunk, hi = min(wg_end, lo + g.chunk);
-  const int my_end = (compute && active) ? qpos + 1 : 0;
-  const int h = hg * HPW + (l16 & (HPW - 1));   // this lane's head
+  const int my_end = active ? qpos + 1 : 0;
+  const int h = h0 + (l16 & (HPW - 1));   // this lane's head
   const size_t cbase = (size_t)seq * g.max_len;
+  const uint8_t* codes_seq = g.c_codes + cbase * DL;
+  const uint16_t* rope_seq = g.c_rope + cbase * DR;
+  const float* sc_seq = g.c_scales + cbase * (DL / QBLK);
 
-  // fill waves: positions p0 .. p0 + 31, loaded into registers (zeros past hi)
-  // two steps before they are written into an LDS buffer, so the loads of a
-  // step have two steps of compute to arrive.  Item = (latent chunk of 16
-  // features, pair of positions), two items per thread; then the rotary keys
-  // (thread = position, 8 features) and the scales (thread = block, position).
-  const int ftid = tid - 256;
-  struct Raw {
-    uint4 cv[2][2];   // [item][position of the pair]: 16 codes each
-    uint4 rope;
-    float sc;
-  };
-  auto load_raw = [&](Raw& r, int p0) {
+  // copies of the step at p0 into stage st; positions past hi copy position
+  // hi - 1 (written, finite), which the mask and p = 0 leave without effect.
+  // Wave w: code instructions 2w, 2w + 1 (two positions each); waves 0-3 one
+  // rotary instruction (8 positions), waves 4-5 one scale instruction (two
+  // blocks): 3 copies per step for waves 0-5, 2 for waves 6-7
+  const int n_copies = wave < 6 ? 3 : 2;
+  auto issue = [&](int st, int p0) {
+    const int plast = hi - 1;
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int itm = ftid + 256 * it, sub = itm >> 4, pr = itm & 15;
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int p = p0 + 2 * pr + j;
-        r.cv[it][j] = p < hi ? *reinterpret_cast<const uint4*>(g.c_codes + (cbase + p) * DL +
-                                                                16 * sub)
-                             : make_uint4(0, 0, 0, 0);
-      }
+    for (int u = 0; u < 2; ++u) {
+      const int i = 2 * wave + u;
+      const int pc = min(p0 + 2 * i + (lane >> 5), plast);
+      const int c = (lane & 31) ^ (i & 15);
+      lds_copy16(codes_seq, (uint32_t)(pc * DL + 16 * c), lds_addr(&cr[st][i * 1024]));
     }
-    const int pr_ = p0 + (ftid >> 3);
-    r.rope = pr_ < hi ? *reinterpret_cast<const uint4*>(g.c_rope + (cbase + pr_) * DR +
-                                                        8 * (ftid & 7))
-                      : make_uint4(0, 0, 0, 0);
-    r.sc = 0.f;
-    if (ftid < (DL / QBLK) * PT) {
-      const int pp = p0 + ftid % PT;
-      if (pp < hi) r.sc = g.c_scales[(cbase + pp) * (DL / QBLK) + ftid / PT];
+    if (wave < 4) {
+      const int p = 8 * wave + (lane >> 3);
+      const int pc = min(p0 + p, plast);
+      const int c = (lane & 7) ^ ((p >> 1) & 7);
+      lds_copy16(rope_seq, (uint32_t)(pc * DR * 2 + 16 * c), lds_addr(&crope[st][wave * 512]));
+    } else if (wave < 6) {
+      const int i = wave - 4, blk = 2 * i + (lane >> 5);
+      const int pc = min(p0 + (lane & 31), plast);
+      lds_copy4(sc_seq, (uint32_t)((pc * (DL / QBLK) + blk) * 4), lds_addr(&csc[st][2 * i][0]));
     }
   };
-  auto store_raw = [&](int b, const Raw& r) {
+  // stage st's codes -> ct, tr: thread = (16-code chunk sub, position pair pr)
+  auto convert = [&](int st) {
+    const int sub = tid >> 4, pr = tid & 15;
+    uint32_t pk[2][8];   // bf16 pairs: codes 2k, 2k+1 of position 2 pr + j
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int itm = ftid + 256 * it, sub = itm >> 4, pr = itm & 15;
-      uint32_t pk[2][8];   // bf16 pairs: codes 2k, 2k+1 of position 2 pr + j
+    for (int j = 0; j < 2; ++j) {
+      const uint4 cv =
+          *reinterpret_cast<const uint4*>(&cr[st][(2 * pr + j) * DL + 16 * (sub ^ pr)]);
+      const uint32_t w4[4] = {cv.x, cv.y, cv.z, cv.w};
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const uint32_t w4[4] = {r.cv[it][j].x, r.cv[it][j].y, r.cv[it][j].z, r.cv[it][j].w};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          pk[j][2 * k] = __builtin_bit_cast(
-              uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w4[k], 1.f, false));
-          pk[j][2 * k + 1] = __builtin_bit_cast(
-              uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w4[k], 1.f, true));
-        }
-        uint4* dst = reinterpret_cast<uint4*>(&ct[b][(2 * pr + j) * CT_LD + 16 * sub]);
-        dst[0] = make_uint4(pk[j][0], pk[j][1], pk[j][2], pk[j][3]);
-        dst[1] = make_uint4(pk[j][4], pk[j][5], pk[j][6], pk[j][7]);
+      for (int k = 0; k < 4; ++k) {
+        pk[j][2 * k] = __builtin_bit_cast(
+            uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w4[k], 1.f, false));
+        pk[j][2 * k + 1] = __builtin_bit_cast(
+            uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w4[k], 1.f, true));
       }
-      // transposed: feature 16 sub + i, positions 2 pr and 2 pr + 1 (i is a
-      // compile-time index: a per-thread index into pk would become select
-      // chains over all its registers)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int w = i >> 1;
-        const uint32_t v = (i & 1) ? ((pk[0][w] >> 16) | (pk[1][w] & 0xFFFF0000u))
-                                   : ((pk[0][w] & 0xFFFFu) | (pk[1][w] << 16));
-        *reinterpret_cast<uint32_t*>(&tr[b][(16 * sub + i) * TR_LD + 2 * pr]) = v;
-      }
+      uint4* dst = reinterpret_cast<uint4*>(&ct[(2 * pr + j) * CT_LD + 16 * sub]);
+      dst[0] = make_uint4(pk[j][0], pk[j][1], pk[j][2], pk[j][3]);
+      dst[1] = make_uint4(pk[j][4], pk[j][5], pk[j][6], pk[j][7]);
     }
-    *reinterpret_cast<uint4*>(&ct[b][(ftid >> 3) * CT_LD + DL + 8 * (ftid & 7)]) = r.rope;
-    if (ftid < (DL / QBLK) * PT) sc_l[b][ftid / PT][ftid % PT] = r.sc;
+    // transposed: feature 16 sub + i, positions 2 pr and 2 pr + 1 (i is a
+    // compile-time index: a per-thread index into pk would become select
+    // chains over all its registers)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int w = i >> 1;
+      const uint32_t v = (i & 1) ? ((pk[0][w] >> 16) | (pk[1][w] & 0xFFFF0000u))
+                                 : ((pk[0][w] & 0xFFFFu) | (pk[1][w] << 16));
+      *reinterpret_cast<uint32_t*>(&tr[(16 * sub + i) * TR_LD + 2 * pr]) = v;
+    }
   };
 
-  // compute waves: the query of head h as B fragments, high or low halves by
-  // column (dims 32 ks + 8 q4 .. + 7)
+  // the query of head h as B fragments, high or low halves by column (dims
+  // 32 ks + 8 q4 .. + 7)
   v8bf qb[DQ / 32];
   v4f o[DL / 16];
   float mrun = -INFINITY, lrun = 0.f;
-  if (compute) {
+  if (active) {
     const float* qp = g.qcat + ((size_t)t * g.H + h) * DQ + 8 * q4;
 #pragma unroll
     for (int ks = 0; ks < DQ / 32; ++ks) {
       const float4 a = *reinterpret_cast<const float4*>(qp + 32 * ks);
       const float4 c = *reinterpret_cast<const float4*>(qp + 32 * ks + 4);
-      const uint4 v = make_uint4(bf16_half(a.x, lo_col) | (bf16_half(a.y, lo_col) << 16),
-                                 bf16_half(a.z, lo_col) | (bf16_half(a.w, lo_col) << 16),
-                                 bf16_half(c.x, lo_col) | (bf16_half(c.y, lo_col) << 16),
-                                 bf16_half(c.z, lo_col) | (bf16_half(c.w, lo_col) << 16));
+      const uint4 v = make_uint4(bf16_half2(a.x, a.y, lo_f), bf16_half2(a.z, a.w, lo_f),
+                                 bf16_half2(c.x, c.y, lo_f), bf16_half2(c.z, c.w, lo_f));
       qb[ks] = __builtin_bit_cast(v8bf, v);
     }
 #pragma unroll
     for (int i = 0; i < DL / 16; ++i) o[i] = v4f{0.f, 0.f, 0.f, 0.f};
   }
-  auto step = [&](int b, int p0) {
+  auto step = [&](int st, int p0) {
     // ---- scores: S^T[pos, column] for positions p0 + 16 pt + 4 q4 + i
     v4f s[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
@@ -459,15 +506,25 @@ __global__ __launch_bounds__(512, 1) void mla_attn_kernel(const AttnArgs g) {
 #pragma unroll
       for (int pt = 0; pt < 2; ++pt) {
         v4f acc = {0.f, 0.f, 0.f, 0.f};
-        const uint16_t* ap = &ct[b][(16 * pt + l16) * CT_LD + 8 * q4];
-        const int ks0 = blk * 4, ks1 = blk < DL / QBLK ? ks0 + 4 : DQ / 32;
+        const int p = 16 * pt + l16;
+        if (blk < DL / QBLK) {
+          const uint16_t* ap = &ct[p * CT_LD + 8 * q4];
 #pragma unroll
-        for (int ks = ks0; ks < ks1; ++ks) {
-          const uint4 av = *reinterpret_cast<const uint4*>(ap + 32 * ks);
-          acc = mfma_bf16(__builtin_bit_cast(v8bf, av), qb[ks], acc);
+          for (int ks = blk * 4; ks < blk * 4 + 4; ++ks) {
+            const uint4 av = *reinterpret_cast<const uint4*>(ap + 32 * ks);
+            acc = mfma_bf16(__builtin_bit_cast(v8bf, av), qb[ks], acc);
+          }
+        } else {
+#pragma unroll
+          for (int ks = DL / 32; ks < DQ / 32; ++ks) {
+            const int c = 4 * (ks - DL / 32) + q4;   // rotary chunk of 8 features
+            const uint4 av = *reinterpret_cast<const uint4*>(
+                &crope[st][p * DR + 8 * (c ^ ((p >> 1) & 7))]);
+            acc = mfma_bf16(__builtin_bit_cast(v8bf, av), qb[ks], acc);
+          }
         }
         if (blk < DL / QBLK) {
-          const float4 sc = *reinterpret_cast<const float4*>(&sc_l[b][blk][16 * pt + 4 * q4]);
+          const float4 sc = *reinterpret_cast<const float4*>(&csc[st][blk][16 * pt + 4 * q4]);
           s[pt][0] = fmaf(sc.x, acc[0], s[pt][0]);
           s[pt][1] = fmaf(sc.y, acc[1], s[pt][1]);
           s[pt][2] = fmaf(sc.z, acc[2], s[pt][2]);
@@ -512,68 +569,48 @@ __global__ __launch_bounds__(512, 1) void mla_attn_kernel(const AttnArgs g) {
     lsum += __shfl_xor(lsum, 32);
     lrun = lrun * alpha + lsum;
     mrun = mnew;
+    // rescale the outputs only when some head's maximum moved (alpha = 1
+    // leaves them unchanged)
+    if (__any(alpha != 1.f)) {
+#pragma unroll
+      for (int nt = 0; nt < DL / 16; ++nt) o[nt] *= alpha;
+    }
     // ---- O^T[latent, column] = alpha O^T + C_b^T (p scale_b)^T, block by block
 #pragma unroll
     for (int blk = 0; blk < DL / QBLK; ++blk) {
-      const float4 s0 = *reinterpret_cast<const float4*>(&sc_l[b][blk][4 * q4]);
-      const float4 s1 = *reinterpret_cast<const float4*>(&sc_l[b][blk][16 + 4 * q4]);
+      const float4 s0 = *reinterpret_cast<const float4*>(&csc[st][blk][4 * q4]);
+      const float4 s1 = *reinterpret_cast<const float4*>(&csc[st][blk][16 + 4 * q4]);
       const uint4 pv = make_uint4(
-          bf16_half(ps[0][0] * s0.x, lo_col) | (bf16_half(ps[0][1] * s0.y, lo_col) << 16),
-          bf16_half(ps[0][2] * s0.z, lo_col) | (bf16_half(ps[0][3] * s0.w, lo_col) << 16),
-          bf16_half(ps[1][0] * s1.x, lo_col) | (bf16_half(ps[1][1] * s1.y, lo_col) << 16),
-          bf16_half(ps[1][2] * s1.z, lo_col) | (bf16_half(ps[1][3] * s1.w, lo_col) << 16));
+          bf16_half2(ps[0][0] * s0.x, ps[0][1] * s0.y, lo_f),
+          bf16_half2(ps[0][2] * s0.z, ps[0][3] * s0.w, lo_f),
+          bf16_half2(ps[1][0] * s1.x, ps[1][1] * s1.y, lo_f),
+          bf16_half2(ps[1][2] * s1.z, ps[1][3] * s1.w, lo_f));
       const v8bf pb = __builtin_bit_cast(v8bf, pv);
 #pragma unroll
       for (int nt = blk * 8; nt < blk * 8 + 8; ++nt) {
-        const uint16_t* tp = &tr[b][(16 * nt + l16) * TR_LD + 4 * q4];
+        const uint16_t* tp = &tr[(16 * nt + l16) * TR_LD + 4 * q4];
         const uint2 a0 = *reinterpret_cast<const uint2*>(tp);
         const uint2 a1 = *reinterpret_cast<const uint2*>(tp + 16);
         const v8bf av = __builtin_bit_cast(v8bf, make_uint4(a0.x, a0.y, a1.x, a1.y));
-        o[nt] = mfma_bf16(av, pb, o[nt] * alpha);
+        o[nt] = mfma_bf16(av, pb, o[nt]);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // The two roles run separate loops with the same barriers (one before the
-  // first step, one after each step), so the compute waves' query fragments
-  // and accumulators are not live across the fill code.
-  if (!compute) {
-    // register ring of two steps: step k + 1 is written while step k + 3's
-    // loads are issued (positions past hi load nothing)
-    Raw ra, rb;
-    if (lo < hi) {
-      load_raw(ra, lo);
-      load_raw(rb, lo + PT);
-      store_raw(0, ra);
-      load_raw(ra, lo + 2 * PT);
-    }
+  // step k: wait for its copies, barrier (they are visible, and step k - 1's
+  // compute is done with ct, tr and stage (k - 1) % NS), copy step k + NS - 1
+  // into that stage, convert, barrier, compute
+  const int nsteps = lo < hi ? (hi - lo + PT - 1) / PT : 0;
+  for (int j = 0; j < NS - 1 && j < nsteps; ++j) issue(j, lo + j * PT);
+  for (int k = 0; k < nsteps; ++k) {
+    const int st = k % NS, p0 = lo + k * PT;
+    vm_wait(n_copies * min(NS - 2, nsteps - 1 - k));
     __syncthreads();
-    int b = 0;
-    for (int p0 = lo; p0 < hi; p0 += 2 * PT) {
-      // step p0 (buffer b) is being computed; write step p0 + PT from rb
-      if (p0 + PT < hi) {
-        store_raw(b ^ 1, rb);
-        load_raw(rb, p0 + 3 * PT);
-      }
-      __syncthreads();
-      if (p0 + PT >= hi) break;
-      // step p0 + PT (buffer b ^ 1) is being computed; write step p0 + 2 PT from ra
-      if (p0 + 2 * PT < hi) {
-        store_raw(b, ra);
-        load_raw(ra, p0 + 4 * PT);
-      }
-      __syncthreads();
-    }
-    return;
-  }
-  __syncthreads();
-  {
-    int b = 0;
-    for (int p0 = lo; p0 < hi; p0 += PT, b ^= 1) {
-      if (active && p0 < my_end) step(b, p0);
-      __syncthreads();
-    }
+    if (k + NS - 1 < nsteps) issue((k + NS - 1) % NS, p0 + (NS - 1) * PT);
+    convert(st);
+    __syncthreads();
+    if (active && p0 < my_end) step(st, p0);
   }
   if (!active) return;
   // a head's two columns (contributions of the high and low p halves) add
@@ -760,8 +797,7 @@ hipError_t launch_mla_attn(int T, int H, int n_seq, int n_new, int max_len, int 
   a.max_len = max_len;
   a.nsplit = nsplit;
   a.chunk = chunk;
-  a.mode = (n_new == 1 && H % 32 == 0) ? 0 : 1;
-  a.items_per_split = a.mode == 0 ? T * (H / 32) : n_seq * ((n_new + 3) / 4) * (H / 8);
+  a.items_per_split = mla_attn_items(T, H, n_seq, n_new, &a.mode, &a.hw);
   mla_attn_kernel<<<a.items_per_split * nsplit, 512, 0, s>>>(a);
   return hipGetLastError();
 }

@@ -155,11 +155,12 @@ int gemm_split(int T, int N, int K) {
   return best;
 }
 
-// attention position splits: enough work items for the chip, >= 256 positions each
+// attention position splits: a work item per CU (one workgroup fills a CU's LDS), >= 256
+// positions each
 void attn_split(int T, int H, int n_seq, int n_new, int max_len, int* nsplit, int* chunk) {
-  const bool mode0 = n_new == 1 && H % 32 == 0;
-  const int items = std::max(1, mode0 ? T * (H / 32) : n_seq * ((n_new + 3) / 4) * (H / 8));
-  int ns = std::max(1, (512 + items - 1) / items);
+  int mode, hw;
+  const int items = std::max(1, k2::mla_attn_items(T, H, n_seq, n_new, &mode, &hw));
+  int ns = std::max(1, (256 + items - 1) / items);
   ns = std::min(ns, std::max(1, max_len / 256));
   int ch = (max_len + ns - 1) / ns;
   ch = (ch + 31) / 32 * 32;

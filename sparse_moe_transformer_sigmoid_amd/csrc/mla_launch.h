@@ -31,6 +31,21 @@ hipError_t launch_mla_qabsorb(int T, int H, float smscale, const float* q, const
                               const float* s_kvb, const double* inv_freq,
                               const int32_t* cached_len, int n_new, int max_len, float* qcat,
                               hipStream_t s);
+// work items per position split of the attention kernel, and its mode:
+// mode 0 (one new token per sequence and heads a multiple of min(heads, 64)):
+// (token, group of hw = min(heads, 64) heads); mode 1: (sequence, 8 new
+// tokens, 8 heads)
+inline int mla_attn_items(int T, int H, int n_seq, int n_new, int* mode, int* hw) {
+  const int w = H < 64 ? H : 64;
+  if (n_new == 1 && H % w == 0) {
+    *mode = 0;
+    *hw = w;
+    return T * (H / w);
+  }
+  *mode = 1;
+  *hw = 8;
+  return n_seq * ((n_new + 7) / 8) * (H / 8);
+}
 hipError_t launch_mla_attn(int T, int H, int n_seq, int n_new, int max_len, int nsplit,
                            int chunk, const uint8_t* c_codes, const float* c_scales,
                            const uint16_t* c_rope, const float* qcat,
