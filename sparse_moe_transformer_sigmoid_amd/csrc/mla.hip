@@ -213,63 +213,6 @@ __global__ __launch_bounds__(256) void mla_latent_kernel(
 }
 
 // --------------------------------------------------------- query absorption
-constexpr int QA_TB = 16;   // tokens per workgroup
-
-// qcat[t, h] = scale * [W_uk^T q_nope (512), rope(q_pe) (64)] in fp32.
-// W_uk of head h: key-value up-projection rows h*(DN+DV) .. + DN - 1 (one
-// 128-row scale block), dequantised as code * block scale; fp32 sums.
-__global__ __launch_bounds__(256) void mla_qabsorb_kernel(
-    int T, int H, float smscale, const float* __restrict__ q, const uint8_t* __restrict__ w_kvb,
-    const float* __restrict__ s_kvb, const double* __restrict__ inv_freq,
-    const int32_t* __restrict__ cached_len, int n_new, int max_len,
-    float* __restrict__ qcat) {
-  const int h = blockIdx.x, t0 = blockIdx.y * QA_TB, tid = threadIdx.x;
-  const int qld = H * (DN + DR);
-  __shared__ __attribute__((aligned(16))) uint8_t wk[DN * DL];   // 64 KiB of codes
-  __shared__ float qn[QA_TB][DN];
-  const uint8_t* wsrc = w_kvb + (size_t)h * (DN + DV) * DL;
-  for (int i = tid; i < DN * DL / 16; i += 256)
-    reinterpret_cast<uint4*>(wk)[i] = reinterpret_cast<const uint4*>(wsrc)[i];
-  for (int i = tid; i < QA_TB * DN; i += 256) {
-    const int tt = i / DN, d = i % DN;
-    qn[tt][d] = (t0 + tt < T) ? q[(size_t)(t0 + tt) * qld + h * (DN + DR) + d] : 0.f;
-  }
-  __syncthreads();
-  // thread tid: latent features r = 2 tid, 2 tid + 1 (scale block r / 128)
-  const int r = 2 * tid;
-  const float sk = s_kvb[(size_t)(2 * h) * (DL / QBLK) + r / QBLK];
-  float acc[QA_TB][2];
-#pragma unroll
-  for (int tt = 0; tt < QA_TB; ++tt) acc[tt][0] = acc[tt][1] = 0.f;
-  for (int d = 0; d < DN; ++d) {
-    const uint32_t c2 = *reinterpret_cast<const uint16_t*>(&wk[d * DL + r]);
-    const v2f w2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)c2, false);
-    const float w0 = w2[0] * sk, w1 = w2[1] * sk;
-#pragma unroll
-    for (int tt = 0; tt < QA_TB; ++tt) {
-      acc[tt][0] = fmaf(qn[tt][d], w0, acc[tt][0]);
-      acc[tt][1] = fmaf(qn[tt][d], w1, acc[tt][1]);
-    }
-  }
-  for (int tt = 0; tt < QA_TB && t0 + tt < T; ++tt) {
-    float* dst = qcat + ((size_t)(t0 + tt) * H + h) * DQ;
-    *reinterpret_cast<float2*>(dst + r) = make_float2(acc[tt][0] * smscale, acc[tt][1] * smscale);
-  }
-  // rotary part: thread (token tt, pair i)
-  for (int i = tid; i < QA_TB * (DR / 2); i += 256) {
-    const int tt = i / (DR / 2), pr = i % (DR / 2), t = t0 + tt;
-    if (t >= T) continue;
-    int seq;
-    const int pos = token_pos(cached_len, t, n_new, max_len, &seq);
-    const float* qp = q + (size_t)t * qld + h * (DN + DR) + DN;
-    float ra, rb;
-    rope_pair(qp[2 * pr], qp[2 * pr + 1], pos, inv_freq[pr], &ra, &rb);
-    float* dst = qcat + ((size_t)t * H + h) * DQ + DL;
-    dst[2 * pr] = ra * smscale;
-    dst[2 * pr + 1] = rb * smscale;
-  }
-}
-
 // ------------------------------------------------------- latent attention
 // Eight waves, each a column block of 8 (token, head) pairs.  mode 0 (one new
 // token per sequence): the waves are one token's groups of 8 heads, so a
@@ -633,95 +576,230 @@ __global__ __launch_bounds__(512, 1) void mla_attn_kernel(const AttnArgs g) {
   }
 }
 
-// ------------------------------------------- merge, value up-projection
-constexpr int VU_TB = 16;   // tokens per workgroup
+// ------------------------------------ query absorption, value up-projection
+// Both are dense bf16 MFMA products per head.  The weight codes are exact in
+// bf16 (pre-converted by mla_pack_ukv_kernel); an fp32 activation a is split
+// into its bf16 high part and the bf16 rounding of a - high, and both halves
+// go through the MFMA into one fp32 accumulator (the product of the two is
+// within about 2^-17 of the fp32 one, sums in fp32).
 
-// For head h and 16 tokens: merge the position splits (m, l, O) into
+// e4m3 codes of the key-value up-projection (per head: 128 key rows, 128
+// value rows, 512 latents) -> bf16 copies: ukt[h][r][d] = W_uk[d][r] (the
+// key rows transposed, so a latent's 128 weights are contiguous) and
+// uv[h][d][r] = W_uv[d][r].
+__global__ __launch_bounds__(256) void mla_pack_ukv_kernel(int H, const uint8_t* __restrict__ w_kvb,
+                                                           uint16_t* __restrict__ ukt,
+                                                           uint16_t* __restrict__ uv) {
+  const size_t n = (size_t)H * DN * DL;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < 2 * n;
+       i += (size_t)gridDim.x * 256) {
+    const bool key = i < n;
+    const size_t j = key ? i : i - n;
+    const int h = (int)(j / (DN * DL)), rem = (int)(j % (DN * DL));
+    if (key) {
+      const int r = rem / DN, d = rem % DN;   // output [h][r][d]
+      const float v = e4m3_val(w_kvb[((size_t)h * (DN + DV) + d) * DL + r]);
+      ukt[j] = (uint16_t)(__float_as_uint(v) >> 16);
+    } else {
+      const int d = rem / DL, r = rem % DL;   // output [h][d][r]
+      const float v = e4m3_val(w_kvb[((size_t)h * (DN + DV) + DN + d) * DL + r]);
+      uv[j] = (uint16_t)(__float_as_uint(v) >> 16);
+    }
+  }
+}
+
+// eight fp32 values -> their bf16 high parts (hi) and remainder roundings (lo)
+__device__ __forceinline__ void split8(const float4 a, const float4 b, v8bf* hi, v8bf* lo) {
+  const uint4 h = make_uint4(pack_bf16(a.x, a.y), pack_bf16(a.z, a.w), pack_bf16(b.x, b.y),
+                             pack_bf16(b.z, b.w));
+  *hi = __builtin_bit_cast(v8bf, h);
+  *lo = __builtin_bit_cast(v8bf, make_uint4(bf16_half2(a.x, a.y, 1.f), bf16_half2(a.z, a.w, 1.f),
+                                            bf16_half2(b.x, b.y, 1.f), bf16_half2(b.z, b.w, 1.f)));
+}
+
+constexpr int QA_TB = 32;   // tokens per workgroup
+
+// qcat[t, h] = scale * [W_uk^T q_nope (512), rope(q_pe) (64)] in fp32, per
+// latent block b: s_b * sum_d code[d][r] q[d] (W_uk of head h: key-value
+// up-projection rows h*(DN+DV) .. + DN - 1, one 128-row scale block).
+// Workgroup = (head, 32 tokens); wave w: latents 128 w .. + 127 (block w).
+__global__ __launch_bounds__(256) void mla_qabsorb_kernel(
+    int T, int H, float smscale, const float* __restrict__ q, const uint16_t* __restrict__ ukt,
+    const float* __restrict__ s_kvb, const double* __restrict__ inv_freq,
+    const int32_t* __restrict__ cached_len, int n_new, int max_len,
+    float* __restrict__ qcat) {
+  const int h = blockIdx.x, t0 = blockIdx.y * QA_TB, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, q4 = lane >> 4, l16 = lane & 15;
+  const int qld = H * (DN + DR);
+  // A: q_nope of tokens t0 + 16 mt + l16 (the last token repeated past T),
+  // features 32 ks + 8 q4 .. + 7
+  v8bf ahi[2][DN / 32], alo[2][DN / 32];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    const int t = min(t0 + 16 * mt + l16, T - 1);
+    const float* qp = q + (size_t)t * qld + h * (DN + DR) + 8 * q4;
+#pragma unroll
+    for (int ks = 0; ks < DN / 32; ++ks)
+      split8(*reinterpret_cast<const float4*>(qp + 32 * ks),
+             *reinterpret_cast<const float4*>(qp + 32 * ks + 4), &ahi[mt][ks], &alo[mt][ks]);
+  }
+  v4f acc[2][8] = {};
+  const uint16_t* bp = ukt + ((size_t)h * DL + 128 * wave + l16) * DN + 8 * q4;
+#pragma unroll
+  for (int ks = 0; ks < DN / 32; ++ks) {
+    v8bf b[8];
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct)
+      b[ct] = __builtin_bit_cast(v8bf,
+                                 *reinterpret_cast<const uint4*>(bp + (size_t)16 * ct * DN + 32 * ks));
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        acc[mt][ct] = mfma_bf16(ahi[mt][ks], b[ct], acc[mt][ct]);
+        acc[mt][ct] = mfma_bf16(alo[mt][ks], b[ct], acc[mt][ct]);
+      }
+  }
+  // lane: latent 128 w + 16 ct + l16, tokens 16 mt + 4 q4 + i
+  const float sk = s_kvb[(size_t)(2 * h) * (DL / QBLK) + wave];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = t0 + 16 * mt + 4 * q4 + i;
+      if (t >= T) continue;
+      float* dst = qcat + ((size_t)t * H + h) * DQ + 128 * wave + l16;
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) dst[16 * ct] = acc[mt][ct][i] * sk * smscale;
+    }
+  // rotary part: thread (token tt, pair i)
+  for (int i = tid; i < QA_TB * (DR / 2); i += 256) {
+    const int tt = i / (DR / 2), pr = i % (DR / 2), t = t0 + tt;
+    if (t >= T) continue;
+    int seq;
+    const int pos = token_pos(cached_len, t, n_new, max_len, &seq);
+    const float* qp = q + (size_t)t * qld + h * (DN + DR) + DN;
+    float ra, rb;
+    rope_pair(qp[2 * pr], qp[2 * pr + 1], pos, inv_freq[pr], &ra, &rb);
+    float* dst = qcat + ((size_t)t * H + h) * DQ + DL;
+    dst[2 * pr] = ra * smscale;
+    dst[2 * pr + 1] = rb * smscale;
+  }
+}
+
+constexpr int VU_TB = 32;             // tokens per workgroup
+constexpr int VA_LD = DL + 8;         // bf16 stride of an activation row in LDS
+
+// For head h and 32 tokens: merge the position splits (m, l, O) into
 // o_lat = sum_j p_j c_j / sum_j p_j, apply W_uv (rows h*(DN+DV)+DN .. + DV - 1,
-// one 128-row scale block) in fp32, write the 128 outputs as one 1x128 block
-// of the output projection's input (codes + scale) and, if attn != null, as
-// fp32.
+// one 128-row scale block) as sum_r code[d][r] (s_(r/128) o_lat[r]), write the
+// 128 outputs as one 1x128 block of the output projection's input (codes +
+// scale) and, if attn != null, as fp32.  Wave w: outputs 32 w .. + 31.
 __global__ __launch_bounds__(256) void mla_vup_kernel(
     int T, int H, int nsplit, const float* __restrict__ part_o, const float* __restrict__ part_ml,
-    const uint8_t* __restrict__ w_kvb, const float* __restrict__ s_kvb,
+    const uint16_t* __restrict__ uv, const float* __restrict__ s_kvb,
     uint8_t* __restrict__ o_q, float* __restrict__ o_s, float* __restrict__ attn) {
   const int h = blockIdx.x, t0 = blockIdx.y * VU_TB, tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  __shared__ __attribute__((aligned(16))) uint8_t wv[DV * DL];      // 64 KiB of codes
-  __shared__ __attribute__((aligned(16))) float ol[VU_TB][DL];      // 32 KiB
-  __shared__ float half_sum[VU_TB][DV];
-  const uint8_t* wsrc = w_kvb + ((size_t)h * (DN + DV) + DN) * DL;
-  for (int i = tid; i < DV * DL / 16; i += 256)
-    reinterpret_cast<uint4*>(wv)[i] = reinterpret_cast<const uint4*>(wsrc)[i];
-  // merge: thread handles latent features tid and tid + 256 of every token
-  for (int tt = 0; tt < VU_TB; ++tt) {
-    const int t = t0 + tt;
-    if (t >= T) {
-      ol[tt][tid] = ol[tt][tid + 256] = 0.f;
-      continue;
-    }
-    float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s)
-      M = fmaxf(M, part_ml[(((size_t)s * T + t) * H + h) * 2]);
-    float L = 0.f, a0 = 0.f, a1 = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-      const size_t pi = ((size_t)s * T + t) * H + h;
-      const float m = part_ml[pi * 2];
-      if (m == -INFINITY) continue;
-      const float wgt = __expf(m - M);
-      L += part_ml[pi * 2 + 1] * wgt;
-      a0 += part_o[pi * DL + tid] * wgt;
-      a1 += part_o[pi * DL + tid + 256] * wgt;
-    }
-    ol[tt][tid] = a0 / L;
-    ol[tt][tid + 256] = a1 / L;
-  }
-  __syncthreads();
-  // o[t, d] = sum_r W_uv[d, r] * s(r / 128) * o_lat[t, r]: thread (d, half of r)
-  const int d = tid & (DV - 1), half = tid >> 7;
+  const int lane = tid & 63, wave = tid >> 6, q4 = lane >> 4, l16 = lane & 15;
+  __shared__ __attribute__((aligned(16))) uint16_t a_hi[VU_TB * VA_LD];
+  __shared__ __attribute__((aligned(16))) uint16_t a_lo[VU_TB * VA_LD];
+  __shared__ float bmax[4][VU_TB];
   const float* sv = s_kvb + (size_t)(2 * h + 1) * (DL / QBLK);
-  float acc[VU_TB];
+  // merge: thread = (token tt, 16 consecutive latents)
+  for (int it = tid; it < VU_TB * (DL / 16); it += 256) {
+    const int tt = it / (DL / 16), r0 = 16 * (it % (DL / 16)), t = t0 + tt;
+    float a[16];
 #pragma unroll
-  for (int tt = 0; tt < VU_TB; ++tt) acc[tt] = 0.f;
-  for (int r = 256 * half; r < 256 * half + 256; r += 4) {
-    const uint32_t c4 = *reinterpret_cast<const uint32_t*>(&wv[d * DL + r]);
-    const v2f wa = __builtin_amdgcn_cvt_pk_f32_fp8((int)c4, false);
-    const v2f wb = __builtin_amdgcn_cvt_pk_f32_fp8((int)c4, true);
-    const float sc = sv[r / QBLK];
-    const float w0 = wa[0] * sc, w1 = wa[1] * sc, w2 = wb[0] * sc, w3 = wb[1] * sc;
-#pragma unroll
-    for (int tt = 0; tt < VU_TB; ++tt) {
-      const float4 x = *reinterpret_cast<const float4*>(&ol[tt][r]);
-      acc[tt] = fmaf(w0, x.x, fmaf(w1, x.y, fmaf(w2, x.z, fmaf(w3, x.w, acc[tt]))));
-    }
-  }
-  if (half == 1)
-    for (int tt = 0; tt < VU_TB; ++tt) half_sum[tt][d] = acc[tt];
-  __syncthreads();
-  // waves 0 and 1 hold d = 0..127 of every token: block maxima, then codes
-  __shared__ float bmax[VU_TB][2];
-  if (half == 0)
-    for (int tt = 0; tt < VU_TB; ++tt) {
-      acc[tt] += half_sum[tt][d];
-      float amax = fabsf(acc[tt]);
-#pragma unroll
-      for (int m = 1; m < 64; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
-      if (lane == 0) bmax[tt][wave] = amax;
-    }
-  __syncthreads();
-  if (half == 1) return;
-  for (int tt = 0; tt < VU_TB; ++tt) {
-    const int t = t0 + tt;
-    const float v = acc[tt];
-    const float amax = fmaxf(bmax[tt][0], bmax[tt][1]);
+    for (int j = 0; j < 16; ++j) a[j] = 0.f;
     if (t < T) {
-      const float s = fp8_scale(amax);
-      const uint32_t q = cvt4_e4m3(clamp_fp8(v / s), 0.f, 0.f, 0.f);
-      o_q[(size_t)t * H * DV + h * DV + d] = (uint8_t)(q & 0xFFu);
-      if (d == 0) o_s[(size_t)t * H + h] = s;
-      if (attn) attn[(size_t)t * H * DV + h * DV + d] = v;
+      float M = -INFINITY;
+      for (int s = 0; s < nsplit; ++s)
+        M = fmaxf(M, part_ml[(((size_t)s * T + t) * H + h) * 2]);
+      float L = 0.f;
+      for (int s = 0; s < nsplit; ++s) {
+        const size_t pi = ((size_t)s * T + t) * H + h;
+        const float m = part_ml[pi * 2];
+        if (m == -INFINITY) continue;
+        const float wgt = __expf(m - M);
+        L += part_ml[pi * 2 + 1] * wgt;
+        const float4* po = reinterpret_cast<const float4*>(part_o + pi * DL + r0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float4 v = po[j];
+          a[4 * j] += v.x * wgt;
+          a[4 * j + 1] += v.y * wgt;
+          a[4 * j + 2] += v.z * wgt;
+          a[4 * j + 3] += v.w * wgt;
+        }
+      }
+      const float sc = sv[r0 / QBLK];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) a[j] = (a[j] / L) * sc;
+    }
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      v8bf hi, lo;
+      split8(make_float4(a[8 * half], a[8 * half + 1], a[8 * half + 2], a[8 * half + 3]),
+             make_float4(a[8 * half + 4], a[8 * half + 5], a[8 * half + 6], a[8 * half + 7]),
+             &hi, &lo);
+      *reinterpret_cast<v8bf*>(&a_hi[tt * VA_LD + r0 + 8 * half]) = hi;
+      *reinterpret_cast<v8bf*>(&a_lo[tt * VA_LD + r0 + 8 * half]) = lo;
     }
   }
+  __syncthreads();
+  // out[t, d]: A = activation halves (tokens 16 mt + l16, latents 32 ks + 8 q4
+  // ..), B = W_uv rows d = 32 w + 16 ct + l16
+  v4f acc[2][2] = {};
+  const uint16_t* bp = uv + ((size_t)h * DV + 32 * wave + l16) * DL + 8 * q4;
+#pragma unroll 4
+  for (int ks = 0; ks < DL / 32; ++ks) {
+    v8bf b[2];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+      b[ct] = __builtin_bit_cast(v8bf,
+                                 *reinterpret_cast<const uint4*>(bp + (size_t)16 * ct * DL + 32 * ks));
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const int ao = (16 * mt + l16) * VA_LD + 32 * ks + 8 * q4;
+      const v8bf ah = *reinterpret_cast<const v8bf*>(&a_hi[ao]);
+      const v8bf al = *reinterpret_cast<const v8bf*>(&a_lo[ao]);
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        acc[mt][ct] = mfma_bf16(ah, b[ct], acc[mt][ct]);
+        acc[mt][ct] = mfma_bf16(al, b[ct], acc[mt][ct]);
+      }
+    }
+  }
+  // lane: outputs d = 32 w + 16 ct + l16 of tokens 16 mt + 4 q4 + i; block
+  // maxima over the 128 outputs of a token (16 lanes x 2 tiles x 4 waves)
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float m = fmaxf(fabsf(acc[mt][0][i]), fabsf(acc[mt][1][i]));
+#pragma unroll
+      for (int x = 1; x < 16; x <<= 1) m = fmaxf(m, __shfl_xor(m, x));
+      if (l16 == 0) bmax[wave][16 * mt + 4 * q4 + i] = m;
+    }
+  __syncthreads();
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tt = 16 * mt + 4 * q4 + i, t = t0 + tt;
+      if (t >= T) continue;
+      const float amax = fmaxf(fmaxf(bmax[0][tt], bmax[1][tt]), fmaxf(bmax[2][tt], bmax[3][tt]));
+      const float s = fp8_scale(amax);
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        const int d = 32 * wave + 16 * ct + l16;
+        const float v = acc[mt][ct][i];
+        const uint32_t c = cvt4_e4m3(clamp_fp8(v / s), 0.f, 0.f, 0.f);
+        o_q[(size_t)t * H * DV + h * DV + d] = (uint8_t)(c & 0xFFu);
+        if (attn) attn[(size_t)t * H * DV + h * DV + d] = v;
+      }
+      if (wave == 0 && l16 == 0) o_s[(size_t)t * H + h] = s;
+    }
 }
 
 }  // namespace
@@ -768,12 +846,18 @@ hipError_t launch_mla_latent(int T, int q_lora, int qkv_ld, float eps, const flo
   return hipGetLastError();
 }
 
-hipError_t launch_mla_qabsorb(int T, int H, float smscale, const float* q, const uint8_t* w_kvb,
+hipError_t launch_mla_pack_ukv(int H, const uint8_t* w_kvb, uint16_t* ukt, uint16_t* uv,
+                              hipStream_t s) {
+  mla_pack_ukv_kernel<<<1024, 256, 0, s>>>(H, w_kvb, ukt, uv);
+  return hipGetLastError();
+}
+
+hipError_t launch_mla_qabsorb(int T, int H, float smscale, const float* q, const uint16_t* ukt,
                               const float* s_kvb, const double* inv_freq,
                               const int32_t* cached_len, int n_new, int max_len, float* qcat,
                               hipStream_t s) {
   dim3 grid(H, (T + QA_TB - 1) / QA_TB);
-  mla_qabsorb_kernel<<<grid, 256, 0, s>>>(T, H, smscale, q, w_kvb, s_kvb, inv_freq, cached_len,
+  mla_qabsorb_kernel<<<grid, 256, 0, s>>>(T, H, smscale, q, ukt, s_kvb, inv_freq, cached_len,
                                           n_new, max_len, qcat);
   return hipGetLastError();
 }
@@ -803,11 +887,10 @@ hipError_t launch_mla_attn(int T, int H, int n_seq, int n_new, int max_len, int 
 }
 
 hipError_t launch_mla_vup(int T, int H, int nsplit, const float* part_o, const float* part_ml,
-                          const uint8_t* w_kvb, const float* s_kvb, uint8_t* o_q, float* o_s,
+                          const uint16_t* uv, const float* s_kvb, uint8_t* o_q, float* o_s,
                           float* attn, hipStream_t s) {
   dim3 grid(H, (T + VU_TB - 1) / VU_TB);
-  mla_vup_kernel<<<grid, 256, 0, s>>>(T, H, nsplit, part_o, part_ml, w_kvb, s_kvb, o_q, o_s,
-                                      attn);
+  mla_vup_kernel<<<grid, 256, 0, s>>>(T, H, nsplit, part_o, part_ml, uv, s_kvb, o_q, o_s, attn);
   return hipGetLastError();
 }
 

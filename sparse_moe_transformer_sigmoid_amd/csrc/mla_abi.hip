@@ -107,9 +107,10 @@ std::vector<double> yarn_inv_freq(const mla_config* c) {
 }
 
 // ---- packed weights: three GEMM matrices in the grouped GEMM's down form,
-// the key-value up-projection as it is, the norm weights, the frequencies
+// the key-value up-projection as bf16 copies of its key rows (transposed) and
+// value rows with its block scales, the norm weights, the frequencies
 struct MPacked {
-  size_t qkv_codes, qkv_scales, qb_codes, qb_scales, o_codes, o_scales, kvb_codes, kvb_scales,
+  size_t qkv_codes, qkv_scales, qb_codes, qb_scales, o_codes, o_scales, kvb_scales, ukt, uv,
       g_qa, g_kva, freq, total;
 };
 
@@ -127,8 +128,9 @@ MPacked packed_layout(const MDims& D) {
   p.qb_scales = take((size_t)(D.n_qb / 128) * (D.ql / 128) * 4);
   p.o_codes = take((size_t)D.n_o * D.H * D.v);
   p.o_scales = take((size_t)(D.n_o / 128) * D.H * 4);
-  p.kvb_codes = take((size_t)D.H * (D.nope + D.v) * D.kv);
   p.kvb_scales = take((size_t)D.H * 2 * (D.kv / 128) * 4);
+  p.ukt = take((size_t)D.H * D.kv * D.nope * 2);
+  p.uv = take((size_t)D.H * D.v * D.kv * 2);
   p.g_qa = take((size_t)D.ql * 2);
   p.g_kva = take((size_t)D.kv * 2);
   p.freq = take((size_t)(D.rope / 2) * 8);
@@ -306,7 +308,8 @@ moe_status run_mla(const mla_config* cfg, int32_t S, int32_t n, int32_t L, const
   uint8_t* o_q = at<uint8_t>(ws, W.o_q);
   float* o_s = at<float>(ws, W.o_s);
   const double* freq = reinterpret_cast<const double*>(pk + P.freq);
-  const uint8_t* kvb = pk + P.kvb_codes;
+  const uint16_t* ukt = reinterpret_cast<const uint16_t*>(pk + P.ukt);
+  const uint16_t* uv = reinterpret_cast<const uint16_t*>(pk + P.uv);
   const float* kvbs = reinterpret_cast<const float*>(pk + P.kvb_scales);
 
   {
@@ -343,7 +346,7 @@ moe_status run_mla(const mla_config* cfg, int32_t S, int32_t n, int32_t L, const
   {
     k2::ProfileScope ps(MOE_STAGE_MLA_LATENT, s);
     // absorbed queries
-    M_HIP(k2::launch_mla_qabsorb(T, D.H, D.smscale, q, kvb, kvbs, freq, cached_len, n, L, qcat,
+    M_HIP(k2::launch_mla_qabsorb(T, D.H, D.smscale, q, ukt, kvbs, freq, cached_len, n, L, qcat,
                                  s));
   }
   {
@@ -355,7 +358,7 @@ moe_status run_mla(const mla_config* cfg, int32_t S, int32_t n, int32_t L, const
   }
   {
     k2::ProfileScope ps(MOE_STAGE_MLA_VUP, s);
-    M_HIP(k2::launch_mla_vup(T, D.H, W.ns_attn, part_o, part_ml, kvb, kvbs, o_q, o_s, attn, s));
+    M_HIP(k2::launch_mla_vup(T, D.H, W.ns_attn, part_o, part_ml, uv, kvbs, o_q, o_s, attn, s));
   }
   if (!out) return MOE_OK;
   k2::ProfileScope ps(MOE_STAGE_MLA_PROJ, s);
@@ -410,8 +413,8 @@ moe_status mla_pack_weights(const mla_config* cfg, const mla_weights* w, void* p
                              base + P.qb_codes, reinterpret_cast<float*>(base + P.qb_scales), s));
   M_HIP(k2::launch_pack_rows(D.n_o, D.H * D.v, u8(w->w_o), D.n_o, nullptr, 0, w->s_o, nullptr,
                              base + P.o_codes, reinterpret_cast<float*>(base + P.o_scales), s));
-  M_HIP(hipMemcpyAsync(base + P.kvb_codes, w->w_kvb, (size_t)D.H * (D.nope + D.v) * D.kv,
-                       hipMemcpyDeviceToDevice, s));
+  M_HIP(k2::launch_mla_pack_ukv(D.H, u8(w->w_kvb), reinterpret_cast<uint16_t*>(base + P.ukt),
+                                reinterpret_cast<uint16_t*>(base + P.uv), s));
   M_HIP(hipMemcpyAsync(base + P.kvb_scales, w->s_kvb, (size_t)D.H * 2 * (D.kv / 128) * 4,
                        hipMemcpyDeviceToDevice, s));
   M_HIP(hipMemcpyAsync(base + P.g_qa, w->g_qa, (size_t)D.ql * 2, hipMemcpyDeviceToDevice, s));

@@ -27,7 +27,11 @@ hipError_t launch_mla_latent(int T, int q_lora, int qkv_ld, float eps, const flo
                              const int32_t* cached_len, int n_new, int max_len, uint8_t* qa_q,
                              float* qa_s, uint8_t* c_codes, float* c_scales, uint16_t* c_rope,
                              hipStream_t s);
-hipError_t launch_mla_qabsorb(int T, int H, float smscale, const float* q, const uint8_t* w_kvb,
+// bf16 copies of the key-value up-projection's codes: ukt [H][512][128] (key
+// rows transposed), uv [H][128][512] (value rows)
+hipError_t launch_mla_pack_ukv(int H, const uint8_t* w_kvb, uint16_t* ukt, uint16_t* uv,
+                              hipStream_t s);
+hipError_t launch_mla_qabsorb(int T, int H, float smscale, const float* q, const uint16_t* ukt,
                               const float* s_kvb, const double* inv_freq,
                               const int32_t* cached_len, int n_new, int max_len, float* qcat,
                               hipStream_t s);
@@ -52,7 +56,7 @@ hipError_t launch_mla_attn(int T, int H, int n_seq, int n_new, int max_len, int 
                            const int32_t* cached_len, float* part_o, float* part_ml,
                            hipStream_t s);
 hipError_t launch_mla_vup(int T, int H, int nsplit, const float* part_o, const float* part_ml,
-                          const uint8_t* w_kvb, const float* s_kvb, uint8_t* o_q, float* o_s,
+                          const uint16_t* uv, const float* s_kvb, uint8_t* o_q, float* o_s,
                           float* attn, hipStream_t s);
 
 }  // namespace k2

@@ -186,11 +186,13 @@ def _mla_cfg(**kw):
 def test_mla_sizes_and_validation():
     lib = L.load()
     cfg = _mla_cfg()
-    # packed: the three GEMM matrices (the stacked down-projections padded to
-    # 2304 rows), the key-value up-projection, norms and frequencies
+    # packed: the three GEMM matrices as FP8 codes (the stacked
+    # down-projections padded to 2304 rows), the key-value up-projection as
+    # bf16 copies (2 bytes per weight), scales, norms and frequencies
     n = lib.mla_packed_weights_bytes(C.byref(cfg))
-    fp8 = 2304 * 7168 + 12288 * 1536 + 7168 * 8192 + 16384 * 512
-    assert fp8 < n < fp8 * 1.01
+    fp8 = 2304 * 7168 + 12288 * 1536 + 7168 * 8192
+    bf16 = 2 * 16384 * 512
+    assert fp8 + bf16 < n < (fp8 + bf16) * 1.01
     nb = C.c_size_t(0)
     assert lib.mla_workspace_bytes(C.byref(cfg), 64, 1, 4097, C.byref(nb)) == L.MOE_OK
     assert nb.value > 64 * 12288 * 4
