@@ -214,11 +214,14 @@ __global__ __launch_bounds__(256) void mla_latent_kernel(
 
 // --------------------------------------------------------- query absorption
 // ------------------------------------------------------- latent attention
-// Eight waves, each a column block of 8 (token, head) pairs.  mode 0 (one new
-// token per sequence): the waves are one token's groups of 8 heads, so a
-// workgroup covers min(heads, 64) heads and reads each cache position once for
-// all of them; mode 1: up to eight consecutive tokens of one sequence with one
-// group of 8 heads.  The cache positions [lo, hi) of the work item's split are
+// Eight waves, each scoring a column block of 8 (token, head) pairs.  mode 0
+// (one new token per sequence): the waves are one token's groups of 8 heads,
+// so a workgroup covers min(heads, 64) heads and reads each cache position
+// once for all of them; mode 1: up to eight consecutive tokens of one sequence
+// with one group of 8 heads.  Waves 2i and 2i + 1 form a pair whose 16
+// columns share the value sum: each wave accumulates the outputs of all 16
+// columns over one half of the latent (256 features), taking the partner's
+// probabilities through LDS, so it holds 64 accumulator registers, not 128.  The cache positions [lo, hi) of the work item's split are
 // visited in steps of 32.  The cache bytes of a step (latent codes, rotary
 // keys, scales) are copied straight from global memory into one of NS LDS
 // stages (global_load_lds, no staging registers), NS - 1 steps ahead of the
@@ -235,9 +238,11 @@ __global__ __launch_bounds__(256) void mla_latent_kernel(
 //   S_b^T = C_b Q^T              (codes, query halves; lane: 4 positions x 1 column)
 //   s = sum_b scale_b(pos) S_b + S_rope, the two columns of a head added
 //   online softmax per head
-//   O_b^T += C_b^T (p scale_b)^T  (p * scale as {hi, lo} columns; the lane's 8 K
-//                                  slots = positions 4q..4q+3 of the first 16 and
-//                                  of the second 16, where S^T left them)
+//   O_b^T [latent, pair column] += C_b^T (p scale_b)^T with the halves in K:
+//                                  the lane's 8 K slots are positions 4q..4q+3
+//                                  of a 16-position group (where S^T left them)
+//                                  as high halves, then the same positions as
+//                                  low halves, the cache fragment repeated
 // and finally writes its running max m, sum l and O^T (head x 512) unscaled.
 struct AttnArgs {
   const uint8_t* c_codes;
@@ -322,7 +327,8 @@ __global__ __launch_bounds__(512, 1) void mla_attn_kernel(const AttnArgs g) {
   __shared__ __attribute__((aligned(16))) float csc[NS][DL / QBLK][PT];
   __shared__ __attribute__((aligned(16))) uint16_t ct[CT_ELEMS];   // row-major bf16 latents
   __shared__ __attribute__((aligned(16))) uint16_t tr[TR_ELEMS];   // transposed bf16 latents
-  __shared__ int kv_sh[AW];
+  __shared__ float xbuf[AW][9][64];   // a wave's probabilities (8) and rescale factor per lane
+  __shared__ int kv_sh[AW], tok_sh[AW], head_sh[AW];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q4 = lane >> 4, l16 = lane & 15;
@@ -351,7 +357,11 @@ __global__ __launch_bounds__(512, 1) void mla_attn_kernel(const AttnArgs g) {
   }
   int seq;
   const int qpos = token_pos(g.cached_len, t, g.n_new, g.max_len, &seq);
-  if (lane == 0) kv_sh[wave] = active ? qpos + 1 : 0;
+  if (lane == 0) {
+    kv_sh[wave] = active ? qpos + 1 : 0;
+    tok_sh[wave] = t;
+    head_sh[wave] = h0;
+  }
   __syncthreads();
   // the workgroup's positions: its split's range, up to its last query position
   int wg_end = 0;
@@ -359,6 +369,8 @@ __global__ __launch_bounds__(512, 1) void mla_attn_kernel(const AttnArgs g) {
   for (int w = 0; w < AW; ++w) wg_end = max(wg_end, kv_sh[w]);
   const int lo = split * g.chunk, hi = min(wg_end, lo + g.chunk);
   const int my_end = active ? qpos + 1 : 0;
+  const int pm = wave & 1;   // member of the wave pair
+  const int pair_end = max(kv_sh[wave & ~1], kv_sh[wave | 1]);   // 0: both members idle
   const int h = h0 + (l16 & (HPW - 1));   // this lane's head
   const size_t cbase = (size_t)seq * g.max_len;
   const uint8_t* codes_seq = g.c_codes + cbase * DL;
@@ -426,8 +438,10 @@ __global__ __launch_bounds__(512, 1) void mla_attn_kernel(const AttnArgs g) {
   // the query of head h as B fragments, high or low halves by column (dims
   // 32 ks + 8 q4 .. + 7)
   v8bf qb[DQ / 32];
-  v4f o[DL / 16];
+  v4f o[DL / 32];   // pair column l mod 16, latents 256 pm + 16 nt + 4 q4 + i
   float mrun = -INFINITY, lrun = 0.f;
+#pragma unroll
+  for (int i = 0; i < DL / 32; ++i) o[i] = v4f{0.f, 0.f, 0.f, 0.f};
   if (active) {
     const float* qp = g.qcat + ((size_t)t * g.H + h) * DQ + 8 * q4;
 #pragma unroll
@@ -438,10 +452,10 @@ __global__ __launch_bounds__(512, 1) void mla_attn_kernel(const AttnArgs g) {
                                  bf16_half2(c.x, c.y, lo_f), bf16_half2(c.z, c.w, lo_f));
       qb[ks] = __builtin_bit_cast(v8bf, v);
     }
-#pragma unroll
-    for (int i = 0; i < DL / 16; ++i) o[i] = v4f{0.f, 0.f, 0.f, 0.f};
   }
-  auto step = [&](int st, int p0) {
+  // scores and online softmax of the wave's 8 heads; ps, alpha: the lane's
+  // probabilities and the rescale factor of its head
+  auto scores = [&](int st, int p0, float (&ps)[2][4], float& alpha) {
     // ---- scores: S^T[pos, column] for positions p0 + 16 pt + 4 q4 + i
     v4f s[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
@@ -499,8 +513,8 @@ __global__ __launch_bounds__(512, 1) void mla_attn_kernel(const AttnArgs g) {
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float mnew = fmaxf(mrun, mx);
-    const float alpha = __expf(mrun - mnew);
-    float ps[2][4], lsum = 0.f;
+    alpha = __expf(mrun - mnew);
+    float lsum = 0.f;
 #pragma unroll
     for (int pt = 0; pt < 2; ++pt)
 #pragma unroll
@@ -512,30 +526,43 @@ __global__ __launch_bounds__(512, 1) void mla_attn_kernel(const AttnArgs g) {
     lsum += __shfl_xor(lsum, 32);
     lrun = lrun * alpha + lsum;
     mrun = mnew;
-    // rescale the outputs only when some head's maximum moved (alpha = 1
-    // leaves them unchanged)
-    if (__any(alpha != 1.f)) {
+  };
+  // value sum of the pair's 16 columns over latents 256 pm .. + 255: column
+  // l mod 16 belongs to member (l mod 16) / 8, whose lane l holds its
+  // probabilities at the same positions
+  auto values = [&](int st) {
+    const bool own = (l16 >> 3) == pm;
+    float v[2][4];
 #pragma unroll
-      for (int nt = 0; nt < DL / 16; ++nt) o[nt] *= alpha;
+    for (int j = 0; j < 8; ++j) v[j >> 2][j & 3] = xbuf[own ? wave : wave ^ 1][j][lane];
+    const float a_col = xbuf[own ? wave : wave ^ 1][8][lane];
+    // rescale only when some column's maximum moved (alpha = 1 leaves them)
+    if (__any(a_col != 1.f)) {
+#pragma unroll
+      for (int nt = 0; nt < DL / 32; ++nt) o[nt] *= a_col;
     }
-    // ---- O^T[latent, column] = alpha O^T + C_b^T (p scale_b)^T, block by block
 #pragma unroll
-    for (int blk = 0; blk < DL / QBLK; ++blk) {
-      const float4 s0 = *reinterpret_cast<const float4*>(&csc[st][blk][4 * q4]);
-      const float4 s1 = *reinterpret_cast<const float4*>(&csc[st][blk][16 + 4 * q4]);
-      const uint4 pv = make_uint4(
-          bf16_half2(ps[0][0] * s0.x, ps[0][1] * s0.y, lo_f),
-          bf16_half2(ps[0][2] * s0.z, ps[0][3] * s0.w, lo_f),
-          bf16_half2(ps[1][0] * s1.x, ps[1][1] * s1.y, lo_f),
-          bf16_half2(ps[1][2] * s1.z, ps[1][3] * s1.w, lo_f));
-      const v8bf pb = __builtin_bit_cast(v8bf, pv);
+    for (int bb = 0; bb < 2; ++bb) {
+      const int blk = 2 * pm + bb;
+      v8bf pb[2];
 #pragma unroll
-      for (int nt = blk * 8; nt < blk * 8 + 8; ++nt) {
-        const uint16_t* tp = &tr[(16 * nt + l16) * TR_LD + 4 * q4];
-        const uint2 a0 = *reinterpret_cast<const uint2*>(tp);
-        const uint2 a1 = *reinterpret_cast<const uint2*>(tp + 16);
-        const v8bf av = __builtin_bit_cast(v8bf, make_uint4(a0.x, a0.y, a1.x, a1.y));
-        o[nt] = mfma_bf16(av, pb, o[nt]);
+      for (int pt = 0; pt < 2; ++pt) {
+        const float4 sc = *reinterpret_cast<const float4*>(&csc[st][blk][16 * pt + 4 * q4]);
+        const float x0 = v[pt][0] * sc.x, x1 = v[pt][1] * sc.y;
+        const float x2 = v[pt][2] * sc.z, x3 = v[pt][3] * sc.w;
+        pb[pt] = __builtin_bit_cast(v8bf, make_uint4(pack_bf16(x0, x1), pack_bf16(x2, x3),
+                                                     bf16_half2(x0, x1, 1.f),
+                                                     bf16_half2(x2, x3, 1.f)));
+      }
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) {
+#pragma unroll
+        for (int pt = 0; pt < 2; ++pt) {
+          const uint2 a = *reinterpret_cast<const uint2*>(
+              &tr[(16 * (8 * blk + nt) + l16) * TR_LD + 16 * pt + 4 * q4]);
+          o[8 * bb + nt] = mfma_bf16(__builtin_bit_cast(v8bf, make_uint4(a.x, a.y, a.x, a.y)),
+                                     pb[pt], o[8 * bb + nt]);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -553,24 +580,31 @@ __global__ __launch_bounds__(512, 1) void mla_attn_kernel(const AttnArgs g) {
     if (k + NS - 1 < nsteps) issue((k + NS - 1) % NS, p0 + (NS - 1) * PT);
     convert(st);
     __syncthreads();
-    if (active && p0 < my_end) step(st, p0);
+    // scores (waves whose token sees this step), exchange, values (pairs
+    // with a member that sees it; an idle member contributes p = 0)
+    float ps[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    float alpha = 1.f;
+    if (active && p0 < my_end) scores(st, p0, ps, alpha);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) xbuf[wave][j][lane] = ps[j >> 2][j & 3];
+    xbuf[wave][8][lane] = alpha;
+    __syncthreads();
+    if (p0 < pair_end) values(st);
   }
-  if (!active) return;
-  // a head's two columns (contributions of the high and low p halves) add
-  // to its output; the high-column lanes write O^T, latent features
-  // 16 nt + 4 q4 + i
+  if (pair_end == 0) return;
+  // lane l writes O^T of pair column l mod 16 (when its member is active),
+  // latent features 256 pm + 16 nt + 4 q4 + i
+  const int cw = (wave & ~1) | (l16 >> 3);
+  if (kv_sh[cw] > 0) {
+    const size_t cidx = ((size_t)split * g.T + tok_sh[cw]) * g.H + head_sh[cw] + (l16 & 7);
+    float* po = g.part_o + cidx * DL + 256 * pm;
 #pragma unroll
-  for (int nt = 0; nt < DL / 16; ++nt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) o[nt][i] += xor8(o[nt][i]);
-  if (lo_col) return;
-  const size_t pidx = ((size_t)split * g.T + t) * g.H + h;
-  float* po = g.part_o + pidx * DL;
-#pragma unroll
-  for (int nt = 0; nt < DL / 16; ++nt)
-    *reinterpret_cast<float4*>(po + 16 * nt + 4 * q4) =
-        make_float4(o[nt][0], o[nt][1], o[nt][2], o[nt][3]);
-  if (q4 == 0) {
+    for (int nt = 0; nt < DL / 32; ++nt)
+      *reinterpret_cast<float4*>(po + 16 * nt + 4 * q4) =
+          make_float4(o[nt][0], o[nt][1], o[nt][2], o[nt][3]);
+  }
+  if (active && !lo_col && q4 == 0) {
+    const size_t pidx = ((size_t)split * g.T + t) * g.H + h;
     g.part_ml[pidx * 2] = mrun;
     g.part_ml[pidx * 2 + 1] = lrun;
   }
