@@ -238,11 +238,11 @@ __global__ __launch_bounds__(256) void mla_latent_kernel(
 //   S_b^T = C_b Q^T              (codes, query halves; lane: 4 positions x 1 column)
 //   s = sum_b scale_b(pos) S_b + S_rope, the two columns of a head added
 //   online softmax per head
-//   O_b^T [latent, pair column] += C_b^T (p scale_b)^T with the halves in K:
-//                                  the lane's 8 K slots are positions 4q..4q+3
-//                                  of a 16-position group (where S^T left them)
-//                                  as high halves, then the same positions as
-//                                  low halves, the cache fragment repeated
+//   O_b^T [latent, pair column] += C_b^T (p scale_b)^T as two MFMAs on one
+//                                  cache fragment, the high and the low halves
+//                                  of p scale_b; the lane's 8 K slots are
+//                                  positions 4q..4q+3 of the first 16 and of
+//                                  the second 16 (where S^T left them)
 // and finally writes its running max m, sum l and O^T (head x 512) unscaled.
 struct AttnArgs {
   const uint8_t* c_codes;
@@ -522,8 +522,8 @@ __global__ __launch_bounds__(512, 1) void mla_attn_kernel(const AttnArgs g) {
         ps[pt][i] = __expf(s[pt][i] - mnew);
         lsum += ps[pt][i];
       }
-    lsum += __shfl_xor(lsum, 16);
-    lsum += __shfl_xor(lsum, 32);
+    // each lane keeps the sum over its own positions; the four lanes of a
+    // column are added once, at the end
     lrun = lrun * alpha + lsum;
     mrun = mnew;
   };
@@ -544,25 +544,29 @@ __global__ __launch_bounds__(512, 1) void mla_attn_kernel(const AttnArgs g) {
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb) {
       const int blk = 2 * pm + bb;
-      v8bf pb[2];
+      // B: the 8 positions 4 q4 .. + 3 of both 16-position groups, high
+      // halves (pbh) and low halves (pbl); one A fragment feeds both
+      uint32_t hv[4], lv[4];
 #pragma unroll
       for (int pt = 0; pt < 2; ++pt) {
         const float4 sc = *reinterpret_cast<const float4*>(&csc[st][blk][16 * pt + 4 * q4]);
         const float x0 = v[pt][0] * sc.x, x1 = v[pt][1] * sc.y;
         const float x2 = v[pt][2] * sc.z, x3 = v[pt][3] * sc.w;
-        pb[pt] = __builtin_bit_cast(v8bf, make_uint4(pack_bf16(x0, x1), pack_bf16(x2, x3),
-                                                     bf16_half2(x0, x1, 1.f),
-                                                     bf16_half2(x2, x3, 1.f)));
+        hv[2 * pt] = pack_bf16(x0, x1);
+        hv[2 * pt + 1] = pack_bf16(x2, x3);
+        lv[2 * pt] = bf16_half2(x0, x1, 1.f);
+        lv[2 * pt + 1] = bf16_half2(x2, x3, 1.f);
       }
+      const v8bf pbh = __builtin_bit_cast(v8bf, make_uint4(hv[0], hv[1], hv[2], hv[3]));
+      const v8bf pbl = __builtin_bit_cast(v8bf, make_uint4(lv[0], lv[1], lv[2], lv[3]));
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) {
-#pragma unroll
-        for (int pt = 0; pt < 2; ++pt) {
-          const uint2 a = *reinterpret_cast<const uint2*>(
-              &tr[(16 * (8 * blk + nt) + l16) * TR_LD + 16 * pt + 4 * q4]);
-          o[8 * bb + nt] = mfma_bf16(__builtin_bit_cast(v8bf, make_uint4(a.x, a.y, a.x, a.y)),
-                                     pb[pt], o[8 * bb + nt]);
-        }
+        const uint16_t* tp = &tr[(16 * (8 * blk + nt) + l16) * TR_LD + 4 * q4];
+        const uint2 a0 = *reinterpret_cast<const uint2*>(tp);
+        const uint2 a1 = *reinterpret_cast<const uint2*>(tp + 16);
+        const v8bf av = __builtin_bit_cast(v8bf, make_uint4(a0.x, a0.y, a1.x, a1.y));
+        o[8 * bb + nt] = mfma_bf16(av, pbh, o[8 * bb + nt]);
+        o[8 * bb + nt] = mfma_bf16(av, pbl, o[8 * bb + nt]);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -603,10 +607,12 @@ __global__ __launch_bounds__(512, 1) void mla_attn_kernel(const AttnArgs g) {
       *reinterpret_cast<float4*>(po + 16 * nt + 4 * q4) =
           make_float4(o[nt][0], o[nt][1], o[nt][2], o[nt][3]);
   }
+  float ltot = lrun + __shfl_xor(lrun, 16);
+  ltot += __shfl_xor(ltot, 32);
   if (active && !lo_col && q4 == 0) {
     const size_t pidx = ((size_t)split * g.T + t) * g.H + h;
     g.part_ml[pidx * 2] = mrun;
-    g.part_ml[pidx * 2 + 1] = lrun;
+    g.part_ml[pidx * 2 + 1] = ltot;
   }
 }
 
