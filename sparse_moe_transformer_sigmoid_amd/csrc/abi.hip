@@ -1187,17 +1187,19 @@ moe_status moe_train_backward(const moe_config* cfg, int64_t T, const void* dout
   g.G = D.G;
   g.pad_off = pad_off;
   g.out_stride = 3 * I * d;
-  g.A = dywT;
-  g.lda = (int)ldt;
+  g.A = dywT;   // K-blocked transposed operands: 32 C elements per K block
+  g.lda = 32 * D.d;
   g.B = aT;
-  g.ldb = (int)ldt;
+  g.ldb = 32 * D.I;
   g.MT = D.d / 256;
   g.NT = D.I / 128;
   g.out = d_w + 2 * I * d;
   g.ldo = D.I;
   K2_HIP(k2::launch_train_gemm(k2::TM_WGRAD, g, (D.G * g.MT * g.NT + 7) / 8 * 8, s));
   g.A = dguT;
+  g.lda = 32 * 2 * D.I;
   g.B = hT;
+  g.ldb = 32 * D.d;
   g.MT = 2 * D.I / 256;
   g.NT = D.d / 128;
   g.out = d_w;

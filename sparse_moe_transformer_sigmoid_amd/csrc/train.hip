@@ -12,13 +12,14 @@
 // (v_mfma_f32_16x16x32_bf16); the backward recomputes a = silu(g) u from the
 // stored g, u.
 //
-// One GEMM template covers the five products of the step:
+// One GEMM template covers the four row-tiled products of the step:
 //   forward gate/up   C[2I rows of W_gate, W_up][rows]  = W h^T      (+ SwiGLU, FP8 copies)
 //   forward down      C[d][rows]                        = W_down a^T (+ routing weight)
 //   dgrad down        C[I][rows]                        = W_down^T dy^T (+ dw, dg, du)
 //   dgrad gate/up     C[d][rows]                        = [W_gate; W_up]^T [dg; du]^T
+// and train_wgrad_kernel the weight gradients
 //   wgrad             C[out][in]  = sum over a group's rows of X^T Y
-// A workgroup computes a 256 x 128 tile (4 waves of 64 M rows, 8 16-row N
+// (both operands K-blocked transposed copies).  A workgroup computes a 256 x 128 tile (4 waves of 64 M rows, 8 16-row N
 // tiles); each wave streams its 64 A rows straight into registers one K
 // step ahead, the 128 B rows are staged through LDS (double-buffered), and
 // lane l of a 16x16 result holds M rows 4(l/16)..+3 of N column l%16.
@@ -127,20 +128,13 @@ __global__ __launch_bounds__(256, 2) void train_gemm_kernel(const TrainGemmArgs 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, q4 = lane >> 4;
 
-  const TileWork wi = MODE == TM_WGRAD ? decode_wgrad(g) : decode_rows(g);
+  static_assert(MODE != TM_WGRAD, "weight gradients use train_wgrad_kernel");
+  const TileWork wi = decode_rows(g);
   if (!wi.valid) return;
   const int grp = wi.grp;
 
   // ---- operand row pointers
-  int nks;           // K steps
-  size_t kbase = 0;  // wgrad: first padded column of the group
-  if constexpr (MODE == TM_WGRAD) {
-    const int k0 = g.pad_off[grp], k1 = g.pad_off[grp + 1];
-    kbase = (size_t)k0;
-    nks = (k1 - k0) / TK;
-  } else {
-    nks = g.K / TK;
-  }
+  const int nks = g.K / TK;   // K steps
   const uint16_t* arow[4];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
@@ -149,14 +143,11 @@ __global__ __launch_bounds__(256, 2) void train_gemm_kernel(const TrainGemmArgs 
     if constexpr (MODE == TM_FWD_GU) {
       base = (mt < 2 ? g.A : g.A2) + (size_t)grp * g.a_stride;
       row = (size_t)(128 * wi.nc + 32 * wave + 16 * (mt & 1) + l16);
-    } else if constexpr (MODE == TM_WGRAD) {
-      base = g.A;
-      row = (size_t)(256 * wi.mi + TMW * wave + 16 * mt + l16);
     } else {
       base = g.A + (size_t)grp * g.a_stride;
       row = (size_t)(256 * wi.nc + TMW * wave + 16 * mt + l16);
     }
-    arow[mt] = base + row * (size_t)g.lda + kbase + 8 * q4;
+    arow[mt] = base + row * (size_t)g.lda + 8 * q4;
   }
   // B rows staged by this thread: tile rows tid/4 and tid/4 + 64, 8 K each
   const uint16_t* brow[2];
@@ -164,17 +155,13 @@ __global__ __launch_bounds__(256, 2) void train_gemm_kernel(const TrainGemmArgs 
   for (int c = 0; c < 2; ++c) {
     const int tr = (tid >> 2) + 64 * c;
     size_t src;
-    if constexpr (MODE == TM_WGRAD) {
-      src = (size_t)(TN * wi.ni + tr) * g.ldb + kbase;
+    const int r = wi.row0 + min(tr, wi.mcount - 1);   // rows past the tile repeat the last
+    if constexpr (MODE == TM_FWD_GU || MODE == TM_BWD_DOWN) {
+      int tok = r >= g.P ? r - g.P : g.row_pair[r] / g.k;
+      tok = min(max(tok, 0), g.T - 1);
+      src = (size_t)tok * g.ldb;
     } else {
-      const int r = wi.row0 + min(tr, wi.mcount - 1);   // rows past the tile repeat the last
-      if constexpr (MODE == TM_FWD_GU || MODE == TM_BWD_DOWN) {
-        int tok = r >= g.P ? r - g.P : g.row_pair[r] / g.k;
-        tok = min(max(tok, 0), g.T - 1);
-        src = (size_t)tok * g.ldb;
-      } else {
-        src = (size_t)r * g.ldb;
-      }
+      src = (size_t)r * g.ldb;
     }
     brow[c] = g.B + src + 8 * (tid & 3);
   }
@@ -236,34 +223,6 @@ __global__ __launch_bounds__(256, 2) void train_gemm_kernel(const TrainGemmArgs 
   }
 
   // ---------------------------------------------------------- epilogues
-  if constexpr (MODE == TM_WGRAD) {
-    // C[m][n] -> out[grp][m][n] (fp32, nn.Linear layout of the gradient).
-    // Each wave turns 16 of its rows at a time around in LDS so that 32
-    // lanes store one row's 128 columns (512 contiguous bytes), non-temporal
-    // (the gradient is not read again here).
-    constexpr int OT_LD = TN + 4;
-    __shared__ __attribute__((aligned(16))) float ot[4][16 * OT_LD];
-    float* out = g.out + (size_t)grp * g.out_stride + (size_t)TN * wi.ni;
-    float* tw = ot[wave];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-      for (int nt = 0; nt < 8; ++nt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) tw[(4 * q4 + r) * OT_LD + 16 * nt + l16] = acc[mt][nt][r];
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int row = 2 * i + (lane >> 5), col = 4 * (lane & 31);
-        const v4f v = *reinterpret_cast<const v4f*>(&tw[row * OT_LD + col]);
-        const size_t m = (size_t)(256 * wi.mi + TMW * wave + 16 * mt + row);
-        __builtin_nontemporal_store(v, reinterpret_cast<v4f*>(out + m * g.ldo + col));
-      }
-      __builtin_amdgcn_wave_barrier();
-    }
-    return;
-  }
   const int ntt = (wi.mcount + 15) >> 4;
   if constexpr (MODE == TM_FWD_GU) {
     // lane: g (acc[h]) and u (acc[h + 2]) of hidden 128 nc + 32 wave + 16 h + 4 q4 + r,
@@ -450,8 +409,11 @@ __global__ __launch_bounds__(1024) void pad_offsets_kernel(int E, int G, int T, 
   if (t == 1023) pad_off[G] = sums[1023];
 }
 
-// Transposed, group-padded copy of per-row data, XT [C][ldt]:
-// column pad_off[g] + j holds row offsets-of-g + j.  Modes:
+// Transposed, group-padded copy of per-row data, K-blocked: padded column q
+// of feature c at ((q / 32) * C + c) * 32 + q % 32, so the 32 columns of a
+// K step are 64 contiguous bytes per feature and consecutive features follow
+// each other (a 16-feature load of one step reads 1 KB contiguous, whole
+// cache lines).  Column pad_off[g] + j holds row offsets-of-g + j.  Modes:
 //   0: bf16 source rows src[r][C]
 //   1: bf16 w_r * dy[token(r)] (routed rows times their routing weight)
 //   2: h~ = bf16(e4m3 code * scale) of token(r) from the stored FP8 h
@@ -526,7 +488,8 @@ __global__ __launch_bounds__(256) void transpose_pad_kernel(const TransposeArgs 
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       w[i] = (uint32_t)tile[qq + 2 * i][cr] | ((uint32_t)tile[qq + 2 * i + 1][cr] << 16);
-    uint4* dst = reinterpret_cast<uint4*>(a.dst + (size_t)(c0 + cr) * a.ldt + q0 + qq);
+    const int q = q0 + qq;   // 16 columns inside one 32-column block
+    uint4* dst = reinterpret_cast<uint4*>(a.dst + ((size_t)(q >> 5) * a.C + c0 + cr) * 32 + (q & 31));
     dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
     dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
   }
@@ -702,6 +665,135 @@ __global__ __launch_bounds__(256) void router_wgrad_kernel(int E, int d, int k, 
   *reinterpret_cast<float4*>(dwr + (size_t)e * d + c) = make_float4(acc[0], acc[1], acc[2], acc[3]);
 }
 
+// Weight gradients C[out][in] = sum over a group's rows of X^T Y, in
+// 256 x 128 tiles (4 waves of 64 M rows, 8 16-row N tiles).  A tile's K is a
+// group's rows, a few steps of 32 at the routed experts' sizes, so a one-step
+// prefetch would leave every step waiting a full memory round trip: the A
+// rows and the staged B rows are loaded PF steps ahead into a register ring
+// of PF + 1 sets.  The B rows go through LDS (double-buffered) as in
+// train_gemm_kernel; the same LDS then turns the results around so that 32
+// lanes store one row's 128 columns (512 contiguous bytes).
+constexpr int WG_M = 256;              // M rows per wgrad workgroup
+constexpr int WG_MT = WG_M / 4 / 16;   // 16-row M tiles per wave
+constexpr int OT_LD = TN + 4;          // fp32 stride of a turned-around row
+constexpr int WG_LDS_BYTES = 4 * 16 * OT_LD * 4;
+static_assert(WG_LDS_BYTES >= 2 * TN * B_LD * 2, "LDS turnaround must hold the B stages");
+
+template <int PF>
+__global__ __launch_bounds__(256, 2) void train_wgrad_kernel(const TrainGemmArgs g) {
+  constexpr int NR = PF + 1;           // register ring sets
+  constexpr int UN = 2 * NR;           // unroll: LDS buffer and ring slot compile-time
+  __shared__ __attribute__((aligned(16))) uint8_t lds[WG_LDS_BYTES];
+  uint16_t* bs = reinterpret_cast<uint16_t*>(lds);   // [2][TN * B_LD] during the K loop
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, q4 = lane >> 4;
+
+  const TileWork wi = decode_wgrad(g);
+  if (!wi.valid) return;
+  const int grp = wi.grp;
+  const int k0 = g.pad_off[grp], k1 = g.pad_off[grp + 1];
+  const size_t kbase = (size_t)k0;
+  const int nks = (k1 - k0) / TK;
+
+  // K-blocked operands: step s of row r at (kbase / 32 + s) * ld + 32 r
+  const uint16_t* arow[WG_MT];
+#pragma unroll
+  for (int mt = 0; mt < WG_MT; ++mt) {
+    const size_t row = (size_t)(WG_M * wi.mi + TMW * wave + 16 * mt + l16);
+    arow[mt] = g.A + (kbase / TK) * (size_t)g.lda + row * TK + 8 * q4;
+  }
+  const uint16_t* brow[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int tr = (tid >> 2) + 64 * c;
+    brow[c] = g.B + (kbase / TK) * (size_t)g.ldb + (size_t)(TN * wi.ni + tr) * TK + 8 * (tid & 3);
+  }
+
+  v4f acc[WG_MT][8];
+#pragma unroll
+  for (int mt = 0; mt < WG_MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) acc[mt][nt] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  v4i ar[NR][WG_MT];
+  v4i br[NR][2];
+  // loads of step s (clamped to the last step: past it they repeat loads
+  // that are never used)
+  auto load = [&](int slot_a, int s) {
+    const int sc = min(s, nks - 1);
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+      br[slot_a][c] = *reinterpret_cast<const v4i*>(brow[c] + (size_t)sc * g.ldb);
+#pragma unroll
+    for (int mt = 0; mt < WG_MT; ++mt)
+      ar[slot_a][mt] = *reinterpret_cast<const v4i*>(arow[mt] + (size_t)sc * g.lda);
+  };
+  auto store_b = [&](int buf, int slot) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+      *reinterpret_cast<v4i*>(&bs[buf * TN * B_LD + ((tid >> 2) + 64 * c) * B_LD + 8 * (tid & 3)]) =
+          br[slot][c];
+  };
+  auto compute = [&](int slot, int buf) {
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+      const v8bf b = __builtin_bit_cast(
+          v8bf, *reinterpret_cast<const v4i*>(&bs[buf * TN * B_LD + (16 * nt + l16) * B_LD + 8 * q4]));
+#pragma unroll
+      for (int mt = 0; mt < WG_MT; ++mt)
+        acc[mt][nt] = mfma16(__builtin_bit_cast(v8bf, ar[slot][mt]), b, acc[mt][nt]);
+    }
+  };
+
+  if (nks > 0) {
+#pragma unroll
+    for (int j = 0; j < NR; ++j) load(j, j);   // steps 0 .. PF
+    store_b(0, 0);
+    __syncthreads();
+    // step s (ring slot s % NR, LDS buffer s % 2): compute, stage B of s + 1
+    // into the other buffer, load step s + NR into the freed slot
+    for (int s0 = 0; s0 < nks; s0 += UN) {
+#pragma unroll
+      for (int j = 0; j < UN; ++j) {
+        const int s = s0 + j;
+        if (s < nks) {
+          compute(j % NR, j & 1);
+          store_b((j + 1) & 1, (j + 1) % NR);
+          load(j % NR, s + NR);
+          __syncthreads();
+        }
+      }
+    }
+  }
+  // after the last step's barrier (or with no K steps, LDS untouched) the
+  // LDS turns C[m][n] around -> out[grp][m][n] (fp32, nn.Linear layout),
+  // non-temporal (the gradient is not read again here)
+  float* out = g.out + (size_t)grp * g.out_stride + (size_t)TN * wi.ni;
+  float* tw = reinterpret_cast<float*>(lds) + wave * 16 * OT_LD;
+#pragma unroll
+  for (int mt = 0; mt < WG_MT; ++mt) {
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) tw[(4 * q4 + r) * OT_LD + 16 * nt + l16] = acc[mt][nt][r];
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = 2 * i + (lane >> 5), col = 4 * (lane & 31);
+      const v4f v = *reinterpret_cast<const v4f*>(&tw[row * OT_LD + col]);
+      const size_t m = (size_t)(WG_M * wi.mi + TMW * wave + 16 * mt + row);
+      __builtin_nontemporal_store(v, reinterpret_cast<v4f*>(out + m * g.ldo + col));
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// the ring depth used: loads one step ahead (two and three steps ahead
+// measured 3% and 7% slower at the K2 prefill batch, bitwise the same)
+constexpr int WGRAD_PF = 1;
+
 }  // namespace
 
 hipError_t launch_train_gemm(int mode, const TrainGemmArgs& a, int grid, hipStream_t s) {
@@ -711,7 +803,7 @@ hipError_t launch_train_gemm(int mode, const TrainGemmArgs& a, int grid, hipStre
     case TM_FWD_DOWN: train_gemm_kernel<TM_FWD_DOWN><<<grid, 256, 0, s>>>(a); break;
     case TM_BWD_DOWN: train_gemm_kernel<TM_BWD_DOWN><<<grid, 256, 0, s>>>(a); break;
     case TM_BWD_GU: train_gemm_kernel<TM_BWD_GU><<<grid, 256, 0, s>>>(a); break;
-    case TM_WGRAD: train_gemm_kernel<TM_WGRAD><<<grid, 256, 0, s>>>(a); break;
+    case TM_WGRAD: train_wgrad_kernel<WGRAD_PF><<<grid, 256, 0, s>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

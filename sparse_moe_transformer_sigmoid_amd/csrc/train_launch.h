@@ -24,12 +24,12 @@ struct TrainGemmArgs {
   const uint16_t* A;          // group 0's matrix (forward gate/up: the gate matrix)
   const uint16_t* A2;         // forward gate/up: the up matrix
   size_t a_stride;            // elements between groups' matrices
-  int lda;
+  int lda;                    // row stride; wgrad: elements per 32-column K block
   // B: 128 rows staged through LDS (bf16, K contiguous)
   const uint16_t* B;
-  int ldb;
+  int ldb;                    // row stride; wgrad: elements per 32-column K block
   // wgrad: padded column offsets of the groups in the transposed operands,
-  // M and N tiles per group, gradient output
+  // 256-row M tiles and 128-column N tiles per group, gradient output
   const int32_t* pad_off;     // [G+1]
   int MT, NT;
   float* out;
@@ -57,7 +57,7 @@ struct TransposeArgs {
   const float* topk_w;        // [P] (mode 1)
   const int32_t* pad_off;     // [G+1]
   int E, G, T, P, k, C;
-  uint16_t* dst;              // [C, ldt]
+  uint16_t* dst;              // ldt / 32 K blocks of [C][32]
   int ldt;
 };
 hipError_t launch_pad_offsets(int E, int G, int T, int P, const int32_t* offsets,
