@@ -51,7 +51,8 @@ extern "C" {
 size_t moe_train_weights_bytes(const moe_config* cfg);
 
 /* Bytes of the transposed copies: per expert down^T [d_ff, d_model] and
- * [gate; up]^T [d_model, 2 d_ff] (bf16). */
+ * [gate; up]^T [d_model, 2 d_ff] (bf16), each stored in 32-column K blocks:
+ * element (row, k) of a [rows, K] copy at ((k / 32) * rows + row) * 32 + k % 32. */
 size_t moe_train_transposed_bytes(const moe_config* cfg);
 
 /* wt <- the transposed copies of w (both canonical / transposed layouts above). */

@@ -925,13 +925,13 @@ moe_status moe_train_transpose_weights(const moe_config* cfg, const void* w, voi
   const size_t d = (size_t)D.d, I = (size_t)D.I, es = 3 * I * d;
   const uint16_t* src = static_cast<const uint16_t*>(w);
   uint16_t* dst = static_cast<uint16_t*>(wt);
-  // expert g: down^T [I, d] at g * 3Id, [gate; up]^T [d, 2I] at g * 3Id + Id
-  K2_HIP(k2::launch_transpose_w(D.G, (int)d, (int)I, src + 2 * I * d, es, (int)I, dst, es,
-                                (int)d, 0, s));
-  K2_HIP(k2::launch_transpose_w(D.G, (int)I, (int)d, src, es, (int)d, dst + I * d, es,
-                                (int)(2 * I), 0, s));
+  // expert g: down^T [I, d] at g * 3Id, [gate; up]^T [d, 2I] at g * 3Id + Id,
+  // both K-blocked
+  K2_HIP(k2::launch_transpose_w(D.G, (int)d, (int)I, src + 2 * I * d, es, (int)I, dst, es, 0,
+                                s));
+  K2_HIP(k2::launch_transpose_w(D.G, (int)I, (int)d, src, es, (int)d, dst + I * d, es, 0, s));
   K2_HIP(k2::launch_transpose_w(D.G, (int)I, (int)d, src + I * d, es, (int)d, dst + I * d, es,
-                                (int)(2 * I), (int)I, s));
+                                (int)I, s));
   return MOE_OK;
 }
 
@@ -1095,7 +1095,7 @@ moe_status moe_train_backward(const moe_config* cfg, int64_t T, const void* dout
     // down: da_raw = W_down^T dy (A = down^T [I, d]), epilogue: a~, dw, dg, du
     a.A = WT;
     a.a_stride = 3 * I * d;
-    a.lda = D.d;
+    a.lda = 32 * D.I;   // K-blocked: 32 K of all I rows per block
     a.B = static_cast<const uint16_t*>(dout);
     a.ldb = D.d;
     a.K = D.d;
@@ -1103,7 +1103,7 @@ moe_status moe_train_backward(const moe_config* cfg, int64_t T, const void* dout
     K2_HIP(k2::launch_train_gemm(k2::TM_BWD_DOWN, a, train_grid(D, a.NC), s));
     // gate/up: dh_row = [W_gate; W_up]^T [dg; du] (A = [gate; up]^T [d, 2I])
     a.A = WT + I * d;
-    a.lda = 2 * D.I;
+    a.lda = 32 * D.d;   // K-blocked: 32 K of all d rows per block
     a.B = a.dgu;
     a.ldb = 2 * D.I;
     a.K = 2 * D.I;

@@ -129,6 +129,7 @@ __global__ __launch_bounds__(256, 2) void train_gemm_kernel(const TrainGemmArgs 
   const int l16 = lane & 15, q4 = lane >> 4;
 
   static_assert(MODE != TM_WGRAD, "weight gradients use train_wgrad_kernel");
+  constexpr bool KBLK_A = MODE == TM_BWD_DOWN || MODE == TM_BWD_GU;
   const TileWork wi = decode_rows(g);
   if (!wi.valid) return;
   const int grp = wi.grp;
@@ -147,7 +148,9 @@ __global__ __launch_bounds__(256, 2) void train_gemm_kernel(const TrainGemmArgs 
       base = g.A + (size_t)grp * g.a_stride;
       row = (size_t)(256 * wi.nc + TMW * wave + 16 * mt + l16);
     }
-    arow[mt] = base + row * (size_t)g.lda + 8 * q4;
+    // dgrad: A is a K-blocked transposed weight copy, step s of row r at
+    // s * lda + 32 r (lda = rows * 32); otherwise row-major with stride lda
+    arow[mt] = base + row * (size_t)(KBLK_A ? TK : g.lda) + 8 * q4;
   }
   // B rows staged by this thread: tile rows tid/4 and tid/4 + 64, 8 K each
   const uint16_t* brow[2];
@@ -176,7 +179,8 @@ __global__ __launch_bounds__(256, 2) void train_gemm_kernel(const TrainGemmArgs 
   v4i breg[2];
   auto load_a = [&](v4i (&a)[4], int s) {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) a[mt] = *reinterpret_cast<const v4i*>(arow[mt] + (size_t)s * TK);
+    for (int mt = 0; mt < 4; ++mt)
+      a[mt] = *reinterpret_cast<const v4i*>(arow[mt] + (size_t)s * (KBLK_A ? g.lda : TK));
   };
   auto load_b = [&](int s) {
 #pragma unroll
@@ -495,13 +499,14 @@ __global__ __launch_bounds__(256) void transpose_pad_kernel(const TransposeArgs 
   }
 }
 
-// Plain transpose of bf16 matrices: dst[c][r] = src[r][c] for one [R][C]
-// matrix per blockIdx.z (the weight copies the dgrad products read).
-// dst_ld / src_ld in elements; (dst column offset for stacking gate and up).
+// Transpose of bf16 matrices into the K-blocked layout the dgrad products
+// read: dst (c, k) = src[k - dst_col0][c] for one [R][C] matrix per
+// blockIdx.z, element (c, k) at ((k / 32) * C + c) * 32 + k % 32 (dst_col0:
+// the K offset, for stacking gate and up); src_ld in elements.
 __global__ __launch_bounds__(256) void transpose_w_kernel(int R, int C, const uint16_t* src,
                                                           size_t src_stride, int src_ld,
                                                           uint16_t* dst, size_t dst_stride,
-                                                          int dst_ld, int dst_col0) {
+                                                          int dst_col0) {
   __shared__ uint16_t tile[64][66];
   const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
   const uint16_t* s = src + (size_t)blockIdx.z * src_stride;
@@ -525,7 +530,8 @@ __global__ __launch_bounds__(256) void transpose_w_kernel(int R, int C, const ui
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       w[i] = (uint32_t)tile[qq + 2 * i][cr] | ((uint32_t)tile[qq + 2 * i + 1][cr] << 16);
-    uint4* o = reinterpret_cast<uint4*>(d + (size_t)(c0 + cr) * dst_ld + dst_col0 + r0 + qq);
+    const int k = dst_col0 + r0 + qq;   // 16 K inside one 32-wide block
+    uint4* o = reinterpret_cast<uint4*>(d + ((size_t)(k >> 5) * C + c0 + cr) * 32 + (k & 31));
     o[0] = make_uint4(w[0], w[1], w[2], w[3]);
     o[1] = make_uint4(w[4], w[5], w[6], w[7]);
   }
@@ -828,11 +834,11 @@ hipError_t launch_transpose_pad(int src_mode, const TransposeArgs& a, int padded
 }
 
 hipError_t launch_transpose_w(int n, int R, int C, const uint16_t* src, size_t src_stride,
-                              int src_ld, uint16_t* dst, size_t dst_stride, int dst_ld,
-                              int dst_col0, hipStream_t s) {
+                              int src_ld, uint16_t* dst, size_t dst_stride, int dst_col0,
+                              hipStream_t s) {
   if (n <= 0) return hipSuccess;
   transpose_w_kernel<<<dim3(R / 64, C / 64, n), 256, 0, s>>>(R, C, src, src_stride, src_ld, dst,
-                                                             dst_stride, dst_ld, dst_col0);
+                                                             dst_stride, dst_col0);
   return hipGetLastError();
 }
 

@@ -24,7 +24,7 @@ struct TrainGemmArgs {
   const uint16_t* A;          // group 0's matrix (forward gate/up: the gate matrix)
   const uint16_t* A2;         // forward gate/up: the up matrix
   size_t a_stride;            // elements between groups' matrices
-  int lda;                    // row stride; wgrad: elements per 32-column K block
+  int lda;                    // row stride; dgrad and wgrad: elements per 32-column K block
   // B: 128 rows staged through LDS (bf16, K contiguous)
   const uint16_t* B;
   int ldb;                    // row stride; wgrad: elements per 32-column K block
@@ -64,9 +64,11 @@ hipError_t launch_pad_offsets(int E, int G, int T, int P, const int32_t* offsets
                               int32_t* pad_off, hipStream_t s);
 hipError_t launch_transpose_pad(int src_mode, const TransposeArgs& a, int padded_cols,
                                 hipStream_t s);
+// n [R][C] bf16 matrices -> K-blocked transposes: element (c, k = dst_col0 + r)
+// at ((k / 32) * C + c) * 32 + k % 32
 hipError_t launch_transpose_w(int n, int R, int C, const uint16_t* src, size_t src_stride,
-                              int src_ld, uint16_t* dst, size_t dst_stride, int dst_ld,
-                              int dst_col0, hipStream_t s);
+                              int src_ld, uint16_t* dst, size_t dst_stride, int dst_col0,
+                              hipStream_t s);
 
 hipError_t launch_chosen_scores(int T, int E, int k, const float* z, const int32_t* ids,
                                 float* sc, hipStream_t s);
