@@ -392,6 +392,15 @@ def train_line(steps, warmup):
     L.check("moe_profile_read", lib.moe_profile_read(ms_a, n_a, 1))
     ms = start.elapsed_time(stop) / steps
     stage = {nm: ms_a[i] / steps for i, nm in enumerate(L.STAGES) if ms_a[i] > 0}
+    # the dgrad products read transposed copies of the weights, which must be
+    # refreshed (moe_train_transpose_weights) after every weight update: once
+    # per optimizer step, outside the forward + backward timed above
+    start.record(s)
+    for _ in range(3):
+        layer.transpose_weights()
+    stop.record(s)
+    torch.cuda.synchronize()
+    copy_ms = start.elapsed_time(stop) / 3
     R = T * sh.top_k + T * sh.n_shared
     flops = 18.0 * R * I * d
     nbytes = 2 * G * 3 * I * d * 2 + G * 3 * I * d * 4
@@ -399,6 +408,7 @@ def train_line(steps, warmup):
     gbs = nbytes / (ms * 1e-3) / 1e9
     line = {"workload": "k2_prefill_train_step", "tokens": T, "rows": R, "ms_per_step": ms,
             "value": T / (ms * 1e-3), "unit": "tokens/s", "stage_ms": stage,
+            "weight_copy_ms": copy_ms, "ms_per_step_with_weight_copy": ms + copy_ms,
             "algorithmic_tflop": flops / 1e12, "bf16_tflops": tf,
             "frac_bf16_peak": tf / BF16_PEAK_TFLOPS,
             # 18 R I d flops over the bytes below is ~144 flop/B, under the bf16

@@ -88,6 +88,12 @@ moe_status moe_train_forward(const moe_config* cfg, int64_t T, const void* x, co
  *   optional (NULL to skip): dh_rows [R, d] (each row's dgrad through its
  *   expert before the per-token sum, permuted order) and dw [T, k] (the
  *   gradient of each routing weight). */
+/* Streams: the weight-gradient chain runs on a second stream that the
+ * library keeps per device (default priority), forked from `stream` after
+ * the down dgrad and joined back into it before the call returns, so all of
+ * the call's work is ordered after earlier and before later work on `stream`
+ * (also under graph capture).  Overlapping calls on one device from several
+ * host threads share that stream's events: the caller serializes them. */
 moe_status moe_train_backward(const moe_config* cfg, int64_t T, const void* dout, const void* x,
                               const void* norm_w, const void* w_router, const void* w,
                               const void* wt, const void* saved, float* dx, float* d_norm_w,

@@ -590,6 +590,105 @@ moe_status scratch_of_current_device(void** ptr) {
   return MOE_OK;
 }
 
+// A second stream (default priority) and a fork / join event pair per
+// device, created on first use and kept until the process ends: the training
+// backward runs its two independent chains on them.
+struct SideStream {
+  hipStream_t s2 = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_side_mu;
+SideStream g_side[MAX_DEVICES];
+
+moe_status side_stream_of_current_device(SideStream* out) {
+  int dev = -1;
+  K2_HIP(hipGetDevice(&dev));
+  K2_REQUIRE(dev >= 0 && dev < MAX_DEVICES, MOE_ERR_UNSUPPORTED, "device index beyond 63");
+  std::lock_guard<std::mutex> g(g_side_mu);
+  SideStream& ss = g_side[dev];
+  if (ss.s2 == nullptr) {
+    SideStream n;
+    K2_HIP(hipStreamCreateWithFlags(&n.s2, hipStreamNonBlocking));
+    K2_HIP(hipEventCreateWithFlags(&n.fork, hipEventDisableTiming));
+    K2_HIP(hipEventCreateWithFlags(&n.join, hipEventDisableTiming));
+    ss = n;
+  }
+  *out = ss;
+  return MOE_OK;
+}
+
+// The weight-gradient chain of the training backward, enqueued on s: the
+// group-padded K-blocked transposes of its operands, then dW_down and
+// dW_gate, dW_up.
+moe_status train_wgrad_chain(const Dims& D, const TrainLayout& L, int64_t T, void* ws, void* sv,
+                             const TrainSaved& v, const int32_t* offsets,
+                             const int32_t* row_pair, const float* wts, const void* dout,
+                             const uint16_t* abf, const uint16_t* dgu, float* d_w,
+                             hipStream_t s) {
+  const size_t d = (size_t)D.d, I = (size_t)D.I;
+  const int64_t ldt = train_ldt(D);
+  Stage stg(MOE_STAGE_TRAIN_WGRAD, s);
+  int32_t* pad_off = at<int32_t>(ws, L.pad_off);
+  K2_HIP(k2::launch_pad_offsets(D.E, D.G, (int)T, (int)D.P, offsets, pad_off, s));
+  k2::TransposeArgs ta{};
+  ta.offsets = offsets;
+  ta.row_pair = row_pair;
+  ta.topk_w = wts;
+  ta.pad_off = pad_off;
+  ta.E = D.E;
+  ta.G = D.G;
+  ta.T = (int)T;
+  ta.P = (int)D.P;
+  ta.k = D.k;
+  ta.ldt = (int)ldt;
+  uint16_t* dywT = at<uint16_t>(ws, L.dywT);
+  uint16_t* aT = at<uint16_t>(ws, L.aT);
+  uint16_t* dguT = at<uint16_t>(ws, L.dguT);
+  uint16_t* hT = at<uint16_t>(ws, L.hT);
+  ta.src = static_cast<const uint16_t*>(dout);
+  ta.C = D.d;
+  ta.dst = dywT;
+  K2_HIP(k2::launch_transpose_pad(1, ta, (int)ldt, s));
+  ta.src = abf;
+  ta.C = D.I;
+  ta.dst = aT;
+  K2_HIP(k2::launch_transpose_pad(0, ta, (int)ldt, s));
+  ta.src = dgu;
+  ta.C = 2 * D.I;
+  ta.dst = dguT;
+  K2_HIP(k2::launch_transpose_pad(0, ta, (int)ldt, s));
+  ta.src = nullptr;
+  ta.codes = at<const uint8_t>(sv, v.hq);
+  ta.scales = at<const float>(sv, v.hs);
+  ta.C = D.d;
+  ta.dst = hT;
+  K2_HIP(k2::launch_transpose_pad(2, ta, (int)ldt, s));
+  // dW_down [d, I] = sum (w dy)^T a~ ; dW_gate, dW_up [2I, d] = sum [dg; du]^T h~
+  k2::TrainGemmArgs g{};
+  g.G = D.G;
+  g.pad_off = pad_off;
+  g.out_stride = 3 * I * d;
+  g.A = dywT;   // K-blocked transposed operands: 32 C elements per K block
+  g.lda = 32 * D.d;
+  g.B = aT;
+  g.ldb = 32 * D.I;
+  g.MT = D.d / 256;
+  g.NT = D.I / 128;
+  g.out = d_w + 2 * I * d;
+  g.ldo = D.I;
+  K2_HIP(k2::launch_train_gemm(k2::TM_WGRAD, g, (D.G * g.MT * g.NT + 7) / 8 * 8, s));
+  g.A = dguT;
+  g.lda = 32 * 2 * D.I;
+  g.B = hT;
+  g.ldb = 32 * D.d;
+  g.MT = 2 * D.I / 256;
+  g.NT = D.d / 128;
+  g.out = d_w;
+  g.ldo = D.d;
+  K2_HIP(k2::launch_train_gemm(k2::TM_WGRAD, g, (D.G * g.MT * g.NT + 7) / 8 * 8, s));
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1101,6 +1200,21 @@ moe_status moe_train_backward(const moe_config* cfg, int64_t T, const void* dout
     a.K = D.d;
     a.NC = D.I / 256;
     K2_HIP(k2::launch_train_gemm(k2::TM_BWD_DOWN, a, train_grid(D, a.NC), s));
+  }
+  // The weight gradients need only the down dgrad's outputs (a~, dg, du) and
+  // the saved state: they run on the side stream while the gate/up dgrad and
+  // the router backward run on `stream` (the gate/up dgrad reads weights, the
+  // weight gradients mostly write), joined before returning.
+  SideStream side;
+  if ((st = side_stream_of_current_device(&side)) != MOE_OK) return st;
+  K2_HIP(hipEventRecord(side.fork, s));
+  K2_HIP(hipStreamWaitEvent(side.s2, side.fork, 0));
+  if ((st = train_wgrad_chain(D, L, T, ws, sv, v, offsets, row_pair, wts, dout, a.abf, a.dgu,
+                              d_w, side.s2)) != MOE_OK)
+    return st;
+  K2_HIP(hipEventRecord(side.join, side.s2));
+  {
+    Stage stg(MOE_STAGE_TRAIN_DGRAD, s);
     // gate/up: dh_row = [W_gate; W_up]^T [dg; du] (A = [gate; up]^T [d, 2I])
     a.A = WT + I * d;
     a.lda = 32 * D.d;   // K-blocked: 32 K of all d rows per block
@@ -1146,65 +1260,7 @@ moe_status moe_train_backward(const moe_config* cfg, int64_t T, const void* dout
                                    at<const uint8_t>(sv, v.hq), at<const float>(sv, v.hs),
                                    d_w_router, s));
   }
-  Stage stg(MOE_STAGE_TRAIN_WGRAD, s);
-  int32_t* pad_off = at<int32_t>(ws, L.pad_off);
-  K2_HIP(k2::launch_pad_offsets(D.E, D.G, (int)T, (int)D.P, offsets, pad_off, s));
-  k2::TransposeArgs ta{};
-  ta.offsets = offsets;
-  ta.row_pair = row_pair;
-  ta.topk_w = wts;
-  ta.pad_off = pad_off;
-  ta.E = D.E;
-  ta.G = D.G;
-  ta.T = (int)T;
-  ta.P = (int)D.P;
-  ta.k = D.k;
-  ta.ldt = (int)ldt;
-  uint16_t* dywT = at<uint16_t>(ws, L.dywT);
-  uint16_t* aT = at<uint16_t>(ws, L.aT);
-  uint16_t* dguT = at<uint16_t>(ws, L.dguT);
-  uint16_t* hT = at<uint16_t>(ws, L.hT);
-  ta.src = static_cast<const uint16_t*>(dout);
-  ta.C = D.d;
-  ta.dst = dywT;
-  K2_HIP(k2::launch_transpose_pad(1, ta, (int)ldt, s));
-  ta.src = a.abf;
-  ta.C = D.I;
-  ta.dst = aT;
-  K2_HIP(k2::launch_transpose_pad(0, ta, (int)ldt, s));
-  ta.src = a.dgu;
-  ta.C = 2 * D.I;
-  ta.dst = dguT;
-  K2_HIP(k2::launch_transpose_pad(0, ta, (int)ldt, s));
-  ta.src = nullptr;
-  ta.codes = at<const uint8_t>(sv, v.hq);
-  ta.scales = at<const float>(sv, v.hs);
-  ta.C = D.d;
-  ta.dst = hT;
-  K2_HIP(k2::launch_transpose_pad(2, ta, (int)ldt, s));
-  // dW_down [d, I] = sum (w dy)^T a~ ; dW_gate, dW_up [2I, d] = sum [dg; du]^T h~
-  k2::TrainGemmArgs g{};
-  g.G = D.G;
-  g.pad_off = pad_off;
-  g.out_stride = 3 * I * d;
-  g.A = dywT;   // K-blocked transposed operands: 32 C elements per K block
-  g.lda = 32 * D.d;
-  g.B = aT;
-  g.ldb = 32 * D.I;
-  g.MT = D.d / 256;
-  g.NT = D.I / 128;
-  g.out = d_w + 2 * I * d;
-  g.ldo = D.I;
-  K2_HIP(k2::launch_train_gemm(k2::TM_WGRAD, g, (D.G * g.MT * g.NT + 7) / 8 * 8, s));
-  g.A = dguT;
-  g.lda = 32 * 2 * D.I;
-  g.B = hT;
-  g.ldb = 32 * D.d;
-  g.MT = 2 * D.I / 256;
-  g.NT = D.d / 128;
-  g.out = d_w;
-  g.ldo = D.d;
-  K2_HIP(k2::launch_train_gemm(k2::TM_WGRAD, g, (D.G * g.MT * g.NT + 7) / 8 * 8, s));
+  K2_HIP(hipStreamWaitEvent(s, side.join, 0));
   return MOE_OK;
 }
 
