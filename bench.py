@@ -224,8 +224,8 @@ def secondary_line(r, workload, sclk=None):
 
 def mla_line(shape, steps, warmup):
     """One MLA attention workload: whole sub-layer time (HIP events on the
-    launch stream), per-stage times, and the attention kernel against its
-    roofline.  Decode is bound by HBM: per step it must read every attended
+    launch stream; decode replayed from a HIP graph, the eager time beside
+    it), per-stage times, and the attention kernel against its roofline.  Decode is bound by HBM: per step it must read every attended
     cache position (656 B: 512 latent codes, 4 scales, 64 bf16 rotary
     features) and the absorbed queries and write the latent outputs.  Prefill
     is bound by the bf16 MFMA: 2 (576 + 512) flops per (query, head, visible
@@ -260,6 +260,23 @@ def mla_line(shape, steps, warmup):
     L.check("moe_profile_read", lib.moe_profile_read(ms_a, n_a, 1))
     step_ms = start.elapsed_time(stop) / steps
     stage = {nm: ms_a[i] / steps for i, nm in enumerate(L.STAGES) if nm.startswith("mla_")}
+    eager_ms = step_ms
+    launch = "eager"
+    if n == 1:
+        # decode: the step replayed from a HIP graph of mla_forward (the same
+        # kernels and buffers; per-stage times above are from the eager calls)
+        g = layer.capture_forward(inp.x, inp.cached_len, cache, S, n, out)
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(steps):
+            g.replay()
+        stop.record()
+        torch.cuda.synchronize()
+        step_ms = start.elapsed_time(stop) / steps
+        launch = "hip_graph"
+        del g
     T, H = shape.tokens, shape.n_heads
     cached = np.asarray(shape.cached, dtype=np.int64)
     visible = int(sum(int(c) * n + n * (n + 1) // 2 for c in cached))   # (query, position) pairs
@@ -273,7 +290,8 @@ def mla_line(shape, steps, warmup):
     layer_bytes = w_bytes + attended * row_bytes + 2 * T * shape.d_model * 2
     line = {"workload": shape.name, "sequences": S, "new_tokens_per_sequence": n,
             "cached_per_sequence": sorted(set(int(c) for c in cached)), "tokens": T,
-            "ms_per_step": step_ms, "value": T / (step_ms * 1e-3), "unit": "tokens/s",
+            "ms_per_step": step_ms, "eager_ms_per_step": eager_ms, "launch": launch,
+            "value": T / (step_ms * 1e-3), "unit": "tokens/s",
             "stage_ms": stage, "layer_bytes": layer_bytes,
             "layer_frac_hbm": layer_bytes / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
     ai = attn_flops / attn_bytes

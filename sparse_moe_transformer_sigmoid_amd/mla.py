@@ -74,6 +74,25 @@ class K2MLA:
                1 if out_f32 else 0, _p(ws), ws.numel(), _stream())
         return out
 
+    def capture_forward(self, x, cached_len, cache, n_seq: int, n_new: int, out):
+        """Record mla_forward into a HIP graph (replay with .replay()).
+
+        The workspace is allocated before capture; mla_forward enqueues kernels
+        only (no allocation, memset or synchronisation), so the graph replays
+        the same launches with the same buffers.  A replay writes the new
+        tokens' cache entries again at the same positions.
+        """
+        self.workspace(n_seq, n_new, cache[0].shape[1])
+        side = torch.cuda.Stream(device=self.device)
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):            # one eager call off the default stream
+            self.forward(x, cached_len, cache, n_seq, n_new, out=out)
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.forward(x, cached_len, cache, n_seq, n_new, out=out)
+        return g
+
     def attention(self, x, cached_len, cache, n_seq: int, n_new: int):
         """The attention output of every head before W_o: [T, heads * v_head] fp32."""
         codes, scales, rope = cache

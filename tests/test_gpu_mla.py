@@ -139,6 +139,40 @@ def test_k2_mla_decode():
     check_mla(inp, tokens=np.array([0, 9, 31, 63]))
 
 
+def test_k2_mla_decode_graph_replay():
+    """mla_forward captured in a HIP graph: every replay equals the eager call
+    bitwise (output and new cache entries), with eager work on other inputs and
+    synchronisations between replays."""
+    from sparse_moe_transformer_sigmoid_amd.mla import K2MLA
+    inp = synth.generate_mla(synth.MLA_K2_DECODE, seed=0, device="cuda")
+    layer = K2MLA(inp)
+    S, n = inp.shape.n_seq, inp.shape.n_new
+    pos = inp.cached_len.long()                 # the new token's position per sequence
+    seqs = torch.arange(S, device=pos.device)
+    cache = inp.fresh_cache()
+    eager = layer.forward(inp.x, inp.cached_len, cache, S, n).clone()
+    eager_cache = [c.clone() for c in cache]
+    other_x = torch.flip(inp.x, dims=[0]).contiguous()
+    other_cache = inp.fresh_cache()
+    out = torch.empty_like(eager)
+    g = layer.capture_forward(inp.x, inp.cached_len, cache, S, n, out)
+    for r in range(3):
+        out.zero_()
+        for c in cache:
+            c[seqs, pos] = 0                    # the replay must write them again
+        layer.forward(other_x, inp.cached_len, other_cache, S, n)   # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        _log(f"mla graph replay {r}")
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {r}"
+        # the replay rewrites only the new positions: compare those entries
+        for c, e in zip(cache, eager_cache):
+            assert torch.equal(c[seqs, pos].view(torch.uint8), e[seqs, pos].view(torch.uint8)), \
+                f"replay {r}: cache entries"
+    del g
+
+
 def test_k2_mla_prefill():
     """2 x 4,096 new tokens from an empty cache; tokens at the start, the middle
     and the end of both sequences."""
