@@ -157,8 +157,12 @@ __device__ __forceinline__ void rope_pair(float a, float b, int pos, double f, f
 // bf16 into the cache.  qkv row: [q_a (q_lora), kv_a latent (512), k_pe (64)].
 // Norms as in the input RMSNorm: mean of squares formed in fp64, rounded to
 // fp32, r = 1/sqrt(ms + eps), h = bf16((v r) g).
+constexpr int MAX_QKV = 8192 + DL + DR;   // longest [q_a; kv_a] row (q_lora <= 8192)
+
+// qkv: the [q_a; kv_a] projection as nsplit K-slice partial sums [nsplit, T,
+// qkv_ld], added in slice order (the order of launch_slice_sum).
 __global__ __launch_bounds__(256) void mla_latent_kernel(
-    int q_lora, int qkv_ld, float eps, const float* __restrict__ qkv,
+    int T, int nsplit, int q_lora, int qkv_ld, float eps, const float* __restrict__ qkv,
     const uint16_t* __restrict__ g_qa, const uint16_t* __restrict__ g_kva,
     const double* __restrict__ inv_freq, const int32_t* __restrict__ cached_len, int n_new,
     int max_len, uint8_t* __restrict__ qa_q, float* __restrict__ qa_s,
@@ -166,9 +170,17 @@ __global__ __launch_bounds__(256) void mla_latent_kernel(
   const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int seq;
   const int pos = token_pos(cached_len, t, n_new, max_len, &seq);
-  const float* row = qkv + (size_t)t * qkv_ld;
   const size_t cidx = (size_t)seq * max_len + pos;
   __shared__ double red[2][4];
+  __shared__ float rowbuf[MAX_QKV];
+  const int nrow = q_lora + DL + DR;
+  for (int i = tid; i < nrow; i += 256) {
+    float a = qkv[(size_t)t * qkv_ld + i];
+    for (int s = 1; s < nsplit; ++s) a += qkv[((size_t)s * T + t) * qkv_ld + i];
+    rowbuf[i] = a;
+  }
+  __syncthreads();
+  const float* row = rowbuf;
   // sums of squares: query latent (q_lora values) and key-value latent (512)
   double sq = 0.0, sc = 0.0;
   for (int i = tid; i < q_lora; i += 256) sq += (double)row[i] * (double)row[i];
@@ -659,18 +671,30 @@ __device__ __forceinline__ void split8(const float4 a, const float4 b, v8bf* hi,
 
 constexpr int QA_TB = 32;   // tokens per workgroup
 
+// q: the q_b projection as nsplit K-slice partial sums [nsplit, T, H*192],
+// added in slice order (the order of launch_slice_sum).
 // qcat[t, h] = scale * [W_uk^T q_nope (512), rope(q_pe) (64)] in fp32, per
 // latent block b: s_b * sum_d code[d][r] q[d] (W_uk of head h: key-value
 // up-projection rows h*(DN+DV) .. + DN - 1, one 128-row scale block).
 // Workgroup = (head, 32 tokens); wave w: latents 128 w .. + 127 (block w).
 __global__ __launch_bounds__(256) void mla_qabsorb_kernel(
-    int T, int H, float smscale, const float* __restrict__ q, const uint16_t* __restrict__ ukt,
+    int T, int H, int nsplit, float smscale, const float* __restrict__ q,
+    const uint16_t* __restrict__ ukt,
     const float* __restrict__ s_kvb, const double* __restrict__ inv_freq,
     const int32_t* __restrict__ cached_len, int n_new, int max_len,
     float* __restrict__ qcat) {
   const int h = blockIdx.x, t0 = blockIdx.y * QA_TB, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, q4 = lane >> 4, l16 = lane & 15;
   const int qld = H * (DN + DR);
+  const size_t slice = (size_t)T * qld;
+  auto q4sum = [&](const float* p) {   // the partial sums of 4 values, in slice order
+    float4 a = *reinterpret_cast<const float4*>(p);
+    for (int s = 1; s < nsplit; ++s) {
+      const float4 b = *reinterpret_cast<const float4*>(p + s * slice);
+      a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+    }
+    return a;
+  };
   // A: q_nope of tokens t0 + 16 mt + l16 (the last token repeated past T),
   // features 32 ks + 8 q4 .. + 7
   v8bf ahi[2][DN / 32], alo[2][DN / 32];
@@ -680,8 +704,7 @@ __global__ __launch_bounds__(256) void mla_qabsorb_kernel(
     const float* qp = q + (size_t)t * qld + h * (DN + DR) + 8 * q4;
 #pragma unroll
     for (int ks = 0; ks < DN / 32; ++ks)
-      split8(*reinterpret_cast<const float4*>(qp + 32 * ks),
-             *reinterpret_cast<const float4*>(qp + 32 * ks + 4), &ahi[mt][ks], &alo[mt][ks]);
+      split8(q4sum(qp + 32 * ks), q4sum(qp + 32 * ks + 4), &ahi[mt][ks], &alo[mt][ks]);
   }
   v4f acc[2][8] = {};
   const uint16_t* bp = ukt + ((size_t)h * DL + 128 * wave + l16) * DN + 8 * q4;
@@ -719,8 +742,13 @@ __global__ __launch_bounds__(256) void mla_qabsorb_kernel(
     int seq;
     const int pos = token_pos(cached_len, t, n_new, max_len, &seq);
     const float* qp = q + (size_t)t * qld + h * (DN + DR) + DN;
+    float qa = qp[2 * pr], qb = qp[2 * pr + 1];
+    for (int s = 1; s < nsplit; ++s) {
+      qa += qp[s * slice + 2 * pr];
+      qb += qp[s * slice + 2 * pr + 1];
+    }
     float ra, rb;
-    rope_pair(qp[2 * pr], qp[2 * pr + 1], pos, inv_freq[pr], &ra, &rb);
+    rope_pair(qa, qb, pos, inv_freq[pr], &ra, &rb);
     float* dst = qcat + ((size_t)t * H + h) * DQ + DL;
     dst[2 * pr] = ra * smscale;
     dst[2 * pr + 1] = rb * smscale;
@@ -875,12 +903,13 @@ hipError_t launch_slice_sum(int T, int ncol, int ld, int nsplit, const float* pa
   return hipGetLastError();
 }
 
-hipError_t launch_mla_latent(int T, int q_lora, int qkv_ld, float eps, const float* qkv,
-                             const uint16_t* g_qa, const uint16_t* g_kva, const double* inv_freq,
-                             const int32_t* cached_len, int n_new, int max_len, uint8_t* qa_q,
-                             float* qa_s, uint8_t* c_codes, float* c_scales, uint16_t* c_rope,
-                             hipStream_t s) {
-  mla_latent_kernel<<<T, 256, 0, s>>>(q_lora, qkv_ld, eps, qkv, g_qa, g_kva, inv_freq,
+hipError_t launch_mla_latent(int T, int nsplit, int q_lora, int qkv_ld, float eps,
+                             const float* qkv, const uint16_t* g_qa, const uint16_t* g_kva,
+                             const double* inv_freq, const int32_t* cached_len, int n_new,
+                             int max_len, uint8_t* qa_q, float* qa_s, uint8_t* c_codes,
+                             float* c_scales, uint16_t* c_rope, hipStream_t s) {
+  if (q_lora + DL + DR > MAX_QKV) return hipErrorInvalidValue;
+  mla_latent_kernel<<<T, 256, 0, s>>>(T, nsplit, q_lora, qkv_ld, eps, qkv, g_qa, g_kva, inv_freq,
                                       cached_len, n_new, max_len, qa_q, qa_s, c_codes, c_scales,
                                       c_rope);
   return hipGetLastError();
@@ -892,13 +921,13 @@ hipError_t launch_mla_pack_ukv(int H, const uint8_t* w_kvb, uint16_t* ukt, uint1
   return hipGetLastError();
 }
 
-hipError_t launch_mla_qabsorb(int T, int H, float smscale, const float* q, const uint16_t* ukt,
-                              const float* s_kvb, const double* inv_freq,
+hipError_t launch_mla_qabsorb(int T, int H, int nsplit, float smscale, const float* q,
+                              const uint16_t* ukt, const float* s_kvb, const double* inv_freq,
                               const int32_t* cached_len, int n_new, int max_len, float* qcat,
                               hipStream_t s) {
   dim3 grid(H, (T + QA_TB - 1) / QA_TB);
-  mla_qabsorb_kernel<<<grid, 256, 0, s>>>(T, H, smscale, q, ukt, s_kvb, inv_freq, cached_len,
-                                          n_new, max_len, qcat);
+  mla_qabsorb_kernel<<<grid, 256, 0, s>>>(T, H, nsplit, smscale, q, ukt, s_kvb, inv_freq,
+                                          cached_len, n_new, max_len, qcat);
   return hipGetLastError();
 }
 

@@ -143,6 +143,8 @@ MPacked packed_layout(const MDims& D) {
 // the next projection match an exact evaluation), K slices to fill the chip
 int gemm_tt(int T) { return T <= 16 ? 1 : T <= 32 ? 2 : 4; }
 
+constexpr int QKV_FUSE_MAX = 2;   // most [q_a; kv_a] K slices the latent kernel adds itself
+
 int gemm_split(int T, int N, int K) {
   const int bm = 16 * gemm_tt(T);
   const int items = ((T + bm - 1) / bm) * (N / 256);
@@ -171,7 +173,7 @@ void attn_split(int T, int H, int n_seq, int n_new, int max_len, int* nsplit, in
 }
 
 struct MLayout {
-  size_t hbuf, xq, xs, offsets, mt_start, tile_group, part, qkv, qa_q, qa_s, q, qcat, part_o,
+  size_t hbuf, xq, xs, offsets, mt_start, tile_group, part, qkv, qa_q, qa_s, qcat, part_o,
       part_ml, o_q, o_s, total;
   int ns_qkv, ns_qb, ns_o, ns_attn, chunk;
 };
@@ -199,10 +201,12 @@ MLayout ws_layout(const MDims& D, int S, int n, int L) {
   const size_t part_elems = std::max({(size_t)w.ns_qkv * T * D.n_qkv_pad,
                                       (size_t)w.ns_qb * T * D.n_qb, (size_t)w.ns_o * T * D.n_o});
   w.part = take(part_elems * 4);
-  w.qkv = take(T * D.n_qkv_pad * 4);
+  // the [q_a; kv_a] K slices are summed by a separate launch when there are
+  // many of them (small batches: the latent kernel has one workgroup per
+  // token, too few to wait on many slices); otherwise in the latent kernel
+  w.qkv = w.ns_qkv > QKV_FUSE_MAX ? take(T * D.n_qkv_pad * 4) : 0;
   w.qa_q = take(T * D.ql);
   w.qa_s = take(T * (D.ql / 128) * 4);
-  w.q = take(T * D.n_qb * 4);
   w.qcat = take(T * D.H * (D.kv + D.rope) * 4);
   w.part_o = take((size_t)w.ns_attn * T * D.H * D.kv * 4);
   w.part_ml = take((size_t)w.ns_attn * T * D.H * 2 * 4);
@@ -224,9 +228,6 @@ moe_status run_gemm(const MDims& D, int T, int N, int K, int nsplit, const uint8
                     float* out, hipStream_t s) {
   const int tt = gemm_tt(T);
   const int bm = 16 * tt;
-  M_HIP(k2::launch_dense_tiles(T, bm, const_cast<int32_t*>(offsets),
-                               const_cast<int32_t*>(mt_start), const_cast<int32_t*>(tile_group),
-                               s));
   k2::GemmArgs a{};
   a.wpk = wcodes;
   a.expert_stride = 0;
@@ -298,10 +299,8 @@ moe_status run_mla(const mla_config* cfg, int32_t S, int32_t n, int32_t L, const
   int32_t* mt_start = at<int32_t>(ws, W.mt_start);
   int32_t* tile_group = at<int32_t>(ws, W.tile_group);
   float* part = at<float>(ws, W.part);
-  float* qkv = at<float>(ws, W.qkv);
   uint8_t* qa_q = at<uint8_t>(ws, W.qa_q);
   float* qa_s = at<float>(ws, W.qa_s);
-  float* q = at<float>(ws, W.q);
   float* qcat = at<float>(ws, W.qcat);
   float* part_o = at<float>(ws, W.part_o);
   float* part_ml = at<float>(ws, W.part_ml);
@@ -317,18 +316,26 @@ moe_status run_mla(const mla_config* cfg, int32_t S, int32_t n, int32_t L, const
     // input RMSNorm + 1x128 quantisation
     M_HIP(k2::launch_norm_quant(true, T, D.d, D.eps, x, norm_w, at<void>(ws, W.hbuf), xq, xs,
                                 s));
+    // the projections' work tables: one group of T rows in m-tiles of
+    // 16 gemm_tt(T) rows (the same for all three projections)
+    M_HIP(k2::launch_dense_tiles((int)T, 16 * gemm_tt((int)T), offsets, mt_start, tile_group,
+                                 s));
     // [q_a; kv_a] = h [W_qa; W_kva]^T
     if ((st = run_gemm(D, T, D.n_qkv_pad, D.d, W.ns_qkv, xq, xs, pk + P.qkv_codes,
                        reinterpret_cast<const float*>(pk + P.qkv_scales), offsets, mt_start,
                        tile_group, part, s)) != MOE_OK)
       return st;
-    M_HIP(k2::launch_slice_sum(T, D.n_qkv_pad, D.n_qkv_pad, W.ns_qkv, part, nullptr, qkv,
-                               D.n_qkv_pad, s));
+    if (W.ns_qkv > QKV_FUSE_MAX)
+      M_HIP(k2::launch_slice_sum(T, D.n_qkv_pad, D.n_qkv_pad, W.ns_qkv, part, nullptr,
+                                 at<float>(ws, W.qkv), D.n_qkv_pad, s));
   }
   {
     k2::ProfileScope ps(MOE_STAGE_MLA_LATENT, s);
-    // latent norms, query-latent codes, cache entries
-    M_HIP(k2::launch_mla_latent(T, D.ql, D.n_qkv_pad, D.eps, qkv,
+    // latent norms, query-latent codes, cache entries (few K slices of the
+    // projection are added in the kernel)
+    const bool fused = W.ns_qkv <= QKV_FUSE_MAX;
+    M_HIP(k2::launch_mla_latent(T, fused ? W.ns_qkv : 1, D.ql, D.n_qkv_pad, D.eps,
+                                fused ? part : at<float>(ws, W.qkv),
                                 reinterpret_cast<const uint16_t*>(pk + P.g_qa),
                                 reinterpret_cast<const uint16_t*>(pk + P.g_kva), freq,
                                 cached_len, n, L, qa_q, qa_s, static_cast<uint8_t*>(cache_codes),
@@ -341,13 +348,13 @@ moe_status run_mla(const mla_config* cfg, int32_t S, int32_t n, int32_t L, const
                        reinterpret_cast<const float*>(pk + P.qb_scales), offsets, mt_start,
                        tile_group, part, s)) != MOE_OK)
       return st;
-    M_HIP(k2::launch_slice_sum(T, D.n_qb, D.n_qb, W.ns_qb, part, nullptr, q, D.n_qb, s));
   }
   {
     k2::ProfileScope ps(MOE_STAGE_MLA_LATENT, s);
     // absorbed queries
-    M_HIP(k2::launch_mla_qabsorb(T, D.H, D.smscale, q, ukt, kvbs, freq, cached_len, n, L, qcat,
-                                 s));
+    // (the q_b projection's K-slice partial sums are added in the kernel)
+    M_HIP(k2::launch_mla_qabsorb(T, D.H, W.ns_qb, D.smscale, part, ukt, kvbs, freq, cached_len,
+                                 n, L, qcat, s));
   }
   {
     k2::ProfileScope ps(MOE_STAGE_MLA_ATTN, s);

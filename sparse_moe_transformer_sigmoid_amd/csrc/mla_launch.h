@@ -22,16 +22,19 @@ hipError_t launch_gemm_dense(int tt, int nsplit, const GemmArgs& a, int grid, hi
 // sum of K slices, optionally + bf16 residual and rounding to bf16
 hipError_t launch_slice_sum(int T, int ncol, int ld, int nsplit, const float* part,
                             const uint16_t* residual, void* out, int out_ld, hipStream_t s);
-hipError_t launch_mla_latent(int T, int q_lora, int qkv_ld, float eps, const float* qkv,
-                             const uint16_t* g_qa, const uint16_t* g_kva, const double* inv_freq,
-                             const int32_t* cached_len, int n_new, int max_len, uint8_t* qa_q,
-                             float* qa_s, uint8_t* c_codes, float* c_scales, uint16_t* c_rope,
-                             hipStream_t s);
+// qkv: nsplit K-slice partial sums [nsplit, T, qkv_ld] of the [q_a; kv_a] projection
+hipError_t launch_mla_latent(int T, int nsplit, int q_lora, int qkv_ld, float eps,
+                             const float* qkv, const uint16_t* g_qa, const uint16_t* g_kva,
+                             const double* inv_freq, const int32_t* cached_len, int n_new,
+                             int max_len, uint8_t* qa_q, float* qa_s, uint8_t* c_codes,
+                             float* c_scales, uint16_t* c_rope, hipStream_t s);
 // bf16 copies of the key-value up-projection's codes: ukt [H][512][128] (key
 // rows transposed), uv [H][128][512] (value rows)
 hipError_t launch_mla_pack_ukv(int H, const uint8_t* w_kvb, uint16_t* ukt, uint16_t* uv,
                               hipStream_t s);
-hipError_t launch_mla_qabsorb(int T, int H, float smscale, const float* q, const uint16_t* ukt,
+// q: nsplit K-slice partial sums [nsplit, T, H * 192] of the q_b projection
+hipError_t launch_mla_qabsorb(int T, int H, int nsplit, float smscale, const float* q,
+                              const uint16_t* ukt,
                               const float* s_kvb, const double* inv_freq,
                               const int32_t* cached_len, int n_new, int max_len, float* qcat,
                               hipStream_t s);
