@@ -35,7 +35,10 @@ namespace k2 {
 
 namespace {
 
-constexpr int TK = 32;       // K per step
+constexpr int TK = 32;       // K per MFMA, per wgrad step and per K block of the blocked layouts
+constexpr int TKR = 64;      // K per step of the row-tiled products (each A row's 128-byte line
+                             // is read whole, as two 16-byte halves per lane)
+constexpr int BR_LD = TKR + 8;   // bf16 stride of a staged row-tiled B row (144 bytes)
 constexpr int TN = 128;      // N per workgroup (rows of a group, or input features)
 constexpr int TMW = 64;      // M rows per wave
 constexpr int B_LD = TK + 8;  // bf16 stride of a staged B row (80 bytes: conflict-free)
@@ -122,7 +125,7 @@ __device__ __forceinline__ TileWork decode_wgrad(const TrainGemmArgs& g) {
 
 template <int MODE>
 __global__ __launch_bounds__(256, 2) void train_gemm_kernel(const TrainGemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint16_t bs[2][TN * B_LD];
+  __shared__ __attribute__((aligned(16))) uint16_t bs[2][TN * BR_LD];
   __shared__ float red[4 * 8 * 16 * 2];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -135,7 +138,7 @@ __global__ __launch_bounds__(256, 2) void train_gemm_kernel(const TrainGemmArgs 
   const int grp = wi.grp;
 
   // ---- operand row pointers
-  const int nks = g.K / TK;   // K steps
+  const int nks = g.K / TKR;   // K steps
   const uint16_t* arow[4];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
@@ -152,7 +155,8 @@ __global__ __launch_bounds__(256, 2) void train_gemm_kernel(const TrainGemmArgs 
     // s * lda + 32 r (lda = rows * 32); otherwise row-major with stride lda
     arow[mt] = base + row * (size_t)(KBLK_A ? TK : g.lda) + 8 * q4;
   }
-  // B rows staged by this thread: tile rows tid/4 and tid/4 + 64, 8 K each
+  // B rows staged by this thread: tile rows tid/4 and tid/4 + 64, K chunks
+  // (tid % 4) and (tid % 4) + 4 of 8 each
   const uint16_t* brow[2];
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
@@ -175,46 +179,62 @@ __global__ __launch_bounds__(256, 2) void train_gemm_kernel(const TrainGemmArgs 
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) acc[mt][nt] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  v4i abuf[2][4];
-  v4i breg[2];
-  auto load_a = [&](v4i (&a)[4], int s) {
+  // A: K halves kh = 0, 1 of a step (32 K each; K-blocked: blocks 2s + kh).
+  // One register set per half: a half is reloaded with the next step's as
+  // soon as its MFMAs are issued, one half-step (32 MFMAs) ahead of its use.
+  v4i abuf[2][4];   // [kh][mt]
+  v4i breg[2][2];
+  auto load_a = [&](int kh, int s) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
-      a[mt] = *reinterpret_cast<const v4i*>(arow[mt] + (size_t)s * (KBLK_A ? g.lda : TK));
+      abuf[kh][mt] = *reinterpret_cast<const v4i*>(
+          arow[mt] + (KBLK_A ? (size_t)(2 * s + kh) * g.lda : (size_t)s * TKR + TK * kh));
   };
   auto load_b = [&](int s) {
 #pragma unroll
-    for (int c = 0; c < 2; ++c) breg[c] = *reinterpret_cast<const v4i*>(brow[c] + (size_t)s * TK);
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        breg[c][h] = *reinterpret_cast<const v4i*>(brow[c] + (size_t)s * TKR + 32 * h);
   };
   auto store_b = [&](int buf) {
 #pragma unroll
     for (int c = 0; c < 2; ++c)
-      *reinterpret_cast<v4i*>(&bs[buf][((tid >> 2) + 64 * c) * B_LD + 8 * (tid & 3)]) = breg[c];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        *reinterpret_cast<v4i*>(&bs[buf][((tid >> 2) + 64 * c) * BR_LD + 8 * (tid & 3) + 32 * h]) =
+            breg[c][h];
   };
-  auto compute = [&](const v4i (&a)[4], int buf) {
+  auto compute = [&](int kh, int buf) {
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) {
-      const v8bf b = __builtin_bit_cast(
-          v8bf, *reinterpret_cast<const v4i*>(&bs[buf][(16 * nt + l16) * B_LD + 8 * q4]));
+      const v8bf b = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(
+                                                  &bs[buf][(16 * nt + l16) * BR_LD + TK * kh + 8 * q4]));
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
-        acc[mt][nt] = mfma16(__builtin_bit_cast(v8bf, a[mt]), b, acc[mt][nt]);
+        acc[mt][nt] = mfma16(__builtin_bit_cast(v8bf, abuf[kh][mt]), b, acc[mt][nt]);
     }
   };
 
   if (nks > 0) {
     load_b(0);
-    load_a(abuf[0], 0);
+    load_a(0, 0);
+    load_a(1, 0);
     store_b(0);
     __syncthreads();
-    // step s: prefetch B of s+1 and A of s+1, compute s from LDS buffer
-    // s & 1 and A ring slot s & 1, stage B of s+1 into the other buffer
+    // step s from LDS buffer s & 1: prefetch B of s+1; per K half, its
+    // MFMAs, then the half's A of s+1; stage B of s+1 into the other buffer
     auto step = [&](const int j, const int s) {
       const int sn = min(s + 1, nks - 1);
       load_b(sn);
-      load_a(abuf[j ^ 1], sn);
       __builtin_amdgcn_sched_barrier(0);
-      compute(abuf[j], j);
+      compute(0, j);
+      __builtin_amdgcn_sched_barrier(0);
+      load_a(0, sn);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(1, j);
+      __builtin_amdgcn_sched_barrier(0);
+      load_a(1, sn);
       store_b(j ^ 1);
       __syncthreads();
     };
