@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIBDIR = os.path.join(PKG, "lib")
 LIBNAME = "libk2moe.so"
 SOURCES = ["abi.hip", "norm_router.hip", "permute.hip", "gemm_fp8.hip", "gemm_fp8_wide.hip",
-           "gemm_f32.hip", "combine_pack.hip", "mla.hip", "mla_abi.hip", "balance.hip",
+           "gemm_f32.hip", "combine_pack.hip", "mla.hip", "mla_mha.hip", "mla_abi.hip", "balance.hip",
            "train.hip"]
 # per-source extra flags: the wide gate/up GEMM is scheduled to minimise registers,
 # which lets it keep two token tiles in flight at 2 waves/SIMD without spilling

@@ -21,39 +21,19 @@
 #include <math.h>
 
 #include "k2_common.h"
+#include "mla_common.h"
 #include "mla_launch.h"
 
 namespace k2 {
 
 namespace {
 
-constexpr int DL = 512;           // latent width (kv_lora)
-constexpr int DR = 64;            // rotary width
-constexpr int DQ = DL + DR;       // absorbed query / cache row width
-constexpr int DN = 128;           // query/key features without position (qk_nope)
-constexpr int DV = 128;           // value features (v_head)
 constexpr int PT = 32;            // cache positions per attention step
 constexpr int CT_LD = DL + 8;     // bf16 stride of a row-major cache latent in LDS
 // bf16 stride of a transposed latent row in LDS: 18 dwords, so the four
 // 16-row chunks a fill wave writes in one instruction fall on two bank halves
 // and the 16 rows a compute wave reads on 16 distinct even banks
 constexpr int TR_LD = PT + 4;
-
-typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
-typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
-typedef float v2f __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ uint16_t bf16_bits(float f) { return (uint16_t)f32_to_bf16_rne(f); }
-
-__device__ __forceinline__ __bf16 to_bf16(float f) {
-  return __builtin_bit_cast(__bf16, bf16_bits(f));
-}
-
-// e4m3 code -> float (exact)
-__device__ __forceinline__ float e4m3_val(uint32_t code) {
-  const v2f p = __builtin_amdgcn_cvt_pk_f32_fp8((int)code, false);
-  return p[0];
-}
 
 // ------------------------------------------------------------------ packing
 // [n0 rows of src0; n1 rows of src1; zero rows] x K codes -> the grouped GEMM's
@@ -135,21 +115,6 @@ __global__ __launch_bounds__(256) void slice_sum_kernel(int T, int ncol, int ld,
 }
 
 // ------------------------------------------------------- latents and cache
-__device__ __forceinline__ int token_pos(const int32_t* cached_len, int t, int n_new,
-                                        int max_len, int* seq) {
-  *seq = t / n_new;
-  const int p = cached_len[*seq] + t % n_new;
-  return min(max(p, 0), max_len - 1);
-}
-
-// rotate (a, b) by pos * f in double, round to fp32
-__device__ __forceinline__ void rope_pair(float a, float b, int pos, double f, float* ra,
-                                          float* rb) {
-  double sn, cs;
-  sincos((double)pos * f, &sn, &cs);
-  *ra = (float)((double)a * cs - (double)b * sn);
-  *rb = (float)((double)a * sn + (double)b * cs);
-}
 
 // Per token: RMSNorm of the query latent -> bf16 -> 1x128 codes (the input of
 // the query up-projection); RMSNorm of the key-value latent -> bf16 -> 1x128
@@ -166,7 +131,8 @@ __global__ __launch_bounds__(256) void mla_latent_kernel(
     const uint16_t* __restrict__ g_qa, const uint16_t* __restrict__ g_kva,
     const double* __restrict__ inv_freq, const int32_t* __restrict__ cached_len, int n_new,
     int max_len, uint8_t* __restrict__ qa_q, float* __restrict__ qa_s,
-    uint8_t* __restrict__ c_codes, float* __restrict__ c_scales, uint16_t* __restrict__ c_rope) {
+    uint8_t* __restrict__ c_codes, float* __restrict__ c_scales, uint16_t* __restrict__ c_rope,
+    double* __restrict__ rot) {
   const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int seq;
   const int pos = token_pos(cached_len, t, n_new, max_len, &seq);
@@ -216,11 +182,17 @@ __global__ __launch_bounds__(256) void mla_latent_kernel(
   quant_block(row + q_lora + wave * QBLK, g_kva + wave * QBLK, rc,
               c_codes + cidx * DL + wave * QBLK, c_scales + cidx * (DL / QBLK) + wave);
   if (tid < DR / 2) {
+    double sn, cs;
+    sincos((double)pos * inv_freq[tid], &sn, &cs);
     float ra, rb;
-    rope_pair(row[q_lora + DL + 2 * tid], row[q_lora + DL + 2 * tid + 1], pos, inv_freq[tid],
-              &ra, &rb);
+    rope_apply(row[q_lora + DL + 2 * tid], row[q_lora + DL + 2 * tid + 1], cs, sn, &ra, &rb);
     c_rope[cidx * DR + 2 * tid] = bf16_bits(ra);
     c_rope[cidx * DR + 2 * tid + 1] = bf16_bits(rb);
+    // the token's rotation of pair tid, for the queries of the per-head form
+    if (rot) {
+      rot[((size_t)t * (DR / 2) + tid) * 2] = cs;
+      rot[((size_t)t * (DR / 2) + tid) * 2 + 1] = sn;
+    }
   }
 }
 
@@ -274,60 +246,10 @@ __device__ __forceinline__ float xor8(float v) {
       0, __builtin_bit_cast(int, v), 0x128 /* row_ror:8 */, 0xF, 0xF, false));
 }
 
-__device__ __forceinline__ v4f mfma_bf16(v8bf a, v8bf b, v4f c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-// two fp32 values -> packed bf16 (a low), round to nearest even (gfx950's
-// converter)
-__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-  typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){a, b}, v2bf));
-}
-// the bf16 high parts of (a, b) (lo = 0) or the bf16 roundings of their
-// remainders a - high (lo = 1; exact in fp32), packed
-__device__ __forceinline__ uint32_t bf16_half2(float a, float b, float lo) {
-  const uint32_t hb = pack_bf16(a, b);
-  return pack_bf16(fmaf(-lo, __uint_as_float(hb << 16), a),
-                   fmaf(-lo, __uint_as_float(hb & 0xFFFF0000u), b));
-}
-
 constexpr int CT_ELEMS = PT * CT_LD, TR_ELEMS = DL * TR_LD;
 constexpr int HPW = 8;   // heads per wave
 constexpr int AW = 8;    // waves per workgroup
 constexpr int NS = 3;    // LDS stages of raw cache bytes (copies run NS - 1 steps ahead)
-
-// Direct global -> LDS copies (global_load_lds_dword / _dwordx4): lane l's 4
-// or 16 bytes from global [base + voff] land at LDS byte address M0 + l *
-// size.  They complete in issue order with the other vector loads (vmcnt);
-// the compiler does not track them, so the kernel waits for them itself.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-__device__ __forceinline__ void lds_copy16(const void* base, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               : : "v"(voff), "s"(base), "s"(lds) : "memory", "m0");
-}
-__device__ __forceinline__ void lds_copy4(const void* base, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
-               : : "v"(voff), "s"(base), "s"(lds) : "memory", "m0");
-}
-// wait until at most n (wave-uniform, 0..9) of this wave's vector loads are
-// outstanding
-__device__ __forceinline__ void vm_wait(int n) {
-  switch (n) {
-    case 0: asm volatile("s_waitcnt vmcnt(0)" : : : "memory"); break;
-    case 1: asm volatile("s_waitcnt vmcnt(1)" : : : "memory"); break;
-    case 2: asm volatile("s_waitcnt vmcnt(2)" : : : "memory"); break;
-    case 3: asm volatile("s_waitcnt vmcnt(3)" : : : "memory"); break;
-    case 4: asm volatile("s_waitcnt vmcnt(4)" : : : "memory"); break;
-    case 5: asm volatile("s_waitcnt vmcnt(5)" : : : "memory"); break;
-    case 6: asm volatile("s_waitcnt vmcnt(6)" : : : "memory"); break;
-    case 7: asm volatile("s_waitcnt vmcnt(7)" : : : "memory"); break;
-    case 8: asm volatile("s_waitcnt vmcnt(8)" : : : "memory"); break;
-    default: asm volatile("s_waitcnt vmcnt(9)" : : : "memory"); break;
-  }
-}
 
 __global__ __launch_bounds__(512, 1) void mla_attn_kernel(const AttnArgs g) {
   // raw stages: codes [pos][512] with the 16-byte chunk c of position p at
@@ -637,36 +559,28 @@ __global__ __launch_bounds__(512, 1) void mla_attn_kernel(const AttnArgs g) {
 
 // e4m3 codes of the key-value up-projection (per head: 128 key rows, 128
 // value rows, 512 latents) -> bf16 copies: ukt[h][r][d] = W_uk[d][r] (the
-// key rows transposed, so a latent's 128 weights are contiguous) and
-// uv[h][d][r] = W_uv[d][r].
+// key rows transposed, so a latent's 128 weights are contiguous),
+// uv[h][d][r] = W_uv[d][r] and uk[h][d][r] = W_uk[d][r].
 __global__ __launch_bounds__(256) void mla_pack_ukv_kernel(int H, const uint8_t* __restrict__ w_kvb,
                                                            uint16_t* __restrict__ ukt,
-                                                           uint16_t* __restrict__ uv) {
+                                                           uint16_t* __restrict__ uv,
+                                                           uint16_t* __restrict__ uk) {
   const size_t n = (size_t)H * DN * DL;
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < 2 * n;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < 3 * n;
        i += (size_t)gridDim.x * 256) {
-    const bool key = i < n;
-    const size_t j = key ? i : i - n;
+    const int part = (int)(i / n);
+    const size_t j = i - part * n;
     const int h = (int)(j / (DN * DL)), rem = (int)(j % (DN * DL));
-    if (key) {
+    if (part == 0) {
       const int r = rem / DN, d = rem % DN;   // output [h][r][d]
       const float v = e4m3_val(w_kvb[((size_t)h * (DN + DV) + d) * DL + r]);
       ukt[j] = (uint16_t)(__float_as_uint(v) >> 16);
     } else {
       const int d = rem / DL, r = rem % DL;   // output [h][d][r]
-      const float v = e4m3_val(w_kvb[((size_t)h * (DN + DV) + DN + d) * DL + r]);
-      uv[j] = (uint16_t)(__float_as_uint(v) >> 16);
+      const float v = e4m3_val(w_kvb[((size_t)h * (DN + DV) + (part == 1 ? DN : 0) + d) * DL + r]);
+      (part == 1 ? uv : uk)[j] = (uint16_t)(__float_as_uint(v) >> 16);
     }
   }
-}
-
-// eight fp32 values -> their bf16 high parts (hi) and remainder roundings (lo)
-__device__ __forceinline__ void split8(const float4 a, const float4 b, v8bf* hi, v8bf* lo) {
-  const uint4 h = make_uint4(pack_bf16(a.x, a.y), pack_bf16(a.z, a.w), pack_bf16(b.x, b.y),
-                             pack_bf16(b.z, b.w));
-  *hi = __builtin_bit_cast(v8bf, h);
-  *lo = __builtin_bit_cast(v8bf, make_uint4(bf16_half2(a.x, a.y, 1.f), bf16_half2(a.z, a.w, 1.f),
-                                            bf16_half2(b.x, b.y, 1.f), bf16_half2(b.z, b.w, 1.f)));
 }
 
 constexpr int QA_TB = 32;   // tokens per workgroup
@@ -907,17 +821,17 @@ hipError_t launch_mla_latent(int T, int nsplit, int q_lora, int qkv_ld, float ep
                              const float* qkv, const uint16_t* g_qa, const uint16_t* g_kva,
                              const double* inv_freq, const int32_t* cached_len, int n_new,
                              int max_len, uint8_t* qa_q, float* qa_s, uint8_t* c_codes,
-                             float* c_scales, uint16_t* c_rope, hipStream_t s) {
+                             float* c_scales, uint16_t* c_rope, double* rot, hipStream_t s) {
   if (q_lora + DL + DR > MAX_QKV) return hipErrorInvalidValue;
   mla_latent_kernel<<<T, 256, 0, s>>>(T, nsplit, q_lora, qkv_ld, eps, qkv, g_qa, g_kva, inv_freq,
                                       cached_len, n_new, max_len, qa_q, qa_s, c_codes, c_scales,
-                                      c_rope);
+                                      c_rope, rot);
   return hipGetLastError();
 }
 
 hipError_t launch_mla_pack_ukv(int H, const uint8_t* w_kvb, uint16_t* ukt, uint16_t* uv,
-                              hipStream_t s) {
-  mla_pack_ukv_kernel<<<1024, 256, 0, s>>>(H, w_kvb, ukt, uv);
+                              uint16_t* uk, hipStream_t s) {
+  mla_pack_ukv_kernel<<<1024, 256, 0, s>>>(H, w_kvb, ukt, uv, uk);
   return hipGetLastError();
 }
 

@@ -107,10 +107,11 @@ std::vector<double> yarn_inv_freq(const mla_config* c) {
 }
 
 // ---- packed weights: three GEMM matrices in the grouped GEMM's down form,
-// the key-value up-projection as bf16 copies of its key rows (transposed) and
-// value rows with its block scales, the norm weights, the frequencies
+// the key-value up-projection as bf16 copies of its key rows (transposed, and
+// as they are) and value rows with its block scales, the norm weights, the
+// frequencies
 struct MPacked {
-  size_t qkv_codes, qkv_scales, qb_codes, qb_scales, o_codes, o_scales, kvb_scales, ukt, uv,
+  size_t qkv_codes, qkv_scales, qb_codes, qb_scales, o_codes, o_scales, kvb_scales, ukt, uv, uk,
       g_qa, g_kva, freq, total;
 };
 
@@ -131,6 +132,7 @@ MPacked packed_layout(const MDims& D) {
   p.kvb_scales = take((size_t)D.H * 2 * (D.kv / 128) * 4);
   p.ukt = take((size_t)D.H * D.kv * D.nope * 2);
   p.uv = take((size_t)D.H * D.v * D.kv * 2);
+  p.uk = take((size_t)D.H * D.nope * D.kv * 2);
   p.g_qa = take((size_t)D.ql * 2);
   p.g_kva = take((size_t)D.kv * 2);
   p.freq = take((size_t)(D.rope / 2) * 8);
@@ -172,10 +174,22 @@ void attn_split(int T, int H, int n_seq, int n_new, int max_len, int* nsplit, in
   *chunk = ch;
 }
 
+// Prompt-sized batches (at least MHA_MIN_NEW new tokens per sequence) attend
+// in the per-head form: forming a position's keys and values costs about as
+// much as 150 queries attending to it in the absorbed form, and each query
+// then needs 2.4x fewer MFMA products.  Its key-value buffer is bounded.
+constexpr int MHA_MIN_NEW = 128;
+constexpr size_t MHA_MAX_KV_BYTES = (size_t)1 << 34;
+
+bool use_mha(const MDims& D, int S, int n, int L) {
+  return n >= MHA_MIN_NEW && k2::mla_mha_kv_bytes(S, D.H, L) <= MHA_MAX_KV_BYTES;
+}
+
 struct MLayout {
   size_t hbuf, xq, xs, offsets, mt_start, tile_group, part, qkv, qa_q, qa_s, qcat, part_o,
-      part_ml, o_q, o_s, total;
+      part_ml, kv, rot, o_q, o_s, total;
   int ns_qkv, ns_qb, ns_o, ns_attn, chunk;
+  bool mha;
 };
 
 MLayout ws_layout(const MDims& D, int S, int n, int L) {
@@ -207,9 +221,15 @@ MLayout ws_layout(const MDims& D, int S, int n, int L) {
   w.qkv = w.ns_qkv > QKV_FUSE_MAX ? take(T * D.n_qkv_pad * 4) : 0;
   w.qa_q = take(T * D.ql);
   w.qa_s = take(T * (D.ql / 128) * 4);
-  w.qcat = take(T * D.H * (D.kv + D.rope) * 4);
-  w.part_o = take((size_t)w.ns_attn * T * D.H * D.kv * 4);
-  w.part_ml = take((size_t)w.ns_attn * T * D.H * 2 * 4);
+  w.mha = use_mha(D, S, n, L);
+  if (w.mha) {
+    w.kv = take(k2::mla_mha_kv_bytes(S, D.H, L));
+    w.rot = take(T * (D.rope / 2) * 2 * 8);
+  } else {
+    w.qcat = take(T * D.H * (D.kv + D.rope) * 4);
+    w.part_o = take((size_t)w.ns_attn * T * D.H * D.kv * 4);
+    w.part_ml = take((size_t)w.ns_attn * T * D.H * 2 * 4);
+  }
   w.o_q = take(T * D.H * D.v);
   w.o_s = take(T * D.H * 4);
   w.total = T == 0 ? 0 : off;
@@ -309,6 +329,7 @@ moe_status run_mla(const mla_config* cfg, int32_t S, int32_t n, int32_t L, const
   const double* freq = reinterpret_cast<const double*>(pk + P.freq);
   const uint16_t* ukt = reinterpret_cast<const uint16_t*>(pk + P.ukt);
   const uint16_t* uv = reinterpret_cast<const uint16_t*>(pk + P.uv);
+  const uint16_t* uk = reinterpret_cast<const uint16_t*>(pk + P.uk);
   const float* kvbs = reinterpret_cast<const float*>(pk + P.kvb_scales);
 
   {
@@ -339,7 +360,8 @@ moe_status run_mla(const mla_config* cfg, int32_t S, int32_t n, int32_t L, const
                                 reinterpret_cast<const uint16_t*>(pk + P.g_qa),
                                 reinterpret_cast<const uint16_t*>(pk + P.g_kva), freq,
                                 cached_len, n, L, qa_q, qa_s, static_cast<uint8_t*>(cache_codes),
-                                cache_scales, static_cast<uint16_t*>(cache_rope), s));
+                                cache_scales, static_cast<uint16_t*>(cache_rope),
+                                W.mha ? at<double>(ws, W.rot) : nullptr, s));
   }
   {
     k2::ProfileScope ps(MOE_STAGE_MLA_PROJ, s);
@@ -349,23 +371,34 @@ moe_status run_mla(const mla_config* cfg, int32_t S, int32_t n, int32_t L, const
                        tile_group, part, s)) != MOE_OK)
       return st;
   }
-  {
-    k2::ProfileScope ps(MOE_STAGE_MLA_LATENT, s);
-    // absorbed queries
+  if (W.mha) {
+    // per-head keys and values of every visible position, then attention
     // (the q_b projection's K-slice partial sums are added in the kernel)
-    M_HIP(k2::launch_mla_qabsorb(T, D.H, W.ns_qb, D.smscale, part, ukt, kvbs, freq, cached_len,
-                                 n, L, qcat, s));
-  }
-  {
     k2::ProfileScope ps(MOE_STAGE_MLA_ATTN, s);
-    M_HIP(k2::launch_mla_attn(T, D.H, S, n, L, W.ns_attn, W.chunk,
-                              static_cast<const uint8_t*>(cache_codes), cache_scales,
-                              static_cast<const uint16_t*>(cache_rope), qcat, cached_len, part_o,
-                              part_ml, s));
-  }
-  {
-    k2::ProfileScope ps(MOE_STAGE_MLA_VUP, s);
-    M_HIP(k2::launch_mla_vup(T, D.H, W.ns_attn, part_o, part_ml, uv, kvbs, o_q, o_s, attn, s));
+    M_HIP(k2::launch_mla_mha(T, D.H, S, n, L, W.ns_qb, D.smscale, part, at<double>(ws, W.rot),
+                             cached_len,
+                             static_cast<const uint8_t*>(cache_codes), cache_scales,
+                             static_cast<const uint16_t*>(cache_rope), uk, uv, kvbs,
+                             at<uint16_t>(ws, W.kv), o_q, o_s, attn, s));
+  } else {
+    {
+      k2::ProfileScope ps(MOE_STAGE_MLA_LATENT, s);
+      // absorbed queries
+      // (the q_b projection's K-slice partial sums are added in the kernel)
+      M_HIP(k2::launch_mla_qabsorb(T, D.H, W.ns_qb, D.smscale, part, ukt, kvbs, freq,
+                                   cached_len, n, L, qcat, s));
+    }
+    {
+      k2::ProfileScope ps(MOE_STAGE_MLA_ATTN, s);
+      M_HIP(k2::launch_mla_attn(T, D.H, S, n, L, W.ns_attn, W.chunk,
+                                static_cast<const uint8_t*>(cache_codes), cache_scales,
+                                static_cast<const uint16_t*>(cache_rope), qcat, cached_len,
+                                part_o, part_ml, s));
+    }
+    {
+      k2::ProfileScope ps(MOE_STAGE_MLA_VUP, s);
+      M_HIP(k2::launch_mla_vup(T, D.H, W.ns_attn, part_o, part_ml, uv, kvbs, o_q, o_s, attn, s));
+    }
   }
   if (!out) return MOE_OK;
   k2::ProfileScope ps(MOE_STAGE_MLA_PROJ, s);
@@ -421,7 +454,8 @@ moe_status mla_pack_weights(const mla_config* cfg, const mla_weights* w, void* p
   M_HIP(k2::launch_pack_rows(D.n_o, D.H * D.v, u8(w->w_o), D.n_o, nullptr, 0, w->s_o, nullptr,
                              base + P.o_codes, reinterpret_cast<float*>(base + P.o_scales), s));
   M_HIP(k2::launch_mla_pack_ukv(D.H, u8(w->w_kvb), reinterpret_cast<uint16_t*>(base + P.ukt),
-                                reinterpret_cast<uint16_t*>(base + P.uv), s));
+                                reinterpret_cast<uint16_t*>(base + P.uv),
+                                reinterpret_cast<uint16_t*>(base + P.uk), s));
   M_HIP(hipMemcpyAsync(base + P.kvb_scales, w->s_kvb, (size_t)D.H * 2 * (D.kv / 128) * 4,
                        hipMemcpyDeviceToDevice, s));
   M_HIP(hipMemcpyAsync(base + P.g_qa, w->g_qa, (size_t)D.ql * 2, hipMemcpyDeviceToDevice, s));

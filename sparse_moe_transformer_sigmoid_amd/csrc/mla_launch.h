@@ -22,16 +22,17 @@ hipError_t launch_gemm_dense(int tt, int nsplit, const GemmArgs& a, int grid, hi
 // sum of K slices, optionally + bf16 residual and rounding to bf16
 hipError_t launch_slice_sum(int T, int ncol, int ld, int nsplit, const float* part,
                             const uint16_t* residual, void* out, int out_ld, hipStream_t s);
-// qkv: nsplit K-slice partial sums [nsplit, T, qkv_ld] of the [q_a; kv_a] projection
+// qkv: nsplit K-slice partial sums [nsplit, T, qkv_ld] of the [q_a; kv_a] projection;
+// rot (optional) [T, 32, 2]: cosine and sine of each token's rotary angles
 hipError_t launch_mla_latent(int T, int nsplit, int q_lora, int qkv_ld, float eps,
                              const float* qkv, const uint16_t* g_qa, const uint16_t* g_kva,
                              const double* inv_freq, const int32_t* cached_len, int n_new,
                              int max_len, uint8_t* qa_q, float* qa_s, uint8_t* c_codes,
-                             float* c_scales, uint16_t* c_rope, hipStream_t s);
+                             float* c_scales, uint16_t* c_rope, double* rot, hipStream_t s);
 // bf16 copies of the key-value up-projection's codes: ukt [H][512][128] (key
-// rows transposed), uv [H][128][512] (value rows)
+// rows transposed), uv [H][128][512] (value rows), uk [H][128][512] (key rows)
 hipError_t launch_mla_pack_ukv(int H, const uint8_t* w_kvb, uint16_t* ukt, uint16_t* uv,
-                              hipStream_t s);
+                              uint16_t* uk, hipStream_t s);
 // q: nsplit K-slice partial sums [nsplit, T, H * 192] of the q_b projection
 hipError_t launch_mla_qabsorb(int T, int H, int nsplit, float smscale, const float* q,
                               const uint16_t* ukt,
@@ -58,6 +59,19 @@ hipError_t launch_mla_attn(int T, int H, int n_seq, int n_new, int max_len, int 
                            const uint16_t* c_rope, const float* qcat,
                            const int32_t* cached_len, float* part_o, float* part_ml,
                            hipStream_t s);
+// Per-head attention for prompt-sized batches (mla_mha.hip): the keys and
+// values of every visible position and head are formed from the cache into
+// kv (mla_mha_kv_bytes, nblk blocks of 32 positions per (sequence, head)),
+// then attended; rot: the new tokens' rotations from launch_mla_latent; writes
+// o_q / o_s (and attn if not null) as launch_mla_vup does.
+int mla_mha_nblk(int max_len);
+size_t mla_mha_kv_bytes(int n_seq, int H, int max_len);
+hipError_t launch_mla_mha(int T, int H, int n_seq, int n_new, int max_len, int nsplit,
+                          float smscale, const float* q, const double* rot,
+                          const int32_t* cached_len, const uint8_t* c_codes,
+                          const float* c_scales, const uint16_t* c_rope, const uint16_t* uk,
+                          const uint16_t* uv, const float* s_kvb, uint16_t* kv, uint8_t* o_q,
+                          float* o_s, float* attn, hipStream_t s);
 hipError_t launch_mla_vup(int T, int H, int nsplit, const float* part_o, const float* part_ml,
                           const uint16_t* uv, const float* s_kvb, uint8_t* o_q, float* o_s,
                           float* attn, hipStream_t s);

@@ -188,16 +188,29 @@ def test_mla_sizes_and_validation():
     cfg = _mla_cfg()
     # packed: the three GEMM matrices as FP8 codes (the stacked
     # down-projections padded to 2304 rows), the key-value up-projection as
-    # bf16 copies (2 bytes per weight), scales, norms and frequencies
+    # bf16 copies (2 bytes per weight; the key rows twice, transposed and as
+    # they are), scales, norms and frequencies
     n = lib.mla_packed_weights_bytes(C.byref(cfg))
     fp8 = 2304 * 7168 + 12288 * 1536 + 7168 * 8192
-    bf16 = 2 * 16384 * 512
+    bf16 = 2 * (16384 + 8192) * 512
     assert fp8 + bf16 < n < (fp8 + bf16) * 1.01
     nb = C.c_size_t(0)
     assert lib.mla_workspace_bytes(C.byref(cfg), 64, 1, 4097, C.byref(nb)) == L.MOE_OK
     assert nb.value > 64 * 12288 * 4
+    decode = nb.value
     assert lib.mla_workspace_bytes(C.byref(cfg), 0, 1, 4097, C.byref(nb)) == L.MOE_OK
     assert nb.value == 0
+    # prompt-sized batches (>= 128 new tokens per sequence) attend in the
+    # per-head form: keys and values of every position and head as bf16
+    # high/low halves, 1 KiB per (position, head), and no absorbed queries
+    # (64 x 576 fp32 per token); below that, the absorbed form's buffers
+    kv = 2 * 64 * 4096 * 1024
+    qcat = 64 * 576 * 4
+    assert lib.mla_workspace_bytes(C.byref(cfg), 2, 4096, 4096, C.byref(nb)) == L.MOE_OK
+    assert kv < nb.value < kv + 2 * 4096 * qcat
+    assert lib.mla_workspace_bytes(C.byref(cfg), 2, 127, 4096, C.byref(nb)) == L.MOE_OK
+    assert 2 * 127 * qcat < nb.value < kv
+    assert decode < kv
     for bad in (dict(kv_lora=256), dict(qk_rope=32), dict(n_heads=24), dict(d_model=7000)):
         c = _mla_cfg(**bad)
         assert lib.mla_packed_weights_bytes(C.byref(c)) == 0

@@ -112,6 +112,31 @@ def test_small_mla(n_seq, n_new, cached, max_len, heads, seed):
     check_mla(inp)
 
 
+def _edge_tokens(n_seq, n_new):
+    """Per sequence: the first and last new token, both ends of every 32-token
+    wave block and of every 256-token workgroup tile, and the middle."""
+    local = {0, n_new - 1, n_new // 2}
+    for b in range(0, n_new, 32):
+        local.update((b, min(b + 31, n_new - 1)))
+    return np.array(sorted(s * n_new + i for s in range(n_seq) for i in local if i < n_new))
+
+
+# Prompt-sized batches (>= 128 new tokens per sequence) attend in the per-head
+# form (keys and values formed per position and head, flash-style attention).
+@pytest.mark.parametrize("n_seq,n_new,cached,max_len,heads,seed", [
+    (2, 128, (0, 37), 192, 16, 10),             # the smallest such batch, one cached prefix
+    (1, 300, (0,), 320, 64, 11),                # 64 heads, a ragged second 256-token tile
+    (2, 150, (500, 3), 700, 32, 12),            # chunked prefill after a long prefix; idle waves
+    (3, 129, (64, 0, 31), 224, 16, 13),         # ragged lengths, a 64-position-aligned prefix
+])
+def test_small_mla_per_head_form(n_seq, n_new, cached, max_len, heads, seed):
+    _log(f"per-head mla S={n_seq} n={n_new} cached={cached} L={max_len} H={heads}")
+    shape = synth.small_mla(n_seq=n_seq, n_new=n_new, cached=cached, max_len=max_len,
+                            n_heads=heads, d_model=512 if heads <= 32 else 256)
+    inp = synth.generate_mla(shape, seed=seed, device="cuda")
+    check_mla(inp, tokens=_edge_tokens(n_seq, n_new))
+
+
 def test_small_mla_random_gamma():
     shape = synth.small_mla(n_seq=2, n_new=3, cached=(7, 40), max_len=64, gamma_std=0.1)
     inp = synth.generate_mla(shape, seed=5, device="cuda")
