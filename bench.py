@@ -225,11 +225,14 @@ def secondary_line(r, workload, sclk=None):
 def mla_line(shape, steps, warmup):
     """One MLA attention workload: whole sub-layer time (HIP events on the
     launch stream; decode replayed from a HIP graph, the eager time beside
-    it), per-stage times, and the attention kernel against its roofline.  Decode is bound by HBM: per step it must read every attended
-    cache position (656 B: 512 latent codes, 4 scales, 64 bf16 rotary
-    features) and the absorbed queries and write the latent outputs.  Prefill
-    is bound by the bf16 MFMA: 2 (576 + 512) flops per (query, head, visible
-    position)."""
+    it), per-stage times, and the attention stage against its roofline.
+    Decode (absorbed form) is bound by HBM: per step it must read every
+    attended cache position (656 B: 512 latent codes, 4 scales, 64 bf16
+    rotary features) and the absorbed queries and write the latent outputs.
+    Prompt-sized batches (>= 128 new tokens per sequence) run the per-head
+    form, bound by the bf16 MFMA: 2 (192 + 128) flops per (query, head,
+    visible position) plus 2 x 256 x 512 per (position, head) to form the keys
+    and values."""
     import numpy as np
     import torch
 
@@ -284,7 +287,24 @@ def mla_line(shape, steps, warmup):
     row_bytes = shape.kv_lora + 4 * (shape.kv_lora // 128) + 2 * shape.qk_rope
     attn_bytes = attended * row_bytes + T * H * (shape.kv_lora + shape.qk_rope) * 4 + \
         T * H * shape.kv_lora * 4
-    attn_flops = 2.0 * visible * H * ((shape.kv_lora + shape.qk_rope) + shape.kv_lora)
+    per_head = n >= 128
+    if per_head:
+        dqk, dv = shape.qk_nope + shape.qk_rope, shape.v_head
+        attn_flops = 2.0 * visible * H * (dqk + dv) + \
+            2.0 * attended * H * (shape.qk_nope + shape.v_head) * shape.kv_lora
+        # each fp32 operand enters the bf16 MFMA as high and low halves: three
+        # products per key/value feature, two per rotary one
+        mfma_flops = 2.0 * visible * H * (3 * shape.qk_nope + 2 * shape.qk_rope + 3 * dv) + \
+            2.0 * attended * H * (shape.qk_nope + shape.v_head) * shape.kv_lora
+        # cache rows in; keys and values (two bf16 halves) written and read back
+        # once; queries in, output codes out
+        attn_bytes = attended * row_bytes + \
+            2 * attended * H * (shape.qk_nope + shape.v_head) * 4 + T * H * (dqk * 4 + shape.v_head)
+        kern = "mla_kv_expand_kernel + mla_mha_kernel"
+    else:
+        attn_flops = 2.0 * visible * H * ((shape.kv_lora + shape.qk_rope) + shape.kv_lora)
+        mfma_flops = 2.0 * attn_flops
+        kern = "mla_attn_kernel"
     a_ms = stage["mla_attn"]
     w_bytes = sum(v.numel() * v.element_size() for v in inp.w.values())
     layer_bytes = w_bytes + attended * row_bytes + 2 * T * shape.d_model * 2
@@ -292,25 +312,27 @@ def mla_line(shape, steps, warmup):
             "cached_per_sequence": sorted(set(int(c) for c in cached)), "tokens": T,
             "ms_per_step": step_ms, "eager_ms_per_step": eager_ms, "launch": launch,
             "value": T / (step_ms * 1e-3), "unit": "tokens/s",
+            "form": "per-head" if per_head else "absorbed",
             "stage_ms": stage, "layer_bytes": layer_bytes,
             "layer_frac_hbm": layer_bytes / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
     ai = attn_flops / attn_bytes
     if ai < BF16_PEAK_TFLOPS * 1e3 / HBM_PEAK_GBS:
         gbs = attn_bytes / (a_ms * 1e-3) / 1e9
-        line["roofline"] = {"kernel": "mla_attn_kernel", "bound": "hbm", "achieved": gbs,
+        line["roofline"] = {"kernel": kern, "bound": "hbm", "achieved": gbs,
                             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
                             "kernel_ms": a_ms, "algorithmic_bytes": attn_bytes,
                             "algorithmic_flops": attn_flops, "arithmetic_intensity": ai}
     else:
         tf = attn_flops / (a_ms * 1e-3) / 1e12
-        line["roofline"] = {"kernel": "mla_attn_kernel", "bound": "mfma", "achieved": tf,
+        line["roofline"] = {"kernel": kern, "bound": "mfma", "achieved": tf,
                             "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                             "frac": tf / BF16_PEAK_TFLOPS, "kernel_ms": a_ms,
                             "algorithmic_bytes": attn_bytes, "algorithmic_flops": attn_flops,
                             "arithmetic_intensity": ai,
-                            "note": "bf16 MFMA peak; every product is formed as high and low "
-                                    "bf16 halves, so the executed MFMA work is twice the "
-                                    "algorithmic flops"}
+                            "executed_mfma_tflops": mfma_flops / (a_ms * 1e-3) / 1e12,
+                            "note": "bf16 MFMA peak; fp32 operands enter the MFMA as high "
+                                    "and low bf16 halves, so the executed MFMA work "
+                                    "(executed_mfma_tflops) exceeds the algorithmic flops"}
     del layer, inp, cache
     return line
 

@@ -57,6 +57,22 @@ __device__ __forceinline__ v8bf e4m3x8_bf16(uint32_t lo, uint32_t hi) {
   return v8bf{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
+// v reduced over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one column of an
+// MFMA result) by the maximum or the sum: two swaps of lane halves between two
+// copies of v (VALU, no LDS traffic), each leaving v_l and its partner's value
+// in the two results at every lane
+template <bool MAX>
+__device__ __forceinline__ float col_reduce(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  v = MAX ? fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]))
+          : __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return MAX ? fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]))
+             : __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // the sequence's cached length, clamped so that its n_new new positions stay
 // inside the cache (the caller guarantees it; a bad value then gives wrong
 // results, never an access outside the buffers)
@@ -66,76 +82,93 @@ __device__ __forceinline__ int cached_of(const int32_t* cached_len, int seq, int
 }
 
 // ------------------------------------------------------------ expansion
-// Workgroup = (sequence, head, 64 positions); wave w: keys (w < 2) or values
-// (w >= 2), features 64 (w % 2) .. + 63.  A 16x16x32 MFMA takes the weight
-// rows as one operand and the codes of 16 positions as the other; keys are
-// formed as K^T (lane: one position, 4 consecutive features), values as V
-// (lane: one feature, 4 consecutive positions), so both are stored 8 bytes
-// at a time.  Positions at or past the visible range are written as zeros
-// (the attention masks them, and zero values keep p = 0 terms finite).
+// Workgroup = (sequence, head, 64 positions), eight waves; wave w forms the
+// keys (w < 4) or values (w >= 4) of features 32 (w % 4) .. + 31 for all 64
+// positions.  The positions' codes (32 KiB) are copied once into LDS; each
+// wave streams its 32 weight rows from global memory one 32-latent step
+// ahead.  A 16x16x32 MFMA takes the weight rows as one operand and the codes
+// of 16 positions as the other; keys are formed as K^T (lane: one position,
+// 4 consecutive features), values as V (lane: one feature, 4 consecutive
+// positions), so both are stored 8 bytes at a time.  Positions at or past
+// the visible range are written as zeros (the attention masks them, and zero
+// values keep p = 0 terms finite).
+//
+// Codes in LDS: position p's 16-byte chunk c at chunk slot c ^ (p % 16), so
+// the 8-byte fragment reads of 16 consecutive positions at one latent offset
+// fall on distinct banks.
+constexpr int XW = 8;                  // waves per expand workgroup
+constexpr int XF = 32;                 // features per wave
+
 template <bool VALUES>
 __device__ __forceinline__ void expand_wave(int h, int nblk, size_t sh, int p0, int valid,
-                                            size_t cbase, const uint8_t* __restrict__ c_codes,
-                                            const float* __restrict__ c_scales,
+                                            const uint8_t* cl_s, const float* sc_s,
                                             const uint16_t* __restrict__ w,
                                             const float* __restrict__ sw, uint16_t* __restrict__ kv,
                                             int f0, int lane) {
   const int g = lane >> 4, l16 = lane & 15;
   const uint16_t* wrow = w + ((size_t)h * DN + f0 + l16) * DL + 8 * g;
-  int cpos[4];
+  // B / A fragment of positions 16 pt + l16, latents k0 + 8 g .. + 7: bytes of
+  // 16-byte chunk (k0 + 8 g) / 16, half g % 2 (k0 a multiple of 32)
+  auto cfrag = [&](int pt, int k0) {
+    const int p = 16 * pt + l16;
+    const int c = (k0 >> 4) + (g >> 1);
+    const uint2 c8 =
+        *reinterpret_cast<const uint2*>(cl_s + p * DL + 16 * (c ^ l16) + 8 * (g & 1));
+    return e4m3x8_bf16(c8.x, c8.y);
+  };
+  auto wfrag = [&](int ft, int k0) {
+    return *reinterpret_cast<const v8bf*>(wrow + (size_t)16 * ft * DL + k0);
+  };
+  v4f acc[2][4];
 #pragma unroll
-  for (int pt = 0; pt < 4; ++pt) cpos[pt] = min(p0 + 16 * pt + l16, valid - 1);
-  v4f acc[4][4];
-#pragma unroll
-  for (int ft = 0; ft < 4; ++ft)
+  for (int ft = 0; ft < 2; ++ft)
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt) acc[ft][pt] = v4f{0.f, 0.f, 0.f, 0.f};
+  v8bf wc[2], wn[2];
+  wc[0] = wfrag(0, 0);
+  wc[1] = wfrag(1, 0);
 #pragma unroll 1
   for (int b = 0; b < DL / QBLK; ++b) {
-    v4f d[4][4];
+    v4f d[2][4];
 #pragma unroll
-    for (int ft = 0; ft < 4; ++ft)
+    for (int ft = 0; ft < 2; ++ft)
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) d[ft][pt] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < QBLK / 32; ++kk) {
       const int k0 = b * QBLK + 32 * kk;
-      v8bf wf[4], cf[4];
-#pragma unroll
-      for (int ft = 0; ft < 4; ++ft)
-        wf[ft] = *reinterpret_cast<const v8bf*>(wrow + (size_t)16 * ft * DL + k0);
-#pragma unroll
-      for (int pt = 0; pt < 4; ++pt) {
-        const uint2 c8 =
-            *reinterpret_cast<const uint2*>(c_codes + (cbase + cpos[pt]) * DL + k0 + 8 * g);
-        cf[pt] = e4m3x8_bf16(c8.x, c8.y);
+      if (k0 + 32 < DL) {
+        wn[0] = wfrag(0, k0 + 32);
+        wn[1] = wfrag(1, k0 + 32);
       }
 #pragma unroll
-      for (int ft = 0; ft < 4; ++ft)
+      for (int pt = 0; pt < 4; ++pt) {
+        const v8bf cf = cfrag(pt, k0);
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt)
-          d[ft][pt] = VALUES ? mfma_bf16(cf[pt], wf[ft], d[ft][pt])
-                             : mfma_bf16(wf[ft], cf[pt], d[ft][pt]);
+        for (int ft = 0; ft < 2; ++ft)
+          d[ft][pt] = VALUES ? mfma_bf16(cf, wc[ft], d[ft][pt]) : mfma_bf16(wc[ft], cf, d[ft][pt]);
+      }
+      if (k0 + 32 < DL) {
+        wc[0] = wn[0];
+        wc[1] = wn[1];
+      }
     }
     const float s_w = sw[b];
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt) {
       if constexpr (VALUES) {
         // lane: feature f0 + 16 ft + l16, positions 16 pt + 4 g + i
-        float sc[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          sc[i] = c_scales[(cbase + min(p0 + 16 * pt + 4 * g + i, valid - 1)) * (DL / QBLK) + b] *
-                  s_w;
+        for (int i = 0; i < 4; ++i) {
+          const float sc = sc_s[(16 * pt + 4 * g + i) * (DL / QBLK) + b] * s_w;
 #pragma unroll
-        for (int ft = 0; ft < 4; ++ft)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[ft][pt][i] += d[ft][pt][i] * sc[i];
+          for (int ft = 0; ft < 2; ++ft) acc[ft][pt][i] += d[ft][pt][i] * sc;
+        }
       } else {
         // lane: position 16 pt + l16, features f0 + 16 ft + 4 g + i
-        const float sc = c_scales[(cbase + cpos[pt]) * (DL / QBLK) + b] * s_w;
+        const float sc = sc_s[(16 * pt + l16) * (DL / QBLK) + b] * s_w;
 #pragma unroll
-        for (int ft = 0; ft < 4; ++ft) acc[ft][pt] += d[ft][pt] * sc;
+        for (int ft = 0; ft < 2; ++ft) acc[ft][pt] += d[ft][pt] * sc;
       }
     }
   }
@@ -146,7 +179,7 @@ __device__ __forceinline__ void expand_wave(int h, int nblk, size_t sh, int p0, 
       uint16_t* blk = kv + (sh * nblk + pb / XB) * XBLK;
       const int r = pb % XB;
 #pragma unroll
-      for (int ft = 0; ft < 4; ++ft) {
+      for (int ft = 0; ft < 2; ++ft) {
         const int f = f0 + 16 * ft + l16;
         v4f v = acc[ft][pt];
 #pragma unroll
@@ -162,7 +195,7 @@ __device__ __forceinline__ void expand_wave(int h, int nblk, size_t sh, int p0, 
       uint16_t* blk = kv + (sh * nblk + p / XB) * XBLK;
       const int r = p % XB;
 #pragma unroll
-      for (int ft = 0; ft < 4; ++ft) {
+      for (int ft = 0; ft < 2; ++ft) {
         const int f = f0 + 16 * ft + 4 * g;
         v4f v = acc[ft][pt];
         if (p >= valid) v = v4f{0.f, 0.f, 0.f, 0.f};
@@ -175,28 +208,44 @@ __device__ __forceinline__ void expand_wave(int h, int nblk, size_t sh, int p0, 
   }
 }
 
-// grid: S * H * (nblk / 2) workgroups of 256 threads; nblk = padded length / 32
+// grid: S * H * (nblk / 2) workgroups of 512 threads; nblk = padded length / 32
 // (even).  kv: per (sequence, head), nblk blocks of XBLK bf16.
-__global__ __launch_bounds__(256) void mla_kv_expand_kernel(
+__global__ __launch_bounds__(512, 4) void mla_kv_expand_kernel(
     int H, int n_new, int max_len, int nblk, const int32_t* __restrict__ cached_len,
     const uint8_t* __restrict__ c_codes, const float* __restrict__ c_scales,
     const uint16_t* __restrict__ uk, const uint16_t* __restrict__ uv,
     const float* __restrict__ s_kvb, uint16_t* __restrict__ kv) {
+  __shared__ __attribute__((aligned(16))) uint8_t cl_s[XP * DL];
+  __shared__ float sc_s[XP * (DL / QBLK)];
   const int per = nblk / 2;
   const int sh = blockIdx.x / per, pb = blockIdx.x % per;
   const int seq = sh / H, h = sh % H;
   const int valid = cached_of(cached_len, seq, n_new, max_len) + n_new;
   const int p0 = pb * XP;
   if (p0 >= valid) return;   // never read: the attention stops at the last visible block
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const size_t cbase = (size_t)seq * max_len;
-  const float* sw = s_kvb + (size_t)(2 * h + (wave >> 1)) * (DL / QBLK);
-  if (wave < 2)
-    expand_wave<false>(h, nblk, (size_t)sh, p0, valid, cbase, c_codes, c_scales, uk, sw, kv,
-                       64 * wave, lane);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint8_t* codes = c_codes + (size_t)seq * max_len * DL;
+  // codes of positions p0 .. p0 + 63 (clamped to the visible range): wave w
+  // copies positions 8 w .. 8 w + 7, two per instruction
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int p = 8 * wave + 2 * i + (lane >> 5);
+    const int c = (lane & 31) ^ (p & 15);
+    lds_copy16(codes, (uint32_t)(min(p0 + p, valid - 1) * DL + 16 * c),
+               lds_addr(cl_s + (8 * wave + 2 * i) * DL));
+  }
+  if (tid < XP * (DL / QBLK))
+    sc_s[tid] = c_scales[((size_t)seq * max_len + min(p0 + tid / (DL / QBLK), valid - 1)) *
+                             (DL / QBLK) + tid % (DL / QBLK)];
+  asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
+  __syncthreads();
+  const float* sw = s_kvb + (size_t)(2 * h + (wave >> 2)) * (DL / QBLK);
+  if (wave < 4)
+    expand_wave<false>(h, nblk, (size_t)sh, p0, valid, cl_s, sc_s, uk, sw, kv, XF * wave, lane);
   else
-    expand_wave<true>(h, nblk, (size_t)sh, p0, valid, cbase, c_codes, c_scales, uv, sw, kv,
-                      64 * (wave - 2), lane);
+    expand_wave<true>(h, nblk, (size_t)sh, p0, valid, cl_s, sc_s, uv, sw, kv, XF * (wave - 4),
+                      lane);
 }
 
 // ------------------------------------------------------------ attention
@@ -239,13 +288,14 @@ __global__ __launch_bounds__(512, 1) void mla_mha_kernel(const MhaArgs g) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int gq = lane >> 4, l16 = lane & 15;
-  // XCD x (= block % 8) takes the nq query tiles of pairs x, x + 8, ... in
-  // turn, heaviest (last) tile first: the tiles of a pair stream the same
-  // keys and values through one L2 at about the same time
+  // XCD x (= block % 8) takes pairs x, x + 8, ...: first the last (heaviest)
+  // query tile of each of them, then the tile before it, and so on, so that
+  // the causal work of a tile shrinks as the launch drains
   const int x = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int pair = (slot / g.nq) * 8 + x;
+  const int npx = (g.n_pairs + 7) / 8;   // pairs per XCD
+  const int pair = (slot % npx) * 8 + x;
   if (pair >= g.n_pairs) return;
-  const int qtile = g.nq - 1 - slot % g.nq;
+  const int qtile = g.nq - 1 - slot / npx;
   const int seq = pair / g.H, h = pair % g.H;
   const int cl = cached_of(g.cached_len, seq, g.n_new, g.max_len);
   const int valid = cl + g.n_new;
@@ -254,9 +304,12 @@ __global__ __launch_bounds__(512, 1) void mla_mha_kernel(const MhaArgs g) {
   const int wq0 = q0 + MQ * wave;
   const bool wact = wq0 < g.n_new;
   const int wsteps = wact ? (cl + min(wq0 + MQ, g.n_new) - 1) / XB + 1 : 0;
+  const int wfull = (cl + wq0 + 1) / XB;   // steps every query of the wave sees whole
 
   // queries: lane holds query wq0 + 16 t2 + l16 (the last new token repeated
-  // past n_new), features 32 ks + 8 gq .. + 7; rotary part rotated; scaled
+  // past n_new), features 32 ks + 8 gq .. + 7; rotary part rotated; scaled by
+  // the softmax scale times log2 e, so the scores are in base-2 units and
+  // p = 2^(s - max)
   v8bf qh[2][6], ql[2][6];
   int qpos[2];
   const size_t qld = (size_t)g.H * (DN + DR), slice = (size_t)g.T * qld;
@@ -285,7 +338,7 @@ __global__ __launch_bounds__(512, 1) void mla_mha_kernel(const MhaArgs g) {
         rope_apply(b.x, b.y, cs[4], cs[5], &b.x, &b.y);
         rope_apply(b.z, b.w, cs[6], cs[7], &b.z, &b.w);
       }
-      const float m = g.smscale;
+      const float m = g.smscale * 1.4426950408889634f;   // log2 e
       split8(make_float4(a.x * m, a.y * m, a.z * m, a.w * m),
              make_float4(b.x * m, b.y * m, b.z * m, b.w * m), &qh[t2][ks], &ql[t2][ks]);
     }
@@ -336,37 +389,56 @@ __global__ __launch_bounds__(512, 1) void mla_mha_kernel(const MhaArgs g) {
     const uint8_t* sb = sl[st];
     v4f s[2][2];
 #pragma unroll
-    for (int pt = 0; pt < 2; ++pt) {
+    for (int pt = 0; pt < 2; ++pt)
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) s[pt][t2] = v4f{0.f, 0.f, 0.f, 0.f};
-      const int r = 8 * (l16 >> 2) + 4 * pt + (l16 & 3);   // row l16 of tile pt
-#pragma unroll
-      for (int ks = 0; ks < DN / 32; ++ks) {
-        const int o16 = r * (DN * 2) + 16 * ((4 * ks + gq) ^ l16);
-        const v8bf kh = *reinterpret_cast<const v8bf*>(sb + o16);
-        const v8bf kl = *reinterpret_cast<const v8bf*>(sb + ST_KL + o16);
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
-          s[pt][t2] = mfma_bf16(kh, qh[t2][ks], s[pt][t2]);
-          s[pt][t2] = mfma_bf16(kh, ql[t2][ks], s[pt][t2]);
-          s[pt][t2] = mfma_bf16(kl, qh[t2][ks], s[pt][t2]);
-        }
+    // twelve fragment groups per step: for each score tile pt, the four K
+    // blocks (high and low halves), then the two rotary blocks; group u + 1's
+    // fragments are read while group u's MFMAs run
+    auto kload = [&](int u, v8bf& a, v8bf& b) {
+      const int pt = u / 6, k = u % 6;
+      const int r = 8 * (l16 >> 2) + 4 * pt + (l16 & 3);
+      if (k < DN / 32) {
+        const int o16 = r * (DN * 2) + 16 * ((4 * k + gq) ^ l16);
+        a = *reinterpret_cast<const v8bf*>(sb + o16);
+        b = *reinterpret_cast<const v8bf*>(sb + ST_KL + o16);
+      } else {
+        const int o16 = ST_KP + r * (DR * 2) + 16 * ((4 * (k - DN / 32) + gq) ^ (l16 >> 1));
+        a = *reinterpret_cast<const v8bf*>(sb + o16);
       }
+    };
+    v8bf ca, cb, na, nb;
+    kload(0, ca, cb);
 #pragma unroll
-      for (int ks = 0; ks < DR / 32; ++ks) {
-        const int o16 = ST_KP + r * (DR * 2) + 16 * ((4 * ks + gq) ^ (l16 >> 1));
-        const v8bf kp = *reinterpret_cast<const v8bf*>(sb + o16);
+    for (int u = 0; u < 12; ++u) {
+      if (u + 1 < 12) kload(u + 1, na, nb);
+      __builtin_amdgcn_sched_barrier(0);
+      const int pt = u / 6, k = u % 6;
 #pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
-          s[pt][t2] = mfma_bf16(kp, qh[t2][DN / 32 + ks], s[pt][t2]);
-          s[pt][t2] = mfma_bf16(kp, ql[t2][DN / 32 + ks], s[pt][t2]);
-        }
+      for (int t2 = 0; t2 < 2; ++t2) {
+        s[pt][t2] = mfma_bf16(ca, qh[t2][k], s[pt][t2]);
+        s[pt][t2] = mfma_bf16(ca, ql[t2][k], s[pt][t2]);
+        if (k < DN / 32) s[pt][t2] = mfma_bf16(cb, qh[t2][k], s[pt][t2]);
+      }
+      if (u + 1 < 12) {
+        ca = na;
+        cb = nb;   // (a rotary group leaves b as it was; only K groups read it)
       }
     }
     // online softmax per query (lane: query 16 t2 + l16, positions
-    // 32 j + 8 gq + 4 pt + i)
+    // 32 j + 8 gq + 4 pt + i); the causal mask only on steps that reach past
+    // some query of the wave
     v8bf ph[2], pl[2];
-    const int kp0 = j * XB + 8 * gq;
+    if (j >= wfull) {
+      const int kp0 = j * XB + 8 * gq;
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+        for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (kp0 + 4 * pt + i > qpos[t2]) s[pt][t2][i] = -INFINITY;
+    }
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2) {
       float v[8];
@@ -375,24 +447,24 @@ __global__ __launch_bounds__(512, 1) void mla_mha_kernel(const MhaArgs g) {
       for (int pt = 0; pt < 2; ++pt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float sv = kp0 + 4 * pt + i <= qpos[t2] ? s[pt][t2][i] : -INFINITY;
-          v[4 * pt + i] = sv;
-          mx = fmaxf(mx, sv);
+          v[4 * pt + i] = s[pt][t2][i];
+          mx = fmaxf(mx, v[4 * pt + i]);
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(mrun[t2], mx);
-      const float alpha = __expf(mrun[t2] - mnew);
+      const float mnew = fmaxf(mrun[t2], col_reduce<true>(mx));
+      const float alpha = __builtin_amdgcn_exp2f(mrun[t2] - mnew);   // 1 where it did not move
       float sum = 0.f;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        v[k] = __expf(v[k] - mnew);
+        v[k] = __builtin_amdgcn_exp2f(v[k] - mnew);
         sum += v[k];
       }
       lrun[t2] = lrun[t2] * alpha + sum;
-      mrun[t2] = mnew;
+      // the outputs are rescaled only when some query's maximum moved
+      if (__builtin_amdgcn_ballot_w64(mnew > mrun[t2]) != 0) {
 #pragma unroll
-      for (int ft = 0; ft < DV / 16; ++ft) o[t2][ft] *= alpha;
+        for (int ft = 0; ft < DV / 16; ++ft) o[t2][ft] *= alpha;
+      }
+      mrun[t2] = mnew;
       split8(make_float4(v[0], v[1], v[2], v[3]), make_float4(v[4], v[5], v[6], v[7]), &ph[t2],
              &pl[t2]);
     }
@@ -427,9 +499,7 @@ __global__ __launch_bounds__(512, 1) void mla_mha_kernel(const MhaArgs g) {
   // o / l, then the 1x128 block of each (token, head): e4m3 codes and scale
 #pragma unroll
   for (int t2 = 0; t2 < 2; ++t2) {
-    float l = lrun[t2];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    const float l = col_reduce<false>(lrun[t2]);
     float amax = 0.f;
 #pragma unroll
     for (int ft = 0; ft < DV / 16; ++ft)
@@ -438,9 +508,7 @@ __global__ __launch_bounds__(512, 1) void mla_mha_kernel(const MhaArgs g) {
         o[t2][ft][i] = o[t2][ft][i] / l;
         amax = fmaxf(amax, fabsf(o[t2][ft][i]));
       }
-    amax = fmaxf(amax, __shfl_xor(amax, 16));
-    amax = fmaxf(amax, __shfl_xor(amax, 32));
-    const float sc = fp8_scale(amax);
+    const float sc = fp8_scale(col_reduce<true>(amax));
     const int qi = wq0 + 16 * t2 + l16;
     if (qi >= g.n_new) continue;
     const size_t t = (size_t)seq * g.n_new + qi;
@@ -474,9 +542,8 @@ hipError_t launch_mla_mha(int T, int H, int n_seq, int n_new, int max_len, int n
                           float* o_s, float* attn, hipStream_t s) {
   if (n_seq <= 0 || n_new <= 0 || T != n_seq * n_new || n_new > max_len) return hipErrorInvalidValue;
   const int nblk = mla_mha_nblk(max_len);
-  mla_kv_expand_kernel<<<n_seq * H * (nblk / 2), 256, 0, s>>>(H, n_new, max_len, nblk, cached_len,
-                                                               c_codes, c_scales, uk, uv, s_kvb,
-                                                               kv);
+  mla_kv_expand_kernel<<<n_seq * H * (nblk / 2), XW * 64, 0, s>>>(
+      H, n_new, max_len, nblk, cached_len, c_codes, c_scales, uk, uv, s_kvb, kv);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   MhaArgs a{};
