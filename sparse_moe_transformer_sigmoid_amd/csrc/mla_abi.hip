@@ -185,11 +185,17 @@ bool use_mha(const MDims& D, int S, int n, int L) {
   return n >= MHA_MIN_NEW && k2::mla_mha_kv_bytes(S, D.H, L) <= MHA_MAX_KV_BYTES;
 }
 
+// The output projection of batches of at least O_WIDE_MIN tokens runs in
+// 128-row m-tiles with the FP8 MFMA's own block sums: its result goes
+// straight to the residual add (no requantisation decides on it), so the
+// exact sums the other two projections need buy nothing there.
+constexpr int O_WIDE_MIN = 2048;
+
 struct MLayout {
-  size_t hbuf, xq, xs, offsets, mt_start, tile_group, part, qkv, qa_q, qa_s, qcat, part_o,
-      part_ml, kv, rot, o_q, o_s, total;
+  size_t hbuf, xq, xs, offsets, mt_start, tile_group, mt_start8, tile_group8, part, qkv, qa_q,
+      qa_s, qcat, part_o, part_ml, kv, rot, o_q, o_s, total;
   int ns_qkv, ns_qb, ns_o, ns_attn, chunk;
-  bool mha;
+  bool mha, o_wide;
 };
 
 MLayout ws_layout(const MDims& D, int S, int n, int L) {
@@ -204,7 +210,8 @@ MLayout ws_layout(const MDims& D, int S, int n, int L) {
   };
   w.ns_qkv = gemm_split((int)T, D.n_qkv_pad, D.d);
   w.ns_qb = gemm_split((int)T, D.n_qb, D.ql);
-  w.ns_o = gemm_split((int)T, D.n_o, D.H * D.v);
+  w.o_wide = T >= (size_t)O_WIDE_MIN;
+  w.ns_o = w.o_wide ? 1 : gemm_split((int)T, D.n_o, D.H * D.v);
   attn_split((int)T, D.H, S, n, L, &w.ns_attn, &w.chunk);
   w.hbuf = take(T * D.d * 2);
   w.xq = take(T * D.d);
@@ -212,6 +219,10 @@ MLayout ws_layout(const MDims& D, int S, int n, int L) {
   w.offsets = take(2 * 4);
   w.mt_start = take(2 * 4);
   w.tile_group = take(((T + 15) / 16 + 1) * 4);
+  if (w.o_wide) {
+    w.mt_start8 = take(2 * 4);
+    w.tile_group8 = take(((T + 127) / 128 + 1) * 4);
+  }
   const size_t part_elems = std::max({(size_t)w.ns_qkv * T * D.n_qkv_pad,
                                       (size_t)w.ns_qb * T * D.n_qb, (size_t)w.ns_o * T * D.n_o});
   w.part = take(part_elems * 4);
@@ -245,8 +256,8 @@ Tp* at(void* base, size_t off) {
 moe_status run_gemm(const MDims& D, int T, int N, int K, int nsplit, const uint8_t* act,
                     const float* act_s, const uint8_t* wcodes, const float* wscales,
                     const int32_t* offsets, const int32_t* mt_start, const int32_t* tile_group,
-                    float* out, hipStream_t s) {
-  const int tt = gemm_tt(T);
+                    float* out, hipStream_t s, bool wide = false) {
+  const int tt = wide ? 8 : gemm_tt(T);
   const int bm = 16 * tt;
   k2::GemmArgs a{};
   a.wpk = wcodes;
@@ -272,7 +283,10 @@ moe_status run_gemm(const MDims& D, int T, int N, int K, int nsplit, const uint8
   a.d = N;
   const int mtiles = (T + bm - 1) / bm;
   const int grid = (mtiles * a.NC + 7) / 8 * 8;
-  M_HIP(k2::launch_gemm_dense(tt, nsplit, a, grid, s));
+  if (wide)
+    M_HIP(k2::launch_gemm_fp8(false, 8, a, grid, s));   // one K slice, FP8 MFMA block sums
+  else
+    M_HIP(k2::launch_gemm_dense(tt, nsplit, a, grid, s));
   return MOE_OK;
 }
 
@@ -341,6 +355,9 @@ moe_status run_mla(const mla_config* cfg, int32_t S, int32_t n, int32_t L, const
     // 16 gemm_tt(T) rows (the same for all three projections)
     M_HIP(k2::launch_dense_tiles((int)T, 16 * gemm_tt((int)T), offsets, mt_start, tile_group,
                                  s));
+    if (W.o_wide)
+      M_HIP(k2::launch_dense_tiles((int)T, 128, offsets, at<int32_t>(ws, W.mt_start8),
+                                   at<int32_t>(ws, W.tile_group8), s));
     // [q_a; kv_a] = h [W_qa; W_kva]^T
     if ((st = run_gemm(D, T, D.n_qkv_pad, D.d, W.ns_qkv, xq, xs, pk + P.qkv_codes,
                        reinterpret_cast<const float*>(pk + P.qkv_scales), offsets, mt_start,
@@ -404,8 +421,10 @@ moe_status run_mla(const mla_config* cfg, int32_t S, int32_t n, int32_t L, const
   k2::ProfileScope ps(MOE_STAGE_MLA_PROJ, s);
   // out = x + o W_o^T
   if ((st = run_gemm(D, T, D.n_o, D.H * D.v, W.ns_o, o_q, o_s, pk + P.o_codes,
-                     reinterpret_cast<const float*>(pk + P.o_scales), offsets, mt_start,
-                     tile_group, part, s)) != MOE_OK)
+                     reinterpret_cast<const float*>(pk + P.o_scales), offsets,
+                     W.o_wide ? at<int32_t>(ws, W.mt_start8) : mt_start,
+                     W.o_wide ? at<int32_t>(ws, W.tile_group8) : tile_group, part, s,
+                     W.o_wide)) != MOE_OK)
     return st;
   M_HIP(k2::launch_slice_sum(T, D.n_o, D.n_o, W.ns_o, part,
                              out_f32 ? nullptr : static_cast<const uint16_t*>(x), out, D.n_o,

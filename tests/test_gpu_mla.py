@@ -128,6 +128,7 @@ def _edge_tokens(n_seq, n_new):
     (1, 300, (0,), 320, 64, 11),                # 64 heads, a ragged second 256-token tile
     (2, 150, (500, 3), 700, 32, 12),            # chunked prefill after a long prefix; idle waves
     (3, 129, (64, 0, 31), 224, 16, 13),         # ragged lengths, a 64-position-aligned prefix
+    (2, 1024, (0, 100), 1200, 16, 14),          # 2,048 tokens: the output projection in 128-row tiles
 ])
 def test_small_mla_per_head_form(n_seq, n_new, cached, max_len, heads, seed):
     _log(f"per-head mla S={n_seq} n={n_new} cached={cached} L={max_len} H={heads}")
