@@ -187,8 +187,11 @@ bool use_mha(const MDims& D, int S, int n, int L) {
 
 // The output projection of batches of at least O_WIDE_MIN tokens runs in
 // 128-row m-tiles with the FP8 MFMA's own block sums: its result goes
-// straight to the residual add (no requantisation decides on it), so the
-// exact sums the other two projections need buy nothing there.
+// straight to the residual add (no requantisation decides on it), so exact
+// block sums buy nothing there.  The same holds for the query up-projection
+// when the per-head form consumes its fp32 output directly; the
+// [q_a; kv_a] projection keeps exact sums (its latents are normalised and
+// requantised, and the absorbed form's queries go through W_uk first).
 constexpr int O_WIDE_MIN = 2048;
 
 struct MLayout {
@@ -383,17 +386,20 @@ moe_status run_mla(const mla_config* cfg, int32_t S, int32_t n, int32_t L, const
   {
     k2::ProfileScope ps(MOE_STAGE_MLA_PROJ, s);
     // q = qa W_qb^T
-    if ((st = run_gemm(D, T, D.n_qb, D.ql, W.ns_qb, qa_q, qa_s, pk + P.qb_codes,
-                       reinterpret_cast<const float*>(pk + P.qb_scales), offsets, mt_start,
-                       tile_group, part, s)) != MOE_OK)
+    const bool qb_wide = W.o_wide && W.mha;
+    if ((st = run_gemm(D, T, D.n_qb, D.ql, qb_wide ? 1 : W.ns_qb, qa_q, qa_s, pk + P.qb_codes,
+                       reinterpret_cast<const float*>(pk + P.qb_scales), offsets,
+                       qb_wide ? at<int32_t>(ws, W.mt_start8) : mt_start,
+                       qb_wide ? at<int32_t>(ws, W.tile_group8) : tile_group, part, s,
+                       qb_wide)) != MOE_OK)
       return st;
   }
   if (W.mha) {
     // per-head keys and values of every visible position, then attention
     // (the q_b projection's K-slice partial sums are added in the kernel)
     k2::ProfileScope ps(MOE_STAGE_MLA_ATTN, s);
-    M_HIP(k2::launch_mla_mha(T, D.H, S, n, L, W.ns_qb, D.smscale, part, at<double>(ws, W.rot),
-                             cached_len,
+    M_HIP(k2::launch_mla_mha(T, D.H, S, n, L, W.o_wide ? 1 : W.ns_qb, D.smscale, part,
+                             at<double>(ws, W.rot), cached_len,
                              static_cast<const uint8_t*>(cache_codes), cache_scales,
                              static_cast<const uint16_t*>(cache_rope), uk, uv, kvbs,
                              at<uint16_t>(ws, W.kv), o_q, o_s, attn, s));
