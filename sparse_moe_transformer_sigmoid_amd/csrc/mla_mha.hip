@@ -542,6 +542,10 @@ hipError_t launch_mla_mha(int T, int H, int n_seq, int n_new, int max_len, int n
                           float* o_s, float* attn, hipStream_t s) {
   if (n_seq <= 0 || n_new <= 0 || T != n_seq * n_new || n_new > max_len) return hipErrorInvalidValue;
   const int nblk = mla_mha_nblk(max_len);
+  // the kernels address one (sequence, head)'s blocks, a sequence's codes and
+  // its rotary keys with 32-bit byte offsets
+  if ((size_t)nblk * XBLK * 2 > 0xFFFFFFFFu || (size_t)max_len * DL > 0xFFFFFFFFu)
+    return hipErrorInvalidValue;
   mla_kv_expand_kernel<<<n_seq * H * (nblk / 2), XW * 64, 0, s>>>(
       H, n_new, max_len, nblk, cached_len, c_codes, c_scales, uk, uv, s_kvb, kv);
   hipError_t e = hipGetLastError();
