@@ -583,21 +583,24 @@ __global__ __launch_bounds__(256) void mla_pack_ukv_kernel(int H, const uint8_t*
   }
 }
 
-constexpr int QA_TB = 32;   // tokens per workgroup
 
 // q: the q_b projection as nsplit K-slice partial sums [nsplit, T, H*192],
 // added in slice order (the order of launch_slice_sum).
 // qcat[t, h] = scale * [W_uk^T q_nope (512), rope(q_pe) (64)] in fp32, per
 // latent block b: s_b * sum_d code[d][r] q[d] (W_uk of head h: key-value
 // up-projection rows h*(DN+DV) .. + DN - 1, one 128-row scale block).
-// Workgroup = (head, 32 tokens); wave w: latents 128 w .. + 127 (block w).
+// Workgroup = (head, TB tokens); wave w: latents 128 w .. + 127 (block w).
+// TB = 16 for small batches (decode), so that 64 heads give 256 workgroups
+// at 64 tokens; 32 otherwise (each head's W_uk fragments feed twice the MFMAs).
+template <int TB>
 __global__ __launch_bounds__(256) void mla_qabsorb_kernel(
     int T, int H, int nsplit, float smscale, const float* __restrict__ q,
     const uint16_t* __restrict__ ukt,
     const float* __restrict__ s_kvb, const double* __restrict__ inv_freq,
     const int32_t* __restrict__ cached_len, int n_new, int max_len,
     float* __restrict__ qcat) {
-  const int h = blockIdx.x, t0 = blockIdx.y * QA_TB, tid = threadIdx.x;
+  constexpr int MT = TB / 16;
+  const int h = blockIdx.x, t0 = blockIdx.y * TB, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, q4 = lane >> 4, l16 = lane & 15;
   const int qld = H * (DN + DR);
   const size_t slice = (size_t)T * qld;
@@ -611,16 +614,16 @@ __global__ __launch_bounds__(256) void mla_qabsorb_kernel(
   };
   // A: q_nope of tokens t0 + 16 mt + l16 (the last token repeated past T),
   // features 32 ks + 8 q4 .. + 7
-  v8bf ahi[2][DN / 32], alo[2][DN / 32];
+  v8bf ahi[MT][DN / 32], alo[MT][DN / 32];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
+  for (int mt = 0; mt < MT; ++mt) {
     const int t = min(t0 + 16 * mt + l16, T - 1);
     const float* qp = q + (size_t)t * qld + h * (DN + DR) + 8 * q4;
 #pragma unroll
     for (int ks = 0; ks < DN / 32; ++ks)
       split8(q4sum(qp + 32 * ks), q4sum(qp + 32 * ks + 4), &ahi[mt][ks], &alo[mt][ks]);
   }
-  v4f acc[2][8] = {};
+  v4f acc[MT][8] = {};
   const uint16_t* bp = ukt + ((size_t)h * DL + 128 * wave + l16) * DN + 8 * q4;
 #pragma unroll
   for (int ks = 0; ks < DN / 32; ++ks) {
@@ -632,7 +635,7 @@ __global__ __launch_bounds__(256) void mla_qabsorb_kernel(
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
+      for (int mt = 0; mt < MT; ++mt) {
         acc[mt][ct] = mfma_bf16(ahi[mt][ks], b[ct], acc[mt][ct]);
         acc[mt][ct] = mfma_bf16(alo[mt][ks], b[ct], acc[mt][ct]);
       }
@@ -640,7 +643,7 @@ __global__ __launch_bounds__(256) void mla_qabsorb_kernel(
   // lane: latent 128 w + 16 ct + l16, tokens 16 mt + 4 q4 + i
   const float sk = s_kvb[(size_t)(2 * h) * (DL / QBLK) + wave];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = t0 + 16 * mt + 4 * q4 + i;
@@ -650,7 +653,7 @@ __global__ __launch_bounds__(256) void mla_qabsorb_kernel(
       for (int ct = 0; ct < 8; ++ct) dst[16 * ct] = acc[mt][ct][i] * sk * smscale;
     }
   // rotary part: thread (token tt, pair i)
-  for (int i = tid; i < QA_TB * (DR / 2); i += 256) {
+  for (int i = tid; i < TB * (DR / 2); i += 256) {
     const int tt = i / (DR / 2), pr = i % (DR / 2), t = t0 + tt;
     if (t >= T) continue;
     int seq;
@@ -669,26 +672,27 @@ __global__ __launch_bounds__(256) void mla_qabsorb_kernel(
   }
 }
 
-constexpr int VU_TB = 32;             // tokens per workgroup
 constexpr int VA_LD = DL + 8;         // bf16 stride of an activation row in LDS
 
-// For head h and 32 tokens: merge the position splits (m, l, O) into
+// For head h and TB tokens (16 or 32): merge the position splits (m, l, O) into
 // o_lat = sum_j p_j c_j / sum_j p_j, apply W_uv (rows h*(DN+DV)+DN .. + DV - 1,
 // one 128-row scale block) as sum_r code[d][r] (s_(r/128) o_lat[r]), write the
 // 128 outputs as one 1x128 block of the output projection's input (codes +
 // scale) and, if attn != null, as fp32.  Wave w: outputs 32 w .. + 31.
+template <int TB>
 __global__ __launch_bounds__(256) void mla_vup_kernel(
     int T, int H, int nsplit, const float* __restrict__ part_o, const float* __restrict__ part_ml,
     const uint16_t* __restrict__ uv, const float* __restrict__ s_kvb,
     uint8_t* __restrict__ o_q, float* __restrict__ o_s, float* __restrict__ attn) {
-  const int h = blockIdx.x, t0 = blockIdx.y * VU_TB, tid = threadIdx.x;
+  constexpr int MT = TB / 16;
+  const int h = blockIdx.x, t0 = blockIdx.y * TB, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, q4 = lane >> 4, l16 = lane & 15;
-  __shared__ __attribute__((aligned(16))) uint16_t a_hi[VU_TB * VA_LD];
-  __shared__ __attribute__((aligned(16))) uint16_t a_lo[VU_TB * VA_LD];
-  __shared__ float bmax[4][VU_TB];
+  __shared__ __attribute__((aligned(16))) uint16_t a_hi[TB * VA_LD];
+  __shared__ __attribute__((aligned(16))) uint16_t a_lo[TB * VA_LD];
+  __shared__ float bmax[4][TB];
   const float* sv = s_kvb + (size_t)(2 * h + 1) * (DL / QBLK);
   // merge: thread = (token tt, 16 consecutive latents)
-  for (int it = tid; it < VU_TB * (DL / 16); it += 256) {
+  for (int it = tid; it < TB * (DL / 16); it += 256) {
     const int tt = it / (DL / 16), r0 = 16 * (it % (DL / 16)), t = t0 + tt;
     float a[16];
 #pragma unroll
@@ -731,7 +735,7 @@ __global__ __launch_bounds__(256) void mla_vup_kernel(
   __syncthreads();
   // out[t, d]: A = activation halves (tokens 16 mt + l16, latents 32 ks + 8 q4
   // ..), B = W_uv rows d = 32 w + 16 ct + l16
-  v4f acc[2][2] = {};
+  v4f acc[MT][2] = {};
   const uint16_t* bp = uv + ((size_t)h * DV + 32 * wave + l16) * DL + 8 * q4;
 #pragma unroll 4
   for (int ks = 0; ks < DL / 32; ++ks) {
@@ -741,7 +745,7 @@ __global__ __launch_bounds__(256) void mla_vup_kernel(
       b[ct] = __builtin_bit_cast(v8bf,
                                  *reinterpret_cast<const uint4*>(bp + (size_t)16 * ct * DL + 32 * ks));
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
+    for (int mt = 0; mt < MT; ++mt) {
       const int ao = (16 * mt + l16) * VA_LD + 32 * ks + 8 * q4;
       const v8bf ah = *reinterpret_cast<const v8bf*>(&a_hi[ao]);
       const v8bf al = *reinterpret_cast<const v8bf*>(&a_lo[ao]);
@@ -755,7 +759,7 @@ __global__ __launch_bounds__(256) void mla_vup_kernel(
   // lane: outputs d = 32 w + 16 ct + l16 of tokens 16 mt + 4 q4 + i; block
   // maxima over the 128 outputs of a token (16 lanes x 2 tiles x 4 waves)
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float m = fmaxf(fabsf(acc[mt][0][i]), fabsf(acc[mt][1][i]));
@@ -765,7 +769,7 @@ __global__ __launch_bounds__(256) void mla_vup_kernel(
     }
   __syncthreads();
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int tt = 16 * mt + 4 * q4 + i, t = t0 + tt;
@@ -839,9 +843,16 @@ hipError_t launch_mla_qabsorb(int T, int H, int nsplit, float smscale, const flo
                               const uint16_t* ukt, const float* s_kvb, const double* inv_freq,
                               const int32_t* cached_len, int n_new, int max_len, float* qcat,
                               hipStream_t s) {
-  dim3 grid(H, (T + QA_TB - 1) / QA_TB);
-  mla_qabsorb_kernel<<<grid, 256, 0, s>>>(T, H, nsplit, smscale, q, ukt, s_kvb, inv_freq,
-                                          cached_len, n_new, max_len, qcat);
+  // 16-token tiles while 32-token ones would leave CUs idle
+  if ((long)H * ((T + 31) / 32) < 256) {
+    dim3 grid(H, (T + 15) / 16);
+    mla_qabsorb_kernel<16><<<grid, 256, 0, s>>>(T, H, nsplit, smscale, q, ukt, s_kvb, inv_freq,
+                                                cached_len, n_new, max_len, qcat);
+  } else {
+    dim3 grid(H, (T + 31) / 32);
+    mla_qabsorb_kernel<32><<<grid, 256, 0, s>>>(T, H, nsplit, smscale, q, ukt, s_kvb, inv_freq,
+                                                cached_len, n_new, max_len, qcat);
+  }
   return hipGetLastError();
 }
 
@@ -872,8 +883,15 @@ hipError_t launch_mla_attn(int T, int H, int n_seq, int n_new, int max_len, int 
 hipError_t launch_mla_vup(int T, int H, int nsplit, const float* part_o, const float* part_ml,
                           const uint16_t* uv, const float* s_kvb, uint8_t* o_q, float* o_s,
                           float* attn, hipStream_t s) {
-  dim3 grid(H, (T + VU_TB - 1) / VU_TB);
-  mla_vup_kernel<<<grid, 256, 0, s>>>(T, H, nsplit, part_o, part_ml, uv, s_kvb, o_q, o_s, attn);
+  if ((long)H * ((T + 31) / 32) < 256) {
+    dim3 grid(H, (T + 15) / 16);
+    mla_vup_kernel<16><<<grid, 256, 0, s>>>(T, H, nsplit, part_o, part_ml, uv, s_kvb, o_q, o_s,
+                                            attn);
+  } else {
+    dim3 grid(H, (T + 31) / 32);
+    mla_vup_kernel<32><<<grid, 256, 0, s>>>(T, H, nsplit, part_o, part_ml, uv, s_kvb, o_q, o_s,
+                                            attn);
+  }
   return hipGetLastError();
 }
 
