@@ -444,20 +444,28 @@ __global__ __launch_bounds__(1024) void pad_offsets_kernel(int E, int G, int T, 
 template <int SRC>
 __global__ __launch_bounds__(256) void transpose_pad_kernel(const TransposeArgs a) {
   __shared__ uint16_t tile[64][66];
+  __shared__ int g_first;
   const int c0 = blockIdx.y * 64;
   const int q0 = blockIdx.x * 64;   // padded column block
   const int tid = threadIdx.x;
+  // group of padded column q0 (largest g with pad_off[g] <= q0), searched
+  // once per workgroup; the block's 64 columns span few groups
+  if (tid == 0) {
+    int lo = 0, hi = a.G;   // pad_off[0] = 0 <= q0 < pad_off[G] for q0 inside
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (a.pad_off[mid] <= q0) lo = mid; else hi = mid;
+    }
+    g_first = lo;
+  }
+  __syncthreads();
   // stage: thread reads 16 consecutive features of one padded row
   {
     const int rr = tid >> 2, cc = (tid & 3) * 16;
     const int q = q0 + rr;
-    // group of padded column q: largest g with pad_off[g] <= q
-    int lo = 0, hi = a.G;   // pad_off[0] = 0 <= q < pad_off[G] for q inside
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (a.pad_off[mid] <= q) lo = mid; else hi = mid;
-    }
-    const int gi = lo;
+    // group of padded column q: walk forward from the block's first group
+    int gi = g_first;
+    while (gi + 1 < a.G && a.pad_off[gi + 1] <= q) ++gi;
     const int j = q - a.pad_off[gi];
     int len, r0;
     if (gi >= a.E) { r0 = a.P; len = a.T; } else {
