@@ -24,9 +24,15 @@
  * 656 bytes per position: the latent is cached as the FP8 input of the
  * key-value up-projection (which is what that FP8 linear reads), where a bf16
  * latent takes 1,152 bytes ("Kimi-K2-Base", KV cache: 70,272 B per token over
- * 61 layers).  Attention runs in the absorbed form: the query's key part is
- * multiplied into latent space and the value up-projection is applied after
- * the weighted sum, so the per-head keys and values are never formed.
+ * 61 layers).  Two forms of the same attention are used:
+ *   - absorbed (decode and small chunks): the query's key part is multiplied
+ *     into latent space and the value up-projection is applied after the
+ *     weighted sum, so the per-head keys and values are never formed;
+ *   - per head (at least 128 new tokens per sequence, key/value buffer at
+ *     most 16 GiB): the keys W_uk c and values W_uv c of every visible
+ *     position and head are formed in the workspace (1 KiB per position and
+ *     head, as bf16 high and low halves) and attended flash-style.
+ * mla_workspace_bytes reports the size for the form the call will use.
  *
  * Batch: S sequences, each with the same number n of new tokens (T = S * n;
  * decode: n = 1; prefill: n = prompt length), token t belongs to sequence
