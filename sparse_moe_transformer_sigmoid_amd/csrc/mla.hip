@@ -8,7 +8,8 @@
 // by the heads) and 128 value features; softmax scale (0.1 ln 32 + 1)^2 /
 // sqrt(192); causal; positions numbered from the cached length.
 //
-// The attention runs in the absorbed form over a latent cache.  With W_uk,
+// Decode and small chunks attend in the absorbed form over the latent cache
+// (below); prompt-sized batches use the per-head form of mla_mha.hip.  With W_uk,
 // W_uv the key and value rows of head h's key-value up-projection and c_j the
 // cached latent of position j:
 //   q_nope . (W_uk c_j) = (W_uk^T q_nope) . c_j,
