@@ -665,6 +665,7 @@ moe_status train_wgrad_chain(const Dims& D, const TrainLayout& L, int64_t T, voi
   K2_HIP(k2::launch_transpose_pad(2, ta, (int)ldt, s));
   // dW_down [d, I] = sum (w dy)^T a~ ; dW_gate, dW_up [2I, d] = sum [dg; du]^T h~
   k2::TrainGemmArgs g{};
+  g.E = D.E;
   g.G = D.G;
   g.pad_off = pad_off;
   g.out_stride = 3 * I * d;
@@ -672,7 +673,7 @@ moe_status train_wgrad_chain(const Dims& D, const TrainLayout& L, int64_t T, voi
   g.lda = 32 * D.d;
   g.B = aT;
   g.ldb = 32 * D.I;
-  g.MT = D.d / 256;
+  g.MT = D.d / k2::WGRAD_M;
   g.NT = D.I / 128;
   g.out = d_w + 2 * I * d;
   g.ldo = D.I;
@@ -681,7 +682,7 @@ moe_status train_wgrad_chain(const Dims& D, const TrainLayout& L, int64_t T, voi
   g.lda = 32 * 2 * D.I;
   g.B = hT;
   g.ldb = 32 * D.d;
-  g.MT = 2 * D.I / 256;
+  g.MT = 2 * D.I / k2::WGRAD_M;
   g.NT = D.d / 128;
   g.out = d_w;
   g.ldo = D.d;

@@ -19,10 +19,11 @@
 //   dgrad gate/up     C[d][rows]                        = [W_gate; W_up]^T [dg; du]^T
 // and train_wgrad_kernel the weight gradients
 //   wgrad             C[out][in]  = sum over a group's rows of X^T Y
-// (both operands K-blocked transposed copies).  A workgroup computes a 256 x 128 tile (4 waves of 64 M rows, 8 16-row N
-// tiles); each wave streams its 64 A rows straight into registers one K
-// step ahead, the 128 B rows are staged through LDS (double-buffered), and
-// lane l of a 16x16 result holds M rows 4(l/16)..+3 of N column l%16.
+// (both operands K-blocked transposed copies).  A workgroup computes a 256 x
+// 128 tile (4 waves of 64 M rows, 8 16-row N tiles); each wave streams its A
+// rows straight into registers one K step ahead, the 128 B rows are staged
+// through LDS (double-buffered), and lane l of a 16x16 result holds M rows
+// 4(l/16)..+3 of N column l%16.
 #include <math.h>
 
 #include <algorithm>
@@ -105,6 +106,14 @@ __device__ __forceinline__ TileWork decode_rows(const TrainGemmArgs& g) {
   return w;
 }
 
+// Work item of the weight gradients: (group, WGRAD_M-row M tile, 128-column N
+// tile).  An item's K is its group's rows, so the shared expert's items (T
+// rows each, groups E .. G-1) are about T / (rows per routed expert) times as
+// long as a routed one.  Every XCD (workgroup b runs on XCD b mod 8) starts
+// with an equal share of the shared items -- shared item j on XCD j mod 8,
+// longest work first -- and then takes a contiguous run of routed items, in
+// which the M tiles of one N tile are adjacent (they share that N tile's Y
+// rows in the XCD's L2).
 __device__ __forceinline__ TileWork decode_wgrad(const TrainGemmArgs& g) {
   TileWork w{};
   const int per = g.MT * g.NT;
@@ -112,8 +121,19 @@ __device__ __forceinline__ TileWork decode_wgrad(const TrainGemmArgs& g) {
   const int b = blockIdx.x;
   const int Wp = (Wtot + 7) & ~7;
   if (b >= Wp) return w;
-  const int L = (b & 7) * (Wp >> 3) + (b >> 3);
-  if (L >= Wtot) return w;
+  const int x = b & 7, i = b >> 3, slots = Wp >> 3;
+  const int R = min(g.E, g.G) * per;   // routed items
+  const int S = Wtot - R;              // shared items
+  const int sq = S >> 3, sr = S & 7;
+  const int sh_x = sq + (x < sr ? 1 : 0);   // shared items of XCD x
+  int L;
+  if (i < sh_x) {
+    L = R + x + 8 * i;
+  } else {
+    // XCD x's routed run follows those of XCDs 0 .. x-1
+    L = x * slots - (sq * x + min(x, sr)) + (i - sh_x);
+    if (L >= R) return w;
+  }
   w.grp = L / per;
   const int rr = L - w.grp * per;
   // M tiles inner: the items sharing an input-feature tile of Y run together
@@ -700,21 +720,21 @@ __global__ __launch_bounds__(256) void router_wgrad_kernel(int E, int d, int k, 
 }
 
 // Weight gradients C[out][in] = sum over a group's rows of X^T Y, in
-// 256 x 128 tiles (4 waves of 64 M rows, 8 16-row N tiles).  A tile's K is a
+// WGM x 128 tiles (4 waves of WGM / 4 M rows, 8 16-row N tiles).  A tile's K is a
 // group's rows, a few steps of 32 at the routed experts' sizes, so a one-step
 // prefetch would leave every step waiting a full memory round trip: the A
 // rows and the staged B rows are loaded PF steps ahead into a register ring
 // of PF + 1 sets.  The B rows go through LDS (double-buffered) as in
 // train_gemm_kernel; the same LDS then turns the results around so that 32
 // lanes store one row's 128 columns (512 contiguous bytes).
-constexpr int WG_M = 256;              // M rows per wgrad workgroup
-constexpr int WG_MT = WG_M / 4 / 16;   // 16-row M tiles per wave
 constexpr int OT_LD = TN + 4;          // fp32 stride of a turned-around row
 constexpr int WG_LDS_BYTES = 4 * 16 * OT_LD * 4;
 static_assert(WG_LDS_BYTES >= 2 * TN * B_LD * 2, "LDS turnaround must hold the B stages");
 
-template <int PF>
-__global__ __launch_bounds__(256, 2) void train_wgrad_kernel(const TrainGemmArgs g) {
+template <int PF, int WGM, int MINW>
+__global__ __launch_bounds__(256, MINW) void train_wgrad_kernel(const TrainGemmArgs g) {
+  constexpr int WG_MW = WGM / 4;       // M rows per wave
+  constexpr int WG_MT = WG_MW / 16;    // 16-row M tiles per wave
   constexpr int NR = PF + 1;           // register ring sets
   constexpr int UN = 2 * NR;           // unroll: LDS buffer and ring slot compile-time
   __shared__ __attribute__((aligned(16))) uint8_t lds[WG_LDS_BYTES];
@@ -734,7 +754,7 @@ __global__ __launch_bounds__(256, 2) void train_wgrad_kernel(const TrainGemmArgs
   const uint16_t* arow[WG_MT];
 #pragma unroll
   for (int mt = 0; mt < WG_MT; ++mt) {
-    const size_t row = (size_t)(WG_M * wi.mi + TMW * wave + 16 * mt + l16);
+    const size_t row = (size_t)(WGM * wi.mi + WG_MW * wave + 16 * mt + l16);
     arow[mt] = g.A + (kbase / TK) * (size_t)g.lda + row * TK + 8 * q4;
   }
   const uint16_t* brow[2];
@@ -817,7 +837,7 @@ __global__ __launch_bounds__(256, 2) void train_wgrad_kernel(const TrainGemmArgs
     for (int i = 0; i < 8; ++i) {
       const int row = 2 * i + (lane >> 5), col = 4 * (lane & 31);
       const v4f v = *reinterpret_cast<const v4f*>(&tw[row * OT_LD + col]);
-      const size_t m = (size_t)(WG_M * wi.mi + TMW * wave + 16 * mt + row);
+      const size_t m = (size_t)(WGM * wi.mi + WG_MW * wave + 16 * mt + row);
       __builtin_nontemporal_store(v, reinterpret_cast<v4f*>(out + m * g.ldo + col));
     }
     __builtin_amdgcn_wave_barrier();
@@ -827,6 +847,10 @@ __global__ __launch_bounds__(256, 2) void train_wgrad_kernel(const TrainGemmArgs
 // the ring depth used: loads one step ahead (two and three steps ahead
 // measured 3% and 7% slower at the K2 prefill batch, bitwise the same)
 constexpr int WGRAD_PF = 1;
+// waves per SIMD the register budget is sized for: two workgroups per CU.
+// 128-row tiles at four per CU (116 registers) were no faster and slowed the
+// input-gradient products that run beside them on the other stream.
+constexpr int WGRAD_MINW = WGRAD_M == 256 ? 2 : 4;
 
 }  // namespace
 
@@ -837,7 +861,9 @@ hipError_t launch_train_gemm(int mode, const TrainGemmArgs& a, int grid, hipStre
     case TM_FWD_DOWN: train_gemm_kernel<TM_FWD_DOWN><<<grid, 256, 0, s>>>(a); break;
     case TM_BWD_DOWN: train_gemm_kernel<TM_BWD_DOWN><<<grid, 256, 0, s>>>(a); break;
     case TM_BWD_GU: train_gemm_kernel<TM_BWD_GU><<<grid, 256, 0, s>>>(a); break;
-    case TM_WGRAD: train_wgrad_kernel<WGRAD_PF><<<grid, 256, 0, s>>>(a); break;
+    case TM_WGRAD:
+      train_wgrad_kernel<WGRAD_PF, WGRAD_M, WGRAD_MINW><<<grid, 256, 0, s>>>(a);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

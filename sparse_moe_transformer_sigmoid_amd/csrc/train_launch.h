@@ -10,6 +10,10 @@ namespace k2 {
 // products of the bf16 grouped GEMM kernel
 enum { TM_FWD_GU = 0, TM_FWD_DOWN = 1, TM_BWD_DOWN = 2, TM_BWD_GU = 3, TM_WGRAD = 4 };
 
+// M rows (output features) of a weight-gradient tile: TrainGemmArgs::MT of a
+// TM_WGRAD launch counts tiles of this height
+constexpr int WGRAD_M = 256;
+
 struct TrainGemmArgs {
   // groups and rows (row-tiled products): routed rows in expert order, then
   // the shared expert's T rows at P .. P + T
