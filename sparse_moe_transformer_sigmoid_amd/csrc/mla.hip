@@ -251,6 +251,7 @@ constexpr int CT_ELEMS = PT * CT_LD, TR_ELEMS = DL * TR_LD;
 constexpr int HPW = 8;   // heads per wave
 constexpr int AW = 8;    // waves per workgroup
 constexpr int NS = 3;    // LDS stages of raw cache bytes (copies run NS - 1 steps ahead)
+constexpr float LAZY_E = 5.5451774f;   // 8 ln 2: margin before a head's reference maximum moves
 
 __global__ __launch_bounds__(512, 1) void mla_attn_kernel(const AttnArgs g) {
   // raw stages: codes [pos][512] with the 16-byte chunk c of position p at
@@ -447,7 +448,11 @@ __global__ __launch_bounds__(512, 1) void mla_attn_kernel(const AttnArgs g) {
       }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mnew = fmaxf(mrun, mx);
+    // the reference maximum moves only when the step's maximum passes it by
+    // more than LAZY_E, so the probabilities stay below e^LAZY_E and the
+    // outputs are rarely rescaled; the merge and the final normalisation
+    // use the same reference, which cancels exactly
+    const float mnew = mx > mrun + LAZY_E ? mx : mrun;
     alpha = __expf(mrun - mnew);
     float lsum = 0.f;
 #pragma unroll
@@ -471,7 +476,7 @@ __global__ __launch_bounds__(512, 1) void mla_attn_kernel(const AttnArgs g) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) v[j >> 2][j & 3] = xbuf[own ? wave : wave ^ 1][j][lane];
     const float a_col = xbuf[own ? wave : wave ^ 1][8][lane];
-    // rescale only when some column's maximum moved (alpha = 1 leaves them)
+    // rescale only when some column's reference moved (alpha = 1 leaves them)
     if (__any(a_col != 1.f)) {
 #pragma unroll
       for (int nt = 0; nt < DL / 32; ++nt) o[nt] *= a_col;

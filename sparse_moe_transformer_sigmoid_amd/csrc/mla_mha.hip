@@ -253,6 +253,7 @@ constexpr int MQ = 32;                   // queries per wave
 constexpr int MW = 8;                    // waves per workgroup
 constexpr int MQT = MQ * MW;             // queries per workgroup
 constexpr int MNS = 3;                   // LDS stages (copies run two steps ahead)
+constexpr float LAZY = 8.f;              // log2 margin before a query's reference maximum moves
 // stage: K hi [32][256 B], K lo, V hi [128][64 B], V lo, rotary keys [32][128 B]
 constexpr int ST_KL = XB * DN * 2, ST_VH = 2 * ST_KL, ST_VL = 3 * ST_KL, ST_KP = 4 * ST_KL;
 constexpr int STAGE = ST_KP + XB * DR * 2;
@@ -450,7 +451,13 @@ __global__ __launch_bounds__(512, 1) void mla_mha_kernel(const MhaArgs g) {
           v[4 * pt + i] = s[pt][t2][i];
           mx = fmaxf(mx, v[4 * pt + i]);
         }
-      const float mnew = fmaxf(mrun[t2], col_reduce<true>(mx));
+      // The reference maximum moves only when the step's maximum passes it by
+      // more than LAZY (log2 units), so the probabilities stay below 2^LAZY
+      // and the outputs are rarely rescaled; the normalisation by the sum
+      // cancels the reference exactly.  Step 0 sees position 0, so every
+      // query's reference is finite after it.
+      const float mxq = col_reduce<true>(mx);
+      const float mnew = mxq > mrun[t2] + LAZY ? mxq : mrun[t2];
       const float alpha = __builtin_amdgcn_exp2f(mrun[t2] - mnew);   // 1 where it did not move
       float sum = 0.f;
 #pragma unroll
@@ -459,7 +466,7 @@ __global__ __launch_bounds__(512, 1) void mla_mha_kernel(const MhaArgs g) {
         sum += v[k];
       }
       lrun[t2] = lrun[t2] * alpha + sum;
-      // the outputs are rescaled only when some query's maximum moved
+      // the outputs are rescaled only when some query's reference moved
       if (__builtin_amdgcn_ballot_w64(mnew > mrun[t2]) != 0) {
 #pragma unroll
         for (int ft = 0; ft < DV / 16; ++ft) o[t2][ft] *= alpha;
