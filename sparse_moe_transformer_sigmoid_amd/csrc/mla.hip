@@ -30,11 +30,6 @@ namespace k2 {
 namespace {
 
 constexpr int PT = 32;            // cache positions per attention step
-constexpr int CT_LD = DL + 8;     // bf16 stride of a row-major cache latent in LDS
-// bf16 stride of a transposed latent row in LDS: 18 dwords, so the four
-// 16-row chunks a fill wave writes in one instruction fall on two bank halves
-// and the 16 rows a compute wave reads on 16 distinct even banks
-constexpr int TR_LD = PT + 4;
 
 // ------------------------------------------------------------------ packing
 // [n0 rows of src0; n1 rows of src1; zero rows] x K codes -> the grouped GEMM's
@@ -197,43 +192,42 @@ __global__ __launch_bounds__(256) void mla_latent_kernel(
   }
 }
 
-// --------------------------------------------------------- query absorption
 // ------------------------------------------------------- latent attention
-// Eight waves, each scoring a column block of 8 (token, head) pairs.  mode 0
-// (one new token per sequence): the waves are one token's groups of 8 heads,
-// so a workgroup covers min(heads, 64) heads and reads each cache position
-// once for all of them; mode 1: up to eight consecutive tokens of one sequence
-// with one group of 8 heads.  Waves 2i and 2i + 1 form a pair whose 16
-// columns share the value sum: each wave accumulates the outputs of all 16
-// columns over one half of the latent (256 features), taking the partner's
-// probabilities through LDS, so it holds 64 accumulator registers, not 128.  The cache positions [lo, hi) of the work item's split are
-// visited in steps of 32.  The cache bytes of a step (latent codes, rotary
-// keys, scales) are copied straight from global memory into one of NS LDS
-// stages (global_load_lds, no staging registers), NS - 1 steps ahead of the
-// compute.  Per step every wave first converts its share of the step's codes
-// into exact bf16 values (every e4m3 value is one), twice -- row-major
-// [pos][512] (the A operand of the scores) and transposed [latent][pos] (the
-// A operand of the value sum) -- and then computes; the rotary keys and the
-// scales are read from their stage as they arrived.
+// A workgroup covers 64 columns, each a (token, head) pair: mode 0 (one new
+// token per sequence) one token's heads, mode 1 up to 8 consecutive new
+// tokens of one sequence x 8 heads.  The cache positions [lo, hi) of its
+// split are visited in steps of 32, by two kinds of waves that work one step
+// apart:
+//  - score waves 0-3, 16 columns each: S^T = C Q^T over a step's 576 cached
+//    features, then the online softmax of their columns; the probabilities
+//    and rescale factors go to LDS.  The cache codes are read as e4m3 bytes
+//    and converted to exact bf16 in registers, and every cache fragment feeds
+//    the MFMAs of both 8-column halves of the wave.
+//  - value waves 4-7, latent block b = wave - 4 (128 features): convert block
+//    b of the previous step's codes into a private transposed bf16 tile, then
+//    O^T[latent, column] += C_b^T (p scale_b)^T for all 64 columns, so every
+//    cache fragment feeds 8 MFMAs.
+// A SIMD holds one wave of each kind, in different phases.  The cache bytes
+// of a step (codes, rotary keys, scales) are copied straight into one of four
+// LDS stages by global_load_lds, two steps ahead; one barrier per step
+// orders the copies, the probabilities of the step before and the reuse of
+// a stage.
 //
-// Sums to fp32 precision: the 16 MFMA columns are 8 heads x {hi, lo}, the
-// bf16 high part of a value and the bf16 rounding of its remainder, so one
-// MFMA gives both halves of the product and the two columns of a head add to
-// it within about 2^-17 relative.  Per 128-latent block b:
-//   S_b^T = C_b Q^T              (codes, query halves; lane: 4 positions x 1 column)
-//   s = sum_b scale_b(pos) S_b + S_rope, the two columns of a head added
-//   online softmax per head
-//   O_b^T [latent, pair column] += C_b^T (p scale_b)^T as two MFMAs on one
-//                                  cache fragment, the high and the low halves
-//                                  of p scale_b; the lane's 8 K slots are
-//                                  positions 4q..4q+3 of the first 16 and of
-//                                  the second 16 (where S^T left them)
-// and finally writes its running max m, sum l and O^T (head x 512) unscaled.
+// Sums to fp32 precision: a score wave's 16 MFMA columns per half are 8
+// columns x {hi, lo}, the bf16 high part of a query and the bf16 rounding of
+// its remainder, so one MFMA gives both halves of the product and the two
+// columns add to it within about 2^-17 relative.  Per 128-latent block b:
+//   S_b^T = C_b Q^T; s = sum_b scale_b(pos) S_b + S_rope
+//   O_b^T += C_b^T (p scale_b)^T as two MFMAs per fragment, the high and the
+//            low bf16 halves of p scale_b
+// and finally O^T (column x 512), the reference maximum m and the sum l are
+// written unscaled for the split merge.
 struct AttnArgs {
   const uint8_t* c_codes;
   const float* c_scales;
   const uint16_t* c_rope;
-  const float* qcat;         // [T, H, 576] fp32, softmax scale folded in
+  const uint16_t* qcat;      // [T, H, 2, 576]: bf16 high parts, then the bf16 roundings of
+                             // the remainders, of the queries with the softmax scale folded in
   const int32_t* cached_len; // [S]
   float* part_o;             // [nsplit, T, H, 512]
   float* part_ml;            // [nsplit, T, H, 2]
@@ -247,67 +241,80 @@ __device__ __forceinline__ float xor8(float v) {
       0, __builtin_bit_cast(int, v), 0x128 /* row_ror:8 */, 0xF, 0xF, false));
 }
 
-constexpr int CT_ELEMS = PT * CT_LD, TR_ELEMS = DL * TR_LD;
-constexpr int HPW = 8;   // heads per wave
-constexpr int AW = 8;    // waves per workgroup
-constexpr int NS = 3;    // LDS stages of raw cache bytes (copies run NS - 1 steps ahead)
-constexpr float LAZY_E = 5.5451774f;   // 8 ln 2: margin before a head's reference maximum moves
+constexpr int AW = 8;        // waves per workgroup
+constexpr int SW = 4;        // score waves (the others are value waves, one per latent block)
+constexpr int ACOLS = 64;    // columns per workgroup
+constexpr int NSR = 4;       // LDS stages of raw cache bytes (copies run two steps ahead)
+constexpr float LAZY_E = 5.5451774f;   // 8 ln 2: margin before a column's reference maximum moves
+// one stage: codes [32][512] (16-byte chunks swizzled by position), rotary
+// keys [32][64] bf16 (chunks swizzled), scales [4][32]
+constexpr int SG_ROPE = PT * DL, SG_SC = SG_ROPE + PT * DR * 2, SG = SG_SC + (DL / QBLK) * PT * 4;
+// probabilities of a column: 32 positions, row stride 36 floats (the 16
+// columns a value wave reads at once fall on distinct banks)
+constexpr int PB_LD = PT + 4;
+// a value wave's transposed bf16 tile: latent rows of 32 positions at a
+// stride of 40 (80 bytes: the 16 rows of a fragment read on distinct banks),
+// 16-row blocks 16 dwords apart in bank (the four blocks a conversion
+// instruction writes do not collide)
+constexpr int TW_LD = PT + 8, TW_BLK = 16 * TW_LD + 32, TW_ELEMS = 8 * TW_BLK;
+
+// slot of the 16-byte code chunk c of stage position p: 16 consecutive
+// positions (a score fragment) and the 16 even or odd positions of a
+// conversion instruction each read 16 distinct bank groups
+__device__ __forceinline__ int code_slot(int c, int p) {
+  return c ^ (((p >> 1) & 15) ^ ((p & 1) << 3));
+}
+
+// 8 e4m3 codes (two dwords) -> 8 exact bf16 values
+__device__ __forceinline__ v8bf codes_bf16(uint2 w) {
+  const uint32_t a = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.f, false));
+  const uint32_t b = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.f, true));
+  const uint32_t c = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.f, false));
+  const uint32_t d = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.f, true));
+  return __builtin_bit_cast(v8bf, make_uint4(a, b, c, d));
+}
 
 __global__ __launch_bounds__(512, 1) void mla_attn_kernel(const AttnArgs g) {
-  // raw stages: codes [pos][512] with the 16-byte chunk c of position p at
-  // chunk slot c ^ ((p / 2) % 16); rotary keys [pos][64] bf16 with chunk c at
-  // slot c ^ ((p / 2) % 8) (both so that 16 consecutive positions read at one
-  // chunk fall on distinct banks); scales [block][pos]
-  __shared__ __attribute__((aligned(16))) uint8_t cr[NS][PT * DL];
-  __shared__ __attribute__((aligned(16))) uint16_t crope[NS][PT * DR];
-  __shared__ __attribute__((aligned(16))) float csc[NS][DL / QBLK][PT];
-  __shared__ __attribute__((aligned(16))) uint16_t ct[CT_ELEMS];   // row-major bf16 latents
-  __shared__ __attribute__((aligned(16))) uint16_t tr[TR_ELEMS];   // transposed bf16 latents
-  __shared__ float xbuf[AW][9][64];   // a wave's probabilities (8) and rescale factor per lane
-  __shared__ int kv_sh[AW], tok_sh[AW], head_sh[AW];
+  __shared__ __attribute__((aligned(16))) uint8_t stg[NSR][SG];
+  __shared__ __attribute__((aligned(16))) uint16_t tw_all[AW - SW][TW_ELEMS];
+  __shared__ __attribute__((aligned(16))) float pbuf[2][ACOLS * PB_LD];
+  __shared__ float abuf[2][ACOLS];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q4 = lane >> 4, l16 = lane & 15;
-  const bool lo_col = l16 >= HPW;           // this lane's column holds the low halves
-  const float lo_f = lo_col ? 1.f : 0.f;
   const int item = blockIdx.x % g.items_per_split, split = blockIdx.x / g.items_per_split;
-  // the wave's token and first head (every wave of a workgroup is on one
-  // sequence; waves past the token count or the head count only convert)
-  int t, h0;
-  bool active;
+
+  // column c -> (token, head); false for columns past the heads or tokens
+  int tok0 = 0, h0 = 0, seq = 0;
   if (g.mode == 0) {
     const int ngrp = g.H / g.hw;
-    t = item / ngrp;
-    h0 = (item % ngrp) * g.hw + wave * HPW;
-    active = wave * HPW < g.hw;
+    tok0 = item / ngrp;
+    h0 = (item % ngrp) * g.hw;
   } else {
-    const int hg_n = g.H / HPW;
-    const int tb_n = (g.n_new + AW - 1) / AW;
-    const int per_seq = tb_n * hg_n;
+    const int hg_n = g.H / 8;
+    const int per_seq = ((g.n_new + 7) / 8) * hg_n;
     const int s_ = item / per_seq, rem = item % per_seq;
-    const int tb = rem / hg_n;
-    h0 = (rem % hg_n) * HPW;
-    const int ti = tb * AW + wave;
-    active = ti < g.n_new;
-    t = s_ * g.n_new + min(ti, g.n_new - 1);
+    tok0 = s_ * g.n_new + (rem / hg_n) * 8;   // first token of the block
+    h0 = (rem % hg_n) * 8;
   }
-  int seq;
-  const int qpos = token_pos(g.cached_len, t, g.n_new, g.max_len, &seq);
-  if (lane == 0) {
-    kv_sh[wave] = active ? qpos + 1 : 0;
-    tok_sh[wave] = t;
-    head_sh[wave] = h0;
-  }
-  __syncthreads();
-  // the workgroup's positions: its split's range, up to its last query position
-  int wg_end = 0;
-#pragma unroll
-  for (int w = 0; w < AW; ++w) wg_end = max(wg_end, kv_sh[w]);
+  auto column = [&](int c, int* t, int* h) -> bool {
+    if (g.mode == 0) {
+      *t = tok0;
+      *h = min(h0 + c, g.H - 1);
+      return c < g.hw;
+    }
+    const int ti = (tok0 % g.n_new) + c / 8;
+    *t = tok0 + min(c / 8, g.n_new - 1 - tok0 % g.n_new);
+    *h = h0 + (c & 7);
+    return ti < g.n_new;
+  };
+  // the workgroup's positions: its split's range, up to the last visible one
+  // of its last token
+  int t_last, h_unused;
+  column(g.mode == 0 ? 0 : ACOLS - 1, &t_last, &h_unused);
+  const int wg_end = token_pos(g.cached_len, t_last, g.n_new, g.max_len, &seq) + 1;
   const int lo = split * g.chunk, hi = min(wg_end, lo + g.chunk);
-  const int my_end = active ? qpos + 1 : 0;
-  const int pm = wave & 1;   // member of the wave pair
-  const int pair_end = max(kv_sh[wave & ~1], kv_sh[wave | 1]);   // 0: both members idle
-  const int h = h0 + (l16 & (HPW - 1));   // this lane's head
+  const int nsteps = lo < hi ? (hi - lo + PT - 1) / PT : 0;
   const size_t cbase = (size_t)seq * g.max_len;
   const uint8_t* codes_seq = g.c_codes + cbase * DL;
   const uint16_t* rope_seq = g.c_rope + cbase * DR;
@@ -315,244 +322,269 @@ __global__ __launch_bounds__(512, 1) void mla_attn_kernel(const AttnArgs g) {
 
   // copies of the step at p0 into stage st; positions past hi copy position
   // hi - 1 (written, finite), which the mask and p = 0 leave without effect.
-  // Wave w: code instructions 2w, 2w + 1 (two positions each); waves 0-3 one
+  // Wave w: code instructions 2w, 2w + 1 (two positions each), waves 0-3 one
   // rotary instruction (8 positions), waves 4-5 one scale instruction (two
   // blocks): 3 copies per step for waves 0-5, 2 for waves 6-7
   const int n_copies = wave < 6 ? 3 : 2;
   auto issue = [&](int st, int p0) {
     const int plast = hi - 1;
+    uint8_t* sb = stg[st];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int i = 2 * wave + u;
-      const int pc = min(p0 + 2 * i + (lane >> 5), plast);
-      const int c = (lane & 31) ^ (i & 15);
-      lds_copy16(codes_seq, (uint32_t)(pc * DL + 16 * c), lds_addr(&cr[st][i * 1024]));
+      const int p = 2 * i + (lane >> 5);
+      const int pc = min(p0 + p, plast);
+      const int c = code_slot(lane & 31, p);   // code_slot is an involution in c
+      lds_copy16(codes_seq, (uint32_t)(pc * DL + 16 * c), lds_addr(sb + i * 1024));
     }
     if (wave < 4) {
       const int p = 8 * wave + (lane >> 3);
       const int pc = min(p0 + p, plast);
       const int c = (lane & 7) ^ ((p >> 1) & 7);
-      lds_copy16(rope_seq, (uint32_t)(pc * DR * 2 + 16 * c), lds_addr(&crope[st][wave * 512]));
+      lds_copy16(rope_seq, (uint32_t)(pc * DR * 2 + 16 * c), lds_addr(sb + SG_ROPE + wave * 1024));
     } else if (wave < 6) {
       const int i = wave - 4, blk = 2 * i + (lane >> 5);
       const int pc = min(p0 + (lane & 31), plast);
-      lds_copy4(sc_seq, (uint32_t)((pc * (DL / QBLK) + blk) * 4), lds_addr(&csc[st][2 * i][0]));
-    }
-  };
-  // stage st's codes -> ct, tr: thread = (16-code chunk sub, position pair pr)
-  auto convert = [&](int st) {
-    const int sub = tid >> 4, pr = tid & 15;
-    uint32_t pk[2][8];   // bf16 pairs: codes 2k, 2k+1 of position 2 pr + j
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const uint4 cv =
-          *reinterpret_cast<const uint4*>(&cr[st][(2 * pr + j) * DL + 16 * (sub ^ pr)]);
-      const uint32_t w4[4] = {cv.x, cv.y, cv.z, cv.w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        pk[j][2 * k] = __builtin_bit_cast(
-            uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w4[k], 1.f, false));
-        pk[j][2 * k + 1] = __builtin_bit_cast(
-            uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w4[k], 1.f, true));
-      }
-      uint4* dst = reinterpret_cast<uint4*>(&ct[(2 * pr + j) * CT_LD + 16 * sub]);
-      dst[0] = make_uint4(pk[j][0], pk[j][1], pk[j][2], pk[j][3]);
-      dst[1] = make_uint4(pk[j][4], pk[j][5], pk[j][6], pk[j][7]);
-    }
-    // transposed: feature 16 sub + i, positions 2 pr and 2 pr + 1 (i is a
-    // compile-time index: a per-thread index into pk would become select
-    // chains over all its registers)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int w = i >> 1;
-      const uint32_t v = (i & 1) ? ((pk[0][w] >> 16) | (pk[1][w] & 0xFFFF0000u))
-                                 : ((pk[0][w] & 0xFFFFu) | (pk[1][w] << 16));
-      *reinterpret_cast<uint32_t*>(&tr[(16 * sub + i) * TR_LD + 2 * pr]) = v;
+      lds_copy4(sc_seq, (uint32_t)((pc * (DL / QBLK) + blk) * 4),
+                lds_addr(sb + SG_SC + 2 * i * PT * 4));
     }
   };
 
-  // the query of head h as B fragments, high or low halves by column (dims
-  // 32 ks + 8 q4 .. + 7)
-  v8bf qb[DQ / 32];
-  v4f o[DL / 32];   // pair column l mod 16, latents 256 pm + 16 nt + 4 q4 + i
-  float mrun = -INFINITY, lrun = 0.f;
+  // probabilities start at 0 and rescale factors at 1 (columns no score wave
+  // owns keep them)
+  for (int i = tid; i < 2 * ACOLS * PB_LD; i += AW * 64) (&pbuf[0][0])[i] = 0.f;
+  if (tid < 2 * ACOLS) (&abuf[0][0])[tid] = 1.f;
+  if (nsteps > 0) issue(0, lo);
+  if (nsteps > 1) issue(1, lo + PT);
+
+  if (wave < SW) {
+    // ------------------------------------------------------ score wave
+    // column of this lane in half ct: 16 wave + 8 ct + l16 % 8, high query
+    // halves in lanes l16 < 8, low halves in l16 >= 8 (a column past the
+    // heads or tokens reads a valid query and is masked)
+    int ctok[2], chead[2], cend[2];
+    bool cact[2];
 #pragma unroll
-  for (int i = 0; i < DL / 32; ++i) o[i] = v4f{0.f, 0.f, 0.f, 0.f};
-  if (active) {
-    const float* qp = g.qcat + ((size_t)t * g.H + h) * DQ + 8 * q4;
-#pragma unroll
-    for (int ks = 0; ks < DQ / 32; ++ks) {
-      const float4 a = *reinterpret_cast<const float4*>(qp + 32 * ks);
-      const float4 c = *reinterpret_cast<const float4*>(qp + 32 * ks + 4);
-      const uint4 v = make_uint4(bf16_half2(a.x, a.y, lo_f), bf16_half2(a.z, a.w, lo_f),
-                                 bf16_half2(c.x, c.y, lo_f), bf16_half2(c.z, c.w, lo_f));
-      qb[ks] = __builtin_bit_cast(v8bf, v);
+    for (int ct = 0; ct < 2; ++ct) {
+      cact[ct] = column(16 * wave + 8 * ct + (l16 & 7), &ctok[ct], &chead[ct]);
+      int sq;
+      cend[ct] = cact[ct] ? token_pos(g.cached_len, ctok[ct], g.n_new, g.max_len, &sq) + 1 : 0;
     }
-  }
-  // scores and online softmax of the wave's 8 heads; ps, alpha: the lane's
-  // probabilities and the rescale factor of its head
-  auto scores = [&](int st, int p0, float (&ps)[2][4], float& alpha) {
-    // ---- scores: S^T[pos, column] for positions p0 + 16 pt + 4 q4 + i
-    v4f s[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    const bool wave_on = __builtin_amdgcn_readfirstlane(
+                             (int)(__builtin_amdgcn_ballot_w64(cact[0] || cact[1]) != 0)) != 0;
+    // the queries as B fragments (dims 32 ks + 8 q4 .. + 7)
+    v8bf qb[2][DQ / 32];
 #pragma unroll
-    for (int blk = 0; blk <= DL / QBLK; ++blk) {   // four latent blocks, then the rotary key
+    for (int ct = 0; ct < 2; ++ct) {
+      const uint16_t* qp = g.qcat + ((size_t)ctok[ct] * g.H + chead[ct]) * (2 * DQ) +
+                           (l16 >= 8 ? DQ : 0) + 8 * q4;
+#pragma unroll
+      for (int ks = 0; ks < DQ / 32; ++ks)
+        qb[ct][ks] = *reinterpret_cast<const v8bf*>(qp + 32 * ks);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
+    float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.f, 0.f};
+
+    for (int j = 0; j <= nsteps; ++j) {
+      if (j < nsteps) vm_wait(j + 1 < nsteps ? n_copies : 0);
+      __syncthreads();
+      if (j + 2 < nsteps) issue((j + 2) % NSR, lo + (j + 2) * PT);
+      if (j == nsteps || !wave_on) continue;
+      const uint8_t* sb = stg[j % NSR];
+      const float* scb = reinterpret_cast<const float*>(sb + SG_SC);
+      const int p0 = lo + j * PT;
+      // S^T[pos, column] for positions p0 + 16 pt + 4 q4 + i
+      v4f s[2][2];
 #pragma unroll
       for (int pt = 0; pt < 2; ++pt) {
-        v4f acc = {0.f, 0.f, 0.f, 0.f};
+        s[pt][0] = v4f{0.f, 0.f, 0.f, 0.f};
+        s[pt][1] = s[pt][0];
         const int p = 16 * pt + l16;
-        if (blk < DL / QBLK) {
-          const uint16_t* ap = &ct[p * CT_LD + 8 * q4];
+        const uint8_t* rowp = sb + p * DL + 8 * (q4 & 1);
 #pragma unroll
-          for (int ks = blk * 4; ks < blk * 4 + 4; ++ks) {
-            const uint4 av = *reinterpret_cast<const uint4*>(ap + 32 * ks);
-            acc = mfma_bf16(__builtin_bit_cast(v8bf, av), qb[ks], acc);
+        for (int blk = 0; blk < DL / QBLK; ++blk) {
+          v4f a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) {
+            const int ks = 4 * blk + kk;
+            const uint2 w = *reinterpret_cast<const uint2*>(
+                rowp + 16 * code_slot(2 * ks + (q4 >> 1), p));
+            const v8bf a = codes_bf16(w);
+            a0 = mfma_bf16(a, qb[0][ks], a0);
+            a1 = mfma_bf16(a, qb[1][ks], a1);
           }
-        } else {
+          const float4 sc = *reinterpret_cast<const float4*>(scb + blk * PT + 16 * pt + 4 * q4);
+          s[pt][0][0] = fmaf(sc.x, a0[0], s[pt][0][0]);
+          s[pt][0][1] = fmaf(sc.y, a0[1], s[pt][0][1]);
+          s[pt][0][2] = fmaf(sc.z, a0[2], s[pt][0][2]);
+          s[pt][0][3] = fmaf(sc.w, a0[3], s[pt][0][3]);
+          s[pt][1][0] = fmaf(sc.x, a1[0], s[pt][1][0]);
+          s[pt][1][1] = fmaf(sc.y, a1[1], s[pt][1][1]);
+          s[pt][1][2] = fmaf(sc.z, a1[2], s[pt][1][2]);
+          s[pt][1][3] = fmaf(sc.w, a1[3], s[pt][1][3]);
+          // operand reads stay with their block
+          __builtin_amdgcn_sched_barrier(0);
+        }
 #pragma unroll
-          for (int ks = DL / 32; ks < DQ / 32; ++ks) {
-            const int c = 4 * (ks - DL / 32) + q4;   // rotary chunk of 8 features
-            const uint4 av = *reinterpret_cast<const uint4*>(
-                &crope[st][p * DR + 8 * (c ^ ((p >> 1) & 7))]);
-            acc = mfma_bf16(__builtin_bit_cast(v8bf, av), qb[ks], acc);
+        for (int kr = 0; kr < DR / 32; ++kr) {
+          const int c = 4 * kr + q4;   // rotary chunk of 8 features
+          const v8bf a = *reinterpret_cast<const v8bf*>(sb + SG_ROPE + p * DR * 2 +
+                                                        16 * (c ^ ((p >> 1) & 7)));
+          s[pt][0] = mfma_bf16(a, qb[0][DL / 32 + kr], s[pt][0]);
+          s[pt][1] = mfma_bf16(a, qb[1][DL / 32 + kr], s[pt][1]);
+        }
+      }
+      // per half: the two columns of a pair add to its score; mask; lazy
+      // reference maximum; probabilities
+      float* pb = pbuf[j & 1];
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        float v[8];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int pos = p0 + 16 * pt + 4 * q4 + i;
+            float x = s[pt][ct][i] + xor8(s[pt][ct][i]);
+            if (pos >= cend[ct] || pos >= hi) x = -INFINITY;
+            v[4 * pt + i] = x;
+            mx = fmaxf(mx, x);
           }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        // the reference maximum moves only when the step's maximum passes it
+        // by more than LAZY_E, so the probabilities stay below e^LAZY_E and
+        // the outputs are rarely rescaled; the merge and the normalisation use
+        // the same reference, which cancels.  A column that has seen no
+        // position yet keeps p = 0.
+        const float mnew = mx > mrun[ct] + LAZY_E ? mx : mrun[ct];
+        const bool none = mnew == -INFINITY;
+        const float alpha = none ? 1.f : __expf(mrun[ct] - mnew);
+        float lsum = 0.f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          v[k] = none ? 0.f : __expf(v[k] - mnew);
+          lsum += v[k];
         }
-        if (blk < DL / QBLK) {
-          const float4 sc = *reinterpret_cast<const float4*>(&csc[st][blk][16 * pt + 4 * q4]);
-          s[pt][0] = fmaf(sc.x, acc[0], s[pt][0]);
-          s[pt][1] = fmaf(sc.y, acc[1], s[pt][1]);
-          s[pt][2] = fmaf(sc.z, acc[2], s[pt][2]);
-          s[pt][3] = fmaf(sc.w, acc[3], s[pt][3]);
-        } else {
-          s[pt] += acc;
+        lrun[ct] = lrun[ct] * alpha + lsum;
+        mrun[ct] = mnew;
+        if (l16 < 8) {
+          const int c = 16 * wave + 8 * ct + l16;
+#pragma unroll
+          for (int pt = 0; pt < 2; ++pt)
+            *reinterpret_cast<float4*>(&pb[c * PB_LD + 16 * pt + 4 * q4]) =
+                make_float4(v[4 * pt], v[4 * pt + 1], v[4 * pt + 2], v[4 * pt + 3]);
+          if (q4 == 0) abuf[j & 1][c] = alpha;
         }
-        // operand reads stay with their block (hoisting all 18 at once would
-        // exceed the register budget)
-        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // the head's two columns (high and low query halves) add to its score
+    // m and l of each column (the four lanes of a column add their sums)
 #pragma unroll
-    for (int pt = 0; pt < 2; ++pt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s[pt][i] += xor8(s[pt][i]);
-    // causal mask and the step's maximum for head h (position p0 <= qpos is
-    // visible, so the maximum is finite)
-    float mx = -INFINITY;
-#pragma unroll
-    for (int pt = 0; pt < 2; ++pt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int p = p0 + 16 * pt + 4 * q4 + i;
-        if (p >= my_end || p >= hi) s[pt][i] = -INFINITY;
-        mx = fmaxf(mx, s[pt][i]);
+    for (int ct = 0; ct < 2; ++ct) {
+      float ltot = lrun[ct] + __shfl_xor(lrun[ct], 16);
+      ltot += __shfl_xor(ltot, 32);
+      if (cact[ct] && l16 < 8 && q4 == 0) {
+        const size_t pidx = ((size_t)split * g.T + ctok[ct]) * g.H + chead[ct];
+        g.part_ml[pidx * 2] = mrun[ct];
+        g.part_ml[pidx * 2 + 1] = ltot;
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    // the reference maximum moves only when the step's maximum passes it by
-    // more than LAZY_E, so the probabilities stay below e^LAZY_E and the
-    // outputs are rarely rescaled; the merge and the final normalisation
-    // use the same reference, which cancels exactly
-    const float mnew = mx > mrun + LAZY_E ? mx : mrun;
-    alpha = __expf(mrun - mnew);
-    float lsum = 0.f;
-#pragma unroll
-    for (int pt = 0; pt < 2; ++pt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        ps[pt][i] = __expf(s[pt][i] - mnew);
-        lsum += ps[pt][i];
-      }
-    // each lane keeps the sum over its own positions; the four lanes of a
-    // column are added once, at the end
-    lrun = lrun * alpha + lsum;
-    mrun = mnew;
-  };
-  // value sum of the pair's 16 columns over latents 256 pm .. + 255: column
-  // l mod 16 belongs to member (l mod 16) / 8, whose lane l holds its
-  // probabilities at the same positions
-  auto values = [&](int st) {
-    const bool own = (l16 >> 3) == pm;
-    float v[2][4];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) v[j >> 2][j & 3] = xbuf[own ? wave : wave ^ 1][j][lane];
-    const float a_col = xbuf[own ? wave : wave ^ 1][8][lane];
-    // rescale only when some column's reference moved (alpha = 1 leaves them)
-    if (__any(a_col != 1.f)) {
-#pragma unroll
-      for (int nt = 0; nt < DL / 32; ++nt) o[nt] *= a_col;
     }
+  } else {
+    // ------------------------------------------------------ value wave
+    const int b = wave - SW;   // latent block
+    uint16_t* tw = tw_all[b];
+    v4f o[8][4];   // O^T: latent 128 b + 16 r + 4 q4 + i, column 16 c4 + l16
 #pragma unroll
-    for (int bb = 0; bb < 2; ++bb) {
-      const int blk = 2 * pm + bb;
-      // B: the 8 positions 4 q4 .. + 3 of both 16-position groups, high
-      // halves (pbh) and low halves (pbl); one A fragment feeds both
-      uint32_t hv[4], lv[4];
+    for (int r = 0; r < 8; ++r)
 #pragma unroll
-      for (int pt = 0; pt < 2; ++pt) {
-        const float4 sc = *reinterpret_cast<const float4*>(&csc[st][blk][16 * pt + 4 * q4]);
-        const float x0 = v[pt][0] * sc.x, x1 = v[pt][1] * sc.y;
-        const float x2 = v[pt][2] * sc.z, x3 = v[pt][3] * sc.w;
-        hv[2 * pt] = pack_bf16(x0, x1);
-        hv[2 * pt + 1] = pack_bf16(x2, x3);
-        lv[2 * pt] = bf16_half2(x0, x1, 1.f);
-        lv[2 * pt + 1] = bf16_half2(x2, x3, 1.f);
-      }
-      const v8bf pbh = __builtin_bit_cast(v8bf, make_uint4(hv[0], hv[1], hv[2], hv[3]));
-      const v8bf pbl = __builtin_bit_cast(v8bf, make_uint4(lv[0], lv[1], lv[2], lv[3]));
-#pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
-        const uint16_t* tp = &tr[(16 * (8 * blk + nt) + l16) * TR_LD + 4 * q4];
-        const uint2 a0 = *reinterpret_cast<const uint2*>(tp);
-        const uint2 a1 = *reinterpret_cast<const uint2*>(tp + 16);
-        const v8bf av = __builtin_bit_cast(v8bf, make_uint4(a0.x, a0.y, a1.x, a1.y));
-        o[8 * bb + nt] = mfma_bf16(av, pbh, o[8 * bb + nt]);
-        o[8 * bb + nt] = mfma_bf16(av, pbl, o[8 * bb + nt]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
+      for (int c4 = 0; c4 < 4; ++c4) o[r][c4] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // step k: wait for its copies, barrier (they are visible, and step k - 1's
-  // compute is done with ct, tr and stage (k - 1) % NS), copy step k + NS - 1
-  // into that stage, convert, barrier, compute
-  const int nsteps = lo < hi ? (hi - lo + PT - 1) / PT : 0;
-  for (int j = 0; j < NS - 1 && j < nsteps; ++j) issue(j, lo + j * PT);
-  for (int k = 0; k < nsteps; ++k) {
-    const int st = k % NS, p0 = lo + k * PT;
-    vm_wait(n_copies * min(NS - 2, nsteps - 1 - k));
-    __syncthreads();
-    if (k + NS - 1 < nsteps) issue((k + NS - 1) % NS, p0 + (NS - 1) * PT);
-    convert(st);
-    __syncthreads();
-    // scores (waves whose token sees this step), exchange, values (pairs
-    // with a member that sees it; an idle member contributes p = 0)
-    float ps[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    float alpha = 1.f;
-    if (active && p0 < my_end) scores(st, p0, ps, alpha);
+    for (int j = 0; j <= nsteps; ++j) {
+      if (j < nsteps) vm_wait(j + 1 < nsteps ? n_copies : 0);
+      __syncthreads();
+      if (j + 2 < nsteps) issue((j + 2) % NSR, lo + (j + 2) * PT);
+      if (j == 0) continue;
+      // step j - 1
+      const uint8_t* sb = stg[(j - 1) % NSR];
+      const float* scb = reinterpret_cast<const float*>(sb + SG_SC);
+      // block b's codes -> tw: lane = (position pair l16, chunk (lane / 16) +
+      // 4 k of the block); row 16 cl + e holds latent 128 b + 16 cl + e at
+      // positions 0..31
 #pragma unroll
-    for (int j = 0; j < 8; ++j) xbuf[wave][j][lane] = ps[j >> 2][j & 3];
-    xbuf[wave][8][lane] = alpha;
-    __syncthreads();
-    if (p0 < pair_end) values(st);
-  }
-  if (pair_end == 0) return;
-  // lane l writes O^T of pair column l mod 16 (when its member is active),
-  // latent features 256 pm + 16 nt + 4 q4 + i
-  const int cw = (wave & ~1) | (l16 >> 3);
-  if (kv_sh[cw] > 0) {
-    const size_t cidx = ((size_t)split * g.T + tok_sh[cw]) * g.H + head_sh[cw] + (l16 & 7);
-    float* po = g.part_o + cidx * DL + 256 * pm;
+      for (int k = 0; k < 2; ++k) {
+        const int cl = q4 + 4 * k, c = 8 * b + cl;
+        uint32_t pk[2][8];   // bf16 pairs: codes 2e, 2e + 1 of position 2 l16 + jj
 #pragma unroll
-    for (int nt = 0; nt < DL / 32; ++nt)
-      *reinterpret_cast<float4*>(po + 16 * nt + 4 * q4) =
-          make_float4(o[nt][0], o[nt][1], o[nt][2], o[nt][3]);
-  }
-  float ltot = lrun + __shfl_xor(lrun, 16);
-  ltot += __shfl_xor(ltot, 32);
-  if (active && !lo_col && q4 == 0) {
-    const size_t pidx = ((size_t)split * g.T + t) * g.H + h;
-    g.part_ml[pidx * 2] = mrun;
-    g.part_ml[pidx * 2 + 1] = ltot;
+        for (int jj = 0; jj < 2; ++jj) {
+          const int p = 2 * l16 + jj;
+          const uint4 cv = *reinterpret_cast<const uint4*>(sb + p * DL + 16 * code_slot(c, p));
+          const uint32_t w4[4] = {cv.x, cv.y, cv.z, cv.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            pk[jj][2 * e] = __builtin_bit_cast(
+                uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w4[e], 1.f, false));
+            pk[jj][2 * e + 1] = __builtin_bit_cast(
+                uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w4[e], 1.f, true));
+          }
+        }
+        uint16_t* dst = tw + cl * TW_BLK + 2 * l16;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int w = e >> 1;
+          const uint32_t v = (e & 1) ? ((pk[0][w] >> 16) | (pk[1][w] & 0xFFFF0000u))
+                                     : ((pk[0][w] & 0xFFFFu) | (pk[1][w] << 16));
+          *reinterpret_cast<uint32_t*>(dst + e * TW_LD) = v;
+        }
+      }
+      // (the tile is this wave's: its own writes above precede its reads)
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      // B: p scale_b at positions 8 q4 .. + 7 of column 16 c4 + l16, as high
+      // and low bf16 halves
+      const float* pb = pbuf[(j - 1) & 1];
+      const float4 s0 = *reinterpret_cast<const float4*>(scb + b * PT + 8 * q4);
+      const float4 s1 = *reinterpret_cast<const float4*>(scb + b * PT + 8 * q4 + 4);
+      v8bf ph[4], pl[4];
+      float al[4];
+      bool moved = false;
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) {
+        const float* pr = pb + (16 * c4 + l16) * PB_LD + 8 * q4;
+        const float4 x0 = *reinterpret_cast<const float4*>(pr);
+        const float4 x1 = *reinterpret_cast<const float4*>(pr + 4);
+        split8(make_float4(x0.x * s0.x, x0.y * s0.y, x0.z * s0.z, x0.w * s0.w),
+               make_float4(x1.x * s1.x, x1.y * s1.y, x1.z * s1.z, x1.w * s1.w), &ph[c4], &pl[c4]);
+        al[c4] = abuf[(j - 1) & 1][16 * c4 + l16];
+        moved = moved || al[c4] != 1.f;
+      }
+      // rescale only when some column's reference moved (alpha = 1 leaves them)
+      if (__builtin_amdgcn_ballot_w64(moved) != 0) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+#pragma unroll
+          for (int c4 = 0; c4 < 4; ++c4) o[r][c4] *= al[c4];
+      }
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const v8bf a = *reinterpret_cast<const v8bf*>(tw + r * TW_BLK + l16 * TW_LD + 8 * q4);
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) o[r][c4] = mfma_bf16(a, ph[c4], o[r][c4]);
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) o[r][c4] = mfma_bf16(a, pl[c4], o[r][c4]);
+      }
+    }
+    // O^T of the columns this workgroup owns
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4) {
+      int t, h;
+      if (!column(16 * c4 + l16, &t, &h)) continue;
+      float* po = g.part_o + (((size_t)split * g.T + t) * g.H + h) * DL + QBLK * b + 4 * q4;
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+        *reinterpret_cast<float4*>(po + 16 * r) =
+            make_float4(o[r][c4][0], o[r][c4][1], o[r][c4][2], o[r][c4][3]);
+    }
   }
 }
 
@@ -604,7 +636,7 @@ __global__ __launch_bounds__(256) void mla_qabsorb_kernel(
     const uint16_t* __restrict__ ukt,
     const float* __restrict__ s_kvb, const double* __restrict__ inv_freq,
     const int32_t* __restrict__ cached_len, int n_new, int max_len,
-    float* __restrict__ qcat) {
+    uint16_t* __restrict__ qcat) {
   constexpr int MT = TB / 16;
   const int h = blockIdx.x, t0 = blockIdx.y * TB, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, q4 = lane >> 4, l16 = lane & 15;
@@ -654,9 +686,13 @@ __global__ __launch_bounds__(256) void mla_qabsorb_kernel(
     for (int i = 0; i < 4; ++i) {
       const int t = t0 + 16 * mt + 4 * q4 + i;
       if (t >= T) continue;
-      float* dst = qcat + ((size_t)t * H + h) * DQ + 128 * wave + l16;
+      uint16_t* dst = qcat + ((size_t)t * H + h) * (2 * DQ) + 128 * wave + l16;
 #pragma unroll
-      for (int ct = 0; ct < 8; ++ct) dst[16 * ct] = acc[mt][ct][i] * sk * smscale;
+      for (int ct = 0; ct < 8; ++ct) {
+        const float v = acc[mt][ct][i] * sk * smscale;
+        dst[16 * ct] = (uint16_t)bf16_half2(v, 0.f, 0.f);
+        dst[DQ + 16 * ct] = (uint16_t)bf16_half2(v, 0.f, 1.f);
+      }
     }
   // rotary part: thread (token tt, pair i)
   for (int i = tid; i < TB * (DR / 2); i += 256) {
@@ -672,9 +708,9 @@ __global__ __launch_bounds__(256) void mla_qabsorb_kernel(
     }
     float ra, rb;
     rope_pair(qa, qb, pos, inv_freq[pr], &ra, &rb);
-    float* dst = qcat + ((size_t)t * H + h) * DQ + DL;
-    dst[2 * pr] = ra * smscale;
-    dst[2 * pr + 1] = rb * smscale;
+    uint32_t* dst = reinterpret_cast<uint32_t*>(qcat + ((size_t)t * H + h) * (2 * DQ) + DL) + pr;
+    dst[0] = bf16_half2(ra * smscale, rb * smscale, 0.f);
+    dst[DQ / 2] = bf16_half2(ra * smscale, rb * smscale, 1.f);
   }
 }
 
@@ -847,7 +883,7 @@ hipError_t launch_mla_pack_ukv(int H, const uint8_t* w_kvb, uint16_t* ukt, uint1
 
 hipError_t launch_mla_qabsorb(int T, int H, int nsplit, float smscale, const float* q,
                               const uint16_t* ukt, const float* s_kvb, const double* inv_freq,
-                              const int32_t* cached_len, int n_new, int max_len, float* qcat,
+                              const int32_t* cached_len, int n_new, int max_len, uint16_t* qcat,
                               hipStream_t s) {
   // 16-token tiles while 32-token ones would leave CUs idle
   if ((long)H * ((T + 31) / 32) < 256) {
@@ -864,7 +900,7 @@ hipError_t launch_mla_qabsorb(int T, int H, int nsplit, float smscale, const flo
 
 hipError_t launch_mla_attn(int T, int H, int n_seq, int n_new, int max_len, int nsplit,
                            int chunk, const uint8_t* c_codes, const float* c_scales,
-                           const uint16_t* c_rope, const float* qcat,
+                           const uint16_t* c_rope, const uint16_t* qcat,
                            const int32_t* cached_len, float* part_o, float* part_ml,
                            hipStream_t s) {
   AttnArgs a{};

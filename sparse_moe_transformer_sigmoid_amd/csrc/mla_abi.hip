@@ -338,7 +338,7 @@ moe_status run_mla(const mla_config* cfg, int32_t S, int32_t n, int32_t L, const
   float* part = at<float>(ws, W.part);
   uint8_t* qa_q = at<uint8_t>(ws, W.qa_q);
   float* qa_s = at<float>(ws, W.qa_s);
-  float* qcat = at<float>(ws, W.qcat);
+  uint16_t* qcat = at<uint16_t>(ws, W.qcat);
   float* part_o = at<float>(ws, W.part_o);
   float* part_ml = at<float>(ws, W.part_ml);
   uint8_t* o_q = at<uint8_t>(ws, W.o_q);

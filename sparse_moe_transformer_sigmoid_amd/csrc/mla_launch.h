@@ -33,11 +33,13 @@ hipError_t launch_mla_latent(int T, int nsplit, int q_lora, int qkv_ld, float ep
 // rows transposed), uv [H][128][512] (value rows), uk [H][128][512] (key rows)
 hipError_t launch_mla_pack_ukv(int H, const uint8_t* w_kvb, uint16_t* ukt, uint16_t* uv,
                               uint16_t* uk, hipStream_t s);
-// q: nsplit K-slice partial sums [nsplit, T, H * 192] of the q_b projection
+// q: nsplit K-slice partial sums [nsplit, T, H * 192] of the q_b projection;
+// qcat [T, H, 2, 576]: the absorbed queries (softmax scale folded in) as their
+// bf16 high parts, then the bf16 roundings of the remainders
 hipError_t launch_mla_qabsorb(int T, int H, int nsplit, float smscale, const float* q,
                               const uint16_t* ukt,
                               const float* s_kvb, const double* inv_freq,
-                              const int32_t* cached_len, int n_new, int max_len, float* qcat,
+                              const int32_t* cached_len, int n_new, int max_len, uint16_t* qcat,
                               hipStream_t s);
 // work items per position split of the attention kernel, and its mode:
 // mode 0 (one new token per sequence and heads a multiple of min(heads, 64)):
@@ -56,7 +58,7 @@ inline int mla_attn_items(int T, int H, int n_seq, int n_new, int* mode, int* hw
 }
 hipError_t launch_mla_attn(int T, int H, int n_seq, int n_new, int max_len, int nsplit,
                            int chunk, const uint8_t* c_codes, const float* c_scales,
-                           const uint16_t* c_rope, const float* qcat,
+                           const uint16_t* c_rope, const uint16_t* qcat,
                            const int32_t* cached_len, float* part_o, float* part_ml,
                            hipStream_t s);
 // Per-head attention for prompt-sized batches (mla_mha.hip): the keys and
