@@ -246,9 +246,12 @@ constexpr int SW = 4;        // score waves (the others are value waves, one per
 constexpr int ACOLS = 64;    // columns per workgroup
 constexpr int NSR = 4;       // LDS stages of raw cache bytes (copies run two steps ahead)
 constexpr float LAZY_E = 5.5451774f;   // 8 ln 2: margin before a column's reference maximum moves
-// one stage: codes [32][512] (16-byte chunks swizzled by position), rotary
-// keys [32][64] bf16 (chunks swizzled), scales [4][32]
-constexpr int SG_ROPE = PT * DL, SG_SC = SG_ROPE + PT * DR * 2, SG = SG_SC + (DL / QBLK) * PT * 4;
+// one stage: codes of 16 position pairs, each pair's two 512-byte rows
+// followed by 16 bytes of padding; rotary keys [32][64] bf16 (chunks
+// swizzled); scales [4][32]
+constexpr int CPAIR = 2 * DL + 16;
+constexpr int SG_ROPE = (PT / 2) * CPAIR, SG_SC = SG_ROPE + PT * DR * 2,
+              SG = SG_SC + (DL / QBLK) * PT * 4;
 // probabilities of a column: 32 positions, row stride 36 floats (the 16
 // columns a value wave reads at once fall on distinct banks)
 constexpr int PB_LD = PT + 4;
@@ -258,11 +261,14 @@ constexpr int PB_LD = PT + 4;
 // instruction writes do not collide)
 constexpr int TW_LD = PT + 8, TW_BLK = 16 * TW_LD + 32, TW_ELEMS = 8 * TW_BLK;
 
-// slot of the 16-byte code chunk c of stage position p: 16 consecutive
-// positions (a score fragment) and the 16 even or odd positions of a
-// conversion instruction each read 16 distinct bank groups
-__device__ __forceinline__ int code_slot(int c, int p) {
-  return c ^ (((p >> 1) & 15) ^ ((p & 1) << 3));
+// byte offset in a stage of the 16-byte code chunk c of position p: the pair
+// padding puts consecutive pairs 4 banks apart, and an odd position's chunks
+// are swapped in halves of 8 (slot c ^ 8), so 16 consecutive positions (a
+// score fragment) and the 16 even or odd positions of a conversion
+// instruction read distinct banks.  The swap only adds or subtracts 128
+// bytes, so a fragment's address is a per-lane base plus a constant.
+__device__ __forceinline__ int code_off(int c, int p) {
+  return (p >> 1) * CPAIR + (p & 1) * DL + 16 * (c ^ ((p & 1) << 3));
 }
 
 // 8 e4m3 codes (two dwords) -> 8 exact bf16 values
@@ -334,8 +340,8 @@ __global__ __launch_bounds__(512, 1) void mla_attn_kernel(const AttnArgs g) {
       const int i = 2 * wave + u;
       const int p = 2 * i + (lane >> 5);
       const int pc = min(p0 + p, plast);
-      const int c = code_slot(lane & 31, p);   // code_slot is an involution in c
-      lds_copy16(codes_seq, (uint32_t)(pc * DL + 16 * c), lds_addr(sb + i * 1024));
+      const int c = (lane & 31) ^ ((lane >> 5) << 3);   // the chunk that lands in slot lane % 32
+      lds_copy16(codes_seq, (uint32_t)(pc * DL + 16 * c), lds_addr(sb + i * CPAIR));
     }
     if (wave < 4) {
       const int p = 8 * wave + (lane >> 3);
@@ -393,27 +399,52 @@ __global__ __launch_bounds__(512, 1) void mla_attn_kernel(const AttnArgs g) {
       const uint8_t* sb = stg[j % NSR];
       const float* scb = reinterpret_cast<const float*>(sb + SG_SC);
       const int p0 = lo + j * PT;
-      // S^T[pos, column] for positions p0 + 16 pt + 4 q4 + i
+      // S^T[pos, column] for positions p0 + 16 pt + 4 q4 + i, in ten fragment
+      // groups per step: for each 16-position tile pt, the four latent blocks
+      // (four e4m3 fragments each) and the rotary key (two bf16 fragments);
+      // group u + 1's fragments are read while group u's MFMAs run
+      // (a group's fragments: four e4m3 ones, 2 dwords each, or two bf16
+      // rotary ones, 4 dwords each)
+      auto kload = [&](int u, uint2 (&w)[4]) {
+        const int pt = u / 5, k = u % 5, p = 16 * pt + l16;
+        if (k < DL / QBLK) {
+          // chunk c = 8 k + 2 kk + q4 / 2: bit 3 of c is k % 2, so its slot
+          // c ^ 8 (p % 2) is c + 8 (p % 2) for even k, c - 8 (p % 2) for odd k
+          const int odd = (p & 1) * 128;
+          const uint8_t* rowp = sb + (p >> 1) * CPAIR + (p & 1) * DL + 8 * (q4 & 1) +
+                                16 * (q4 >> 1) + ((k & 1) ? -odd : odd);
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk)
+            w[kk] = *reinterpret_cast<const uint2*>(rowp + 16 * (8 * k + 2 * kk));
+        } else {
+#pragma unroll
+          for (int kr = 0; kr < DR / 32; ++kr) {
+            const uint4 r = *reinterpret_cast<const uint4*>(
+                sb + SG_ROPE + p * DR * 2 + 16 * ((4 * kr + q4) ^ ((p >> 1) & 7)));
+            w[2 * kr] = make_uint2(r.x, r.y);
+            w[2 * kr + 1] = make_uint2(r.z, r.w);
+          }
+        }
+      };
       v4f s[2][2];
 #pragma unroll
-      for (int pt = 0; pt < 2; ++pt) {
-        s[pt][0] = v4f{0.f, 0.f, 0.f, 0.f};
-        s[pt][1] = s[pt][0];
-        const int p = 16 * pt + l16;
-        const uint8_t* rowp = sb + p * DL + 8 * (q4 & 1);
+      for (int pt = 0; pt < 2; ++pt) s[pt][0] = s[pt][1] = v4f{0.f, 0.f, 0.f, 0.f};
+      uint2 wc[4], wn[4];
+      kload(0, wc);
 #pragma unroll
-        for (int blk = 0; blk < DL / QBLK; ++blk) {
+      for (int u = 0; u < 10; ++u) {
+        if (u + 1 < 10) kload(u + 1, wn);
+        __builtin_amdgcn_sched_barrier(0);
+        const int pt = u / 5, k = u % 5;
+        if (k < DL / QBLK) {
           v4f a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
 #pragma unroll
           for (int kk = 0; kk < 4; ++kk) {
-            const int ks = 4 * blk + kk;
-            const uint2 w = *reinterpret_cast<const uint2*>(
-                rowp + 16 * code_slot(2 * ks + (q4 >> 1), p));
-            const v8bf a = codes_bf16(w);
-            a0 = mfma_bf16(a, qb[0][ks], a0);
-            a1 = mfma_bf16(a, qb[1][ks], a1);
+            const v8bf a = codes_bf16(wc[kk]);
+            a0 = mfma_bf16(a, qb[0][4 * k + kk], a0);
+            a1 = mfma_bf16(a, qb[1][4 * k + kk], a1);
           }
-          const float4 sc = *reinterpret_cast<const float4*>(scb + blk * PT + 16 * pt + 4 * q4);
+          const float4 sc = *reinterpret_cast<const float4*>(scb + k * PT + 16 * pt + 4 * q4);
           s[pt][0][0] = fmaf(sc.x, a0[0], s[pt][0][0]);
           s[pt][0][1] = fmaf(sc.y, a0[1], s[pt][0][1]);
           s[pt][0][2] = fmaf(sc.z, a0[2], s[pt][0][2]);
@@ -422,16 +453,18 @@ __global__ __launch_bounds__(512, 1) void mla_attn_kernel(const AttnArgs g) {
           s[pt][1][1] = fmaf(sc.y, a1[1], s[pt][1][1]);
           s[pt][1][2] = fmaf(sc.z, a1[2], s[pt][1][2]);
           s[pt][1][3] = fmaf(sc.w, a1[3], s[pt][1][3]);
-          // operand reads stay with their block
-          __builtin_amdgcn_sched_barrier(0);
-        }
+        } else {
 #pragma unroll
-        for (int kr = 0; kr < DR / 32; ++kr) {
-          const int c = 4 * kr + q4;   // rotary chunk of 8 features
-          const v8bf a = *reinterpret_cast<const v8bf*>(sb + SG_ROPE + p * DR * 2 +
-                                                        16 * (c ^ ((p >> 1) & 7)));
-          s[pt][0] = mfma_bf16(a, qb[0][DL / 32 + kr], s[pt][0]);
-          s[pt][1] = mfma_bf16(a, qb[1][DL / 32 + kr], s[pt][1]);
+          for (int kr = 0; kr < DR / 32; ++kr) {
+            const v8bf a = __builtin_bit_cast(
+                v8bf, make_uint4(wc[2 * kr].x, wc[2 * kr].y, wc[2 * kr + 1].x, wc[2 * kr + 1].y));
+            s[pt][0] = mfma_bf16(a, qb[0][DL / 32 + kr], s[pt][0]);
+            s[pt][1] = mfma_bf16(a, qb[1][DL / 32 + kr], s[pt][1]);
+          }
+        }
+        if (u + 1 < 10) {
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) wc[kk] = wn[kk];
         }
       }
       // per half: the two columns of a pair add to its score; mask; lazy
@@ -518,7 +551,7 @@ __global__ __launch_bounds__(512, 1) void mla_attn_kernel(const AttnArgs g) {
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
           const int p = 2 * l16 + jj;
-          const uint4 cv = *reinterpret_cast<const uint4*>(sb + p * DL + 16 * code_slot(c, p));
+          const uint4 cv = *reinterpret_cast<const uint4*>(sb + code_off(c, p));
           const uint32_t w4[4] = {cv.x, cv.y, cv.z, cv.w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
