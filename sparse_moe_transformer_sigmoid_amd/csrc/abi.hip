@@ -590,12 +590,13 @@ moe_status scratch_of_current_device(void** ptr) {
   return MOE_OK;
 }
 
-// A second stream (default priority) and a fork / join event pair per
-// device, created on first use and kept until the process ends: the training
-// backward runs its two independent chains on them.
+// A second stream (default priority) and its events per device, created on
+// first use and kept until the process ends: the training backward runs its
+// two independent chains on them (fork: the side stream starts; mid: the
+// side stream's transposes are done; join: the side chain is done).
 struct SideStream {
   hipStream_t s2 = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
+  hipEvent_t fork = nullptr, mid = nullptr, join = nullptr;
 };
 std::mutex g_side_mu;
 SideStream g_side[MAX_DEVICES];
@@ -610,6 +611,7 @@ moe_status side_stream_of_current_device(SideStream* out) {
     SideStream n;
     K2_HIP(hipStreamCreateWithFlags(&n.s2, hipStreamNonBlocking));
     K2_HIP(hipEventCreateWithFlags(&n.fork, hipEventDisableTiming));
+    K2_HIP(hipEventCreateWithFlags(&n.mid, hipEventDisableTiming));
     K2_HIP(hipEventCreateWithFlags(&n.join, hipEventDisableTiming));
     ss = n;
   }
@@ -617,15 +619,13 @@ moe_status side_stream_of_current_device(SideStream* out) {
   return MOE_OK;
 }
 
-// The weight-gradient chain of the training backward, enqueued on s: the
-// group-padded K-blocked transposes of its operands, then dW_down and
-// dW_gate, dW_up.
-moe_status train_wgrad_chain(const Dims& D, const TrainLayout& L, int64_t T, void* ws, void* sv,
-                             const TrainSaved& v, const int32_t* offsets,
-                             const int32_t* row_pair, const float* wts, const void* dout,
-                             const uint16_t* abf, const uint16_t* dgu, float* d_w,
-                             hipStream_t s) {
-  const size_t d = (size_t)D.d, I = (size_t)D.I;
+// The weight gradients of the training backward: the group-padded K-blocked
+// transposes of their operands (train_wgrad_transposes), then dW_down and
+// dW_gate, dW_up (train_wgrad_gemm), each enqueued on the stream given.
+moe_status train_wgrad_transposes(const Dims& D, const TrainLayout& L, int64_t T, void* ws,
+                                  void* sv, const TrainSaved& v, const int32_t* offsets,
+                                  const int32_t* row_pair, const float* wts, const void* dout,
+                                  const uint16_t* abf, const uint16_t* dgu, hipStream_t s) {
   const int64_t ldt = train_ldt(D);
   Stage stg(MOE_STAGE_TRAIN_WGRAD, s);
   int32_t* pad_off = at<int32_t>(ws, L.pad_off);
@@ -663,7 +663,20 @@ moe_status train_wgrad_chain(const Dims& D, const TrainLayout& L, int64_t T, voi
   ta.C = D.d;
   ta.dst = hT;
   K2_HIP(k2::launch_transpose_pad(2, ta, (int)ldt, s));
-  // dW_down [d, I] = sum (w dy)^T a~ ; dW_gate, dW_up [2I, d] = sum [dg; du]^T h~
+  return MOE_OK;
+}
+
+// down: dW_down [d, I] = sum (w dy)^T a~; otherwise dW_gate, dW_up [2I, d] =
+// sum [dg; du]^T h~ (after train_wgrad_transposes)
+moe_status train_wgrad_gemm(const Dims& D, const TrainLayout& L, void* ws, bool down, float* d_w,
+                            hipStream_t s) {
+  const size_t d = (size_t)D.d, I = (size_t)D.I;
+  Stage stg(MOE_STAGE_TRAIN_WGRAD, s);
+  const int32_t* pad_off = at<int32_t>(ws, L.pad_off);
+  const uint16_t* dywT = at<uint16_t>(ws, L.dywT);
+  const uint16_t* aT = at<uint16_t>(ws, L.aT);
+  const uint16_t* dguT = at<uint16_t>(ws, L.dguT);
+  const uint16_t* hT = at<uint16_t>(ws, L.hT);
   k2::TrainGemmArgs g{};
   g.E = D.E;
   g.G = D.G;
@@ -677,7 +690,10 @@ moe_status train_wgrad_chain(const Dims& D, const TrainLayout& L, int64_t T, voi
   g.NT = D.I / 128;
   g.out = d_w + 2 * I * d;
   g.ldo = D.I;
-  K2_HIP(k2::launch_train_gemm(k2::TM_WGRAD, g, (D.G * g.MT * g.NT + 7) / 8 * 8, s));
+  if (down) {
+    K2_HIP(k2::launch_train_gemm(k2::TM_WGRAD, g, (D.G * g.MT * g.NT + 7) / 8 * 8, s));
+    return MOE_OK;
+  }
   g.A = dguT;
   g.lda = 32 * 2 * D.I;
   g.B = hT;
@@ -1203,16 +1219,20 @@ moe_status moe_train_backward(const moe_config* cfg, int64_t T, const void* dout
     K2_HIP(k2::launch_train_gemm(k2::TM_BWD_DOWN, a, train_grid(D, a.NC), s));
   }
   // The weight gradients need only the down dgrad's outputs (a~, dg, du) and
-  // the saved state: they run on the side stream while the gate/up dgrad and
-  // the router backward run on `stream` (the gate/up dgrad reads weights, the
-  // weight gradients mostly write), joined before returning.
+  // the saved state.  The side stream forms their transposed operands and
+  // dW_gate, dW_up while `stream` runs the gate/up dgrad and the router
+  // backward and then dW_down (the gate/up dgrad reads weights, the weight
+  // gradients mostly write; this split gives the two streams about equal
+  // work); joined before returning.
   SideStream side;
   if ((st = side_stream_of_current_device(&side)) != MOE_OK) return st;
   K2_HIP(hipEventRecord(side.fork, s));
   K2_HIP(hipStreamWaitEvent(side.s2, side.fork, 0));
-  if ((st = train_wgrad_chain(D, L, T, ws, sv, v, offsets, row_pair, wts, dout, a.abf, a.dgu,
-                              d_w, side.s2)) != MOE_OK)
+  if ((st = train_wgrad_transposes(D, L, T, ws, sv, v, offsets, row_pair, wts, dout, a.abf,
+                                   a.dgu, side.s2)) != MOE_OK)
     return st;
+  K2_HIP(hipEventRecord(side.mid, side.s2));
+  if ((st = train_wgrad_gemm(D, L, ws, false, d_w, side.s2)) != MOE_OK) return st;
   K2_HIP(hipEventRecord(side.join, side.s2));
   {
     Stage stg(MOE_STAGE_TRAIN_DGRAD, s);
@@ -1261,6 +1281,9 @@ moe_status moe_train_backward(const moe_config* cfg, int64_t T, const void* dout
                                    at<const uint8_t>(sv, v.hq), at<const float>(sv, v.hs),
                                    d_w_router, s));
   }
+  // dW_down, once the side stream's transposes are done
+  K2_HIP(hipStreamWaitEvent(s, side.mid, 0));
+  if ((st = train_wgrad_gemm(D, L, ws, true, d_w, s)) != MOE_OK) return st;
   K2_HIP(hipStreamWaitEvent(s, side.join, 0));
   return MOE_OK;
 }
