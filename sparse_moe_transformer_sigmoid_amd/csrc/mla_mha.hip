@@ -89,22 +89,31 @@ __device__ __forceinline__ int cached_of(const int32_t* cached_len, int seq, int
 // ahead.  A 16x16x32 MFMA takes the weight rows as one operand and the codes
 // of 16 positions as the other; keys are formed as K^T (lane: one position,
 // 4 consecutive features), values as V (lane: one feature, 4 consecutive
-// positions), so both are stored 8 bytes at a time.  Positions at or past
-// the visible range are written as zeros (the attention masks them, and zero
-// values keep p = 0 terms finite).
+// positions).  The workgroup's two blocks of keys and values (64 KiB) are
+// assembled in LDS (rows padded so the 8-byte writes of 16 lanes fall on
+// distinct banks) and then written as eight contiguous 8 KiB regions, every
+// store a whole 16 bytes of a line.  Positions at or past the visible range
+// are written as zeros (the attention masks them, and zero values keep
+// p = 0 terms finite).
 //
 // Codes in LDS: position p's 16-byte chunk c at chunk slot c ^ (p % 16), so
 // the 8-byte fragment reads of 16 consecutive positions at one latent offset
 // fall on distinct banks.
 constexpr int XW = 8;                  // waves per expand workgroup
 constexpr int XF = 32;                 // features per wave
+// LDS assembly of a workgroup's output: keys [block][hi, lo][32 positions][128
+// features] with rows of 272 bytes, then values [block][hi, lo][128
+// features][32 positions] with rows of 80 bytes; the codes share the start
+constexpr int XK_LD = DN * 2 + 16, XV_LD = XB * 2 + 16;
+constexpr int XK_BYTES = 2 * 2 * XB * XK_LD, XV_BYTES = 2 * 2 * DN * XV_LD;
+constexpr int XS_BYTES = XK_BYTES + XV_BYTES;
+static_assert(XS_BYTES >= XP * DL, "the assembly area holds the codes first");
 
 template <bool VALUES>
-__device__ __forceinline__ void expand_wave(int h, int nblk, size_t sh, int p0, int valid,
-                                            const uint8_t* cl_s, const float* sc_s,
-                                            const uint16_t* __restrict__ w,
-                                            const float* __restrict__ sw, uint16_t* __restrict__ kv,
-                                            int f0, int lane) {
+__device__ __forceinline__ void expand_wave(int h, int p0, int valid, uint8_t* xs,
+                                            const float* sc_s, const uint16_t* __restrict__ w,
+                                            const float* __restrict__ sw, int f0, int lane) {
+  const uint8_t* cl_s = xs;
   const int g = lane >> 4, l16 = lane & 15;
   const uint16_t* wrow = w + ((size_t)h * DN + f0 + l16) * DL + 8 * g;
   // B / A fragment of positions 16 pt + l16, latents k0 + 8 g .. + 7: bytes of
@@ -172,36 +181,38 @@ __device__ __forceinline__ void expand_wave(int h, int nblk, size_t sh, int p0, 
       }
     }
   }
+  // every wave is done reading the codes before they are overwritten
+  __syncthreads();
 #pragma unroll
   for (int pt = 0; pt < 4; ++pt) {
     if constexpr (VALUES) {
-      const int pb = p0 + 16 * pt + 4 * g;   // four positions, all in one block
-      uint16_t* blk = kv + (sh * nblk + pb / XB) * XBLK;
-      const int r = pb % XB;
+      const int pl = 16 * pt + 4 * g;   // four positions, all in one block
+      const int bi = pl / XB, r = pl % XB;
 #pragma unroll
       for (int ft = 0; ft < 2; ++ft) {
         const int f = f0 + 16 * ft + l16;
         v4f v = acc[ft][pt];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (pb + i >= valid) v[i] = 0.f;
-        *reinterpret_cast<uint2*>(blk + 2 * XB * DN + f * XB + r) =
+          if (p0 + pl + i >= valid) v[i] = 0.f;
+        uint8_t* row = xs + XK_BYTES + ((bi * 2) * DN + f) * XV_LD + 2 * r;
+        *reinterpret_cast<uint2*>(row) =
             make_uint2(bf16_half2(v[0], v[1], 0.f), bf16_half2(v[2], v[3], 0.f));
-        *reinterpret_cast<uint2*>(blk + 3 * XB * DN + f * XB + r) =
+        *reinterpret_cast<uint2*>(row + DN * XV_LD) =
             make_uint2(bf16_half2(v[0], v[1], 1.f), bf16_half2(v[2], v[3], 1.f));
       }
     } else {
-      const int p = p0 + 16 * pt + l16;
-      uint16_t* blk = kv + (sh * nblk + p / XB) * XBLK;
-      const int r = p % XB;
+      const int pl = 16 * pt + l16;
+      const int bi = pl / XB, r = pl % XB;
 #pragma unroll
       for (int ft = 0; ft < 2; ++ft) {
         const int f = f0 + 16 * ft + 4 * g;
         v4f v = acc[ft][pt];
-        if (p >= valid) v = v4f{0.f, 0.f, 0.f, 0.f};
-        *reinterpret_cast<uint2*>(blk + r * DN + f) =
+        if (p0 + pl >= valid) v = v4f{0.f, 0.f, 0.f, 0.f};
+        uint8_t* row = xs + ((bi * 2) * XB + r) * XK_LD + 2 * f;
+        *reinterpret_cast<uint2*>(row) =
             make_uint2(bf16_half2(v[0], v[1], 0.f), bf16_half2(v[2], v[3], 0.f));
-        *reinterpret_cast<uint2*>(blk + XB * DN + r * DN + f) =
+        *reinterpret_cast<uint2*>(row + XB * XK_LD) =
             make_uint2(bf16_half2(v[0], v[1], 1.f), bf16_half2(v[2], v[3], 1.f));
       }
     }
@@ -215,7 +226,7 @@ __global__ __launch_bounds__(512, 4) void mla_kv_expand_kernel(
     const uint8_t* __restrict__ c_codes, const float* __restrict__ c_scales,
     const uint16_t* __restrict__ uk, const uint16_t* __restrict__ uv,
     const float* __restrict__ s_kvb, uint16_t* __restrict__ kv) {
-  __shared__ __attribute__((aligned(16))) uint8_t cl_s[XP * DL];
+  __shared__ __attribute__((aligned(16))) uint8_t xs[XS_BYTES];   // codes, then the output
   __shared__ float sc_s[XP * (DL / QBLK)];
   const int per = nblk / 2;
   const int sh = blockIdx.x / per, pb = blockIdx.x % per;
@@ -233,7 +244,7 @@ __global__ __launch_bounds__(512, 4) void mla_kv_expand_kernel(
     const int p = 8 * wave + 2 * i + (lane >> 5);
     const int c = (lane & 31) ^ (p & 15);
     lds_copy16(codes, (uint32_t)(min(p0 + p, valid - 1) * DL + 16 * c),
-               lds_addr(cl_s + (8 * wave + 2 * i) * DL));
+               lds_addr(xs + (8 * wave + 2 * i) * DL));
   }
   if (tid < XP * (DL / QBLK))
     sc_s[tid] = c_scales[((size_t)seq * max_len + min(p0 + tid / (DL / QBLK), valid - 1)) *
@@ -242,10 +253,25 @@ __global__ __launch_bounds__(512, 4) void mla_kv_expand_kernel(
   __syncthreads();
   const float* sw = s_kvb + (size_t)(2 * h + (wave >> 2)) * (DL / QBLK);
   if (wave < 4)
-    expand_wave<false>(h, nblk, (size_t)sh, p0, valid, cl_s, sc_s, uk, sw, kv, XF * wave, lane);
+    expand_wave<false>(h, p0, valid, xs, sc_s, uk, sw, XF * wave, lane);
   else
-    expand_wave<true>(h, nblk, (size_t)sh, p0, valid, cl_s, sc_s, uv, sw, kv, XF * (wave - 4),
-                      lane);
+    expand_wave<true>(h, p0, valid, xs, sc_s, uv, sw, XF * (wave - 4), lane);
+  __syncthreads();
+  // the two blocks: K hi, K lo, V hi, V lo, each 8 KiB contiguous in kv
+  uint16_t* dst0 = kv + ((size_t)sh * nblk + 2 * pb) * XBLK;
+#pragma unroll
+  for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+    for (int hl = 0; hl < 2; ++hl) {
+      uint8_t* dk = reinterpret_cast<uint8_t*>(dst0 + bi * XBLK + hl * XB * DN);
+      const int kr = tid >> 4, kc = tid & 15;   // 32 rows x 16 chunks
+      *reinterpret_cast<uint4*>(dk + kr * DN * 2 + 16 * kc) = *reinterpret_cast<const uint4*>(
+          xs + ((bi * 2 + hl) * XB + kr) * XK_LD + 16 * kc);
+      uint8_t* dv = reinterpret_cast<uint8_t*>(dst0 + bi * XBLK + (2 + hl) * XB * DN);
+      const int vr = tid >> 2, vc = tid & 3;    // 128 rows x 4 chunks
+      *reinterpret_cast<uint4*>(dv + vr * XB * 2 + 16 * vc) = *reinterpret_cast<const uint4*>(
+          xs + XK_BYTES + ((bi * 2 + hl) * DN + vr) * XV_LD + 16 * vc);
+    }
 }
 
 // ------------------------------------------------------------ attention
