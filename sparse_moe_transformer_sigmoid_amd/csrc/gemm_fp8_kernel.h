@@ -266,6 +266,21 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, v4f (&acc)[4][TT], f
         const int m = tt * 16 + (lane & 15);
         if (m < mcount) {
           const int row = row0 + m;
+          if (g.out_bf16) {
+            // out = bf16(res + row), the residual add of a dense projection
+            const size_t o0 = (size_t)row * g.d + nc * 256 + 64 * wave + 4 * (lane >> 4);
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+              const v4f o = acc[rt][tt];
+              const uint2 xr = *reinterpret_cast<const uint2*>(g.res + o0 + 16 * rt);
+              const uint32_t w0 = f32_to_bf16_rne(bf16_to_f32(xr.x & 0xFFFFu) + o[0]) |
+                                  (f32_to_bf16_rne(bf16_to_f32(xr.x >> 16) + o[1]) << 16);
+              const uint32_t w1 = f32_to_bf16_rne(bf16_to_f32(xr.y & 0xFFFFu) + o[2]) |
+                                  (f32_to_bf16_rne(bf16_to_f32(xr.y >> 16) + o[3]) << 16);
+              *reinterpret_cast<uint2*>(g.out_bf16 + o0 + 16 * rt) = make_uint2(w0, w1);
+            }
+            continue;
+          }
           float wt = 1.f;
           const bool mul = g.weighted && !shared_grp;
           if (mul) wt = g.topk_w[min(max(g.row_pair[row], 0), g.P - 1)];

@@ -77,6 +77,10 @@ struct GemmArgs {
   const float* topk_w;      // [P] pair weights, used when weighted
   int weighted;
   int d;
+  // down form, one group of token rows, one K slice: if out_bf16 is set, each
+  // row is written as bf16(res + row) to out_bf16 [T, d] instead of to rows
+  const uint16_t* res;      // [T, d] bf16
+  uint16_t* out_bf16;       // [T, d] bf16
 };
 hipError_t launch_gemm_fp8(bool gateup, int tt, const GemmArgs& a, int grid, hipStream_t s);
 

@@ -259,7 +259,8 @@ Tp* at(void* base, size_t off) {
 moe_status run_gemm(const MDims& D, int T, int N, int K, int nsplit, const uint8_t* act,
                     const float* act_s, const uint8_t* wcodes, const float* wscales,
                     const int32_t* offsets, const int32_t* mt_start, const int32_t* tile_group,
-                    float* out, hipStream_t s, bool wide = false) {
+                    float* out, hipStream_t s, bool wide = false,
+                    const uint16_t* res = nullptr, uint16_t* out_bf16 = nullptr) {
   const int tt = wide ? 8 : gemm_tt(T);
   const int bm = 16 * tt;
   k2::GemmArgs a{};
@@ -284,6 +285,8 @@ moe_status run_gemm(const MDims& D, int T, int N, int K, int nsplit, const uint8
   a.rows = out;
   a.weighted = 0;
   a.d = N;
+  a.res = res;
+  a.out_bf16 = out_bf16;
   const int mtiles = (T + bm - 1) / bm;
   const int grid = (mtiles * a.NC + 7) / 8 * 8;
   if (wide)
@@ -425,16 +428,20 @@ moe_status run_mla(const mla_config* cfg, int32_t S, int32_t n, int32_t L, const
   }
   if (!out) return MOE_OK;
   k2::ProfileScope ps(MOE_STAGE_MLA_PROJ, s);
-  // out = x + o W_o^T
+  // out = x + o W_o^T; one K slice with a bf16 output: the residual add in
+  // the GEMM's epilogue (the same rounding as the slice sum's)
+  const bool fused = W.ns_o == 1 && !out_f32;
   if ((st = run_gemm(D, T, D.n_o, D.H * D.v, W.ns_o, o_q, o_s, pk + P.o_codes,
                      reinterpret_cast<const float*>(pk + P.o_scales), offsets,
                      W.o_wide ? at<int32_t>(ws, W.mt_start8) : mt_start,
                      W.o_wide ? at<int32_t>(ws, W.tile_group8) : tile_group, part, s,
-                     W.o_wide)) != MOE_OK)
+                     W.o_wide, fused ? static_cast<const uint16_t*>(x) : nullptr,
+                     fused ? static_cast<uint16_t*>(out) : nullptr)) != MOE_OK)
     return st;
-  M_HIP(k2::launch_slice_sum(T, D.n_o, D.n_o, W.ns_o, part,
-                             out_f32 ? nullptr : static_cast<const uint16_t*>(x), out, D.n_o,
-                             s));
+  if (!fused)
+    M_HIP(k2::launch_slice_sum(T, D.n_o, D.n_o, W.ns_o, part,
+                               out_f32 ? nullptr : static_cast<const uint16_t*>(x), out, D.n_o,
+                               s));
   return MOE_OK;
 }
 
