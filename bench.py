@@ -41,14 +41,14 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 # the factor a 1 GiB copy probe gives) + WRITE_SIZE (x1.000), see
 # profiles/gemm_gateup_k2_decode.md; valid only for the GEMM sources whose combined
 # sha256 starts with the recorded prefix (null otherwise).
-MEASURED_TRAFFIC = {"k2_decode": ("c6660126787d3675", 7.891e9),
-                    "k2_prefill": ("c6660126787d3675", 15.077e9)}
+MEASURED_TRAFFIC = {"k2_decode": ("7abebc1c55f983c1", 7.893e9),
+                    "k2_prefill": ("7abebc1c55f983c1", 15.166e9)}
 # FP8 MFMA busy fraction of the gate/up launch (SQ_VALU_MFMA_BUSY_CYCLES over
 # GRBM_GUI_ACTIVE x SIMDs) and its executed/algorithmic MFMA work
 # (SQ_INSTS_VALU_MFMA_MOPS_F8 x 512), from rocprofv3 counters, see
 # profiles/gemm_mfma_k2_prefill_dense.md; same source-hash rule as the traffic.
-MEASURED_MFMA = {"k2_prefill": ("c6660126787d3675", 0.335, 1.041),
-                 "k2_dense": ("c6660126787d3675", 0.437, 1.000)}
+MEASURED_MFMA = {"k2_prefill": ("7abebc1c55f983c1", 0.338, 1.041),
+                 "k2_dense": ("7abebc1c55f983c1", 0.438, 1.000)}
 GEMM_SRCS = [os.path.join(ROOT, "sparse_moe_transformer_sigmoid_amd", "csrc", f)
              for f in ("gemm_fp8_kernel.h", "gemm_fp8.hip", "gemm_fp8_wide.hip")]
 
